@@ -1,0 +1,216 @@
+"""KDA oracle: plain CPU reference for the gated delta-rule mixer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its Python binding) never imports, links or calls it, and it
+shares no code with them.
+
+Contents
+--------
+* ``recurrence``    -- the sequential recurrence in C (``kda_oracle.c``), fp64 or
+  fp32, OpenMP over independent (sequence, head) pairs.
+* ``short_conv``    -- width-4 causal depthwise convolution (C, fp64).
+* ``l2norm_heads``  -- per-head L2 normalisation (C, fp64).
+* ``brute_force``   -- a second, independent formulation in numpy fp64: the
+  dense transition matrices M_t = (I - beta_t k_t k_t^T) Diag(alpha_t) multiplied
+  out, for tiny inputs only.
+
+Where each step comes from is stated in ``kda_oracle.c``'s header: page
+"Ling-3.1-flash: a 560B hybrid-attention MoE, counted from its safetensors
+headers", section "How KDA and MLA split the work" (per-channel decay, per-head
+write strength, width-4 causal convolution of q, k, v), whose display equation
+did not survive extraction; the recurrence is the gated delta rule
+S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T, o_t = S_t^T q_t.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "kda_oracle.c")
+LIB = os.path.join(HERE, "libkda_oracle.so")
+
+
+def build(out: str = LIB, mutant: int = 0) -> str:
+    """Compile the C oracle with gcc.  ``mutant`` plants a deliberate mistake
+    (pin tests only); the default build has none."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", SRC, "-o", out, "-lm"]
+    if mutant:
+        cmd.insert(1, f"-DKDA_ORACLE_MUTANT={int(mutant)}")
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+_ip = ctypes.POINTER(ctypes.c_int32)
+
+
+def _ptr(a, kind):
+    if a is None:
+        return None
+    return a.ctypes.data_as(kind)
+
+
+class Oracle:
+    """ctypes view of one build of ``kda_oracle.c``."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            build(path)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        for name, fp in (("kda_oracle_recurrence_f64", _dp), ("kda_oracle_recurrence_f32", _fp)):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [fp, fp, fp, fp, fp, _ip, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                           ctypes.c_int, fp, fp, fp, ctypes.c_int]
+        lib.kda_oracle_short_conv_f64.restype = ctypes.c_int
+        lib.kda_oracle_short_conv_f64.argtypes = [_dp, _dp, _ip, ctypes.c_int, ctypes.c_int, _dp,
+                                                  _dp, _dp]
+        lib.kda_oracle_l2norm_heads_f64.restype = ctypes.c_int
+        lib.kda_oracle_l2norm_heads_f64.argtypes = [_dp, ctypes.c_int64, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.c_double]
+        lib.kda_oracle_mutant.restype = ctypes.c_int
+        self.lib = lib
+        self.mutant = lib.kda_oracle_mutant()
+
+    # ------------------------------------------------------------------ recurrence
+    def recurrence(self, q, k, v, g, beta, cu_seqlens=None, S0=None, precision="f64",
+                   n_threads=0):
+        """Run the recurrence.
+
+        q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H] (any real dtype; they are
+        converted exactly to the working precision).  ``cu_seqlens`` [n+1] packs n
+        sequences (default: one sequence of T tokens).  ``S0`` [n, H, dk, dv] or
+        None (zeros).  Returns (o [T, H, dv], S_final [n, H, dk, dv]) in the working
+        precision.
+        """
+        real = np.float64 if precision == "f64" else np.float32
+        kind = _dp if precision == "f64" else _fp
+        fn = self.lib.kda_oracle_recurrence_f64 if precision == "f64" else \
+            self.lib.kda_oracle_recurrence_f32
+        q, k, v, g = (np.ascontiguousarray(x, dtype=real) for x in (q, k, v, g))
+        beta = np.ascontiguousarray(beta, dtype=real)
+        T, H, dk = q.shape
+        dv = v.shape[2]
+        if k.shape != (T, H, dk) or g.shape != (T, H, dk) or v.shape[:2] != (T, H) \
+                or beta.shape != (T, H):
+            raise ValueError("oracle: inconsistent shapes")
+        if cu_seqlens is None:
+            cu_seqlens = np.array([0, T], dtype=np.int32)
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        n = cu.shape[0] - 1
+        if int(cu[-1]) != T:
+            raise ValueError("oracle: cu_seqlens[-1] != T")
+        if S0 is not None:
+            S0 = np.ascontiguousarray(S0, dtype=real)
+            if S0.shape != (n, H, dk, dv):
+                raise ValueError("oracle: S0 shape")
+        o = np.empty((T, H, dv), dtype=real)
+        S = np.empty((n, H, dk, dv), dtype=real)
+        rc = fn(_ptr(q, kind), _ptr(k, kind), _ptr(v, kind), _ptr(g, kind), _ptr(beta, kind),
+                _ptr(cu, _ip), n, H, dk, dv, _ptr(S0, kind), _ptr(o, kind), _ptr(S, kind),
+                int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"oracle recurrence failed: {rc}")
+        return o, S
+
+    # ------------------------------------------------------------------ conv + norm
+    def short_conv(self, x, w, cu_seqlens=None, tail=None):
+        """Width-4 causal depthwise convolution.  x [T, Cch], w [Cch, 4],
+        tail [n, 3, Cch] or None.  Returns (y [T, Cch], tail_out [n, 3, Cch]) fp64."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        T, C = x.shape
+        if w.shape != (C, 4):
+            raise ValueError("oracle: conv weight shape")
+        if cu_seqlens is None:
+            cu_seqlens = np.array([0, T], dtype=np.int32)
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        n = cu.shape[0] - 1
+        if tail is not None:
+            tail = np.ascontiguousarray(tail, dtype=np.float64)
+            if tail.shape != (n, 3, C):
+                raise ValueError("oracle: tail shape")
+        y = np.empty((T, C), dtype=np.float64)
+        tail_out = np.empty((n, 3, C), dtype=np.float64)
+        rc = self.lib.kda_oracle_short_conv_f64(_ptr(x, _dp), _ptr(w, _dp), _ptr(cu, _ip), n, C,
+                                                _ptr(tail, _dp), _ptr(y, _dp),
+                                                _ptr(tail_out, _dp))
+        if rc != 0:
+            raise RuntimeError(f"oracle short_conv failed: {rc}")
+        return y, tail_out
+
+    def l2norm_heads(self, x, head_dim, eps=1e-6):
+        """x / sqrt(sum x^2 + eps) over each run of ``head_dim`` channels of each
+        row of x [rows, width].  Returns a new fp64 array."""
+        y = np.array(x, dtype=np.float64, order="C", copy=True)
+        rows = y.shape[0]
+        width = int(np.prod(y.shape[1:]))
+        rc = self.lib.kda_oracle_l2norm_heads_f64(_ptr(y, _dp), rows, width, int(head_dim),
+                                                  float(eps))
+        if rc != 0:
+            raise RuntimeError(f"oracle l2norm failed: {rc}")
+        return y
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle(LIB)
+    return _default
+
+
+def recurrence(*args, **kw):
+    return default().recurrence(*args, **kw)
+
+
+def short_conv(*args, **kw):
+    return default().short_conv(*args, **kw)
+
+
+def l2norm_heads(*args, **kw):
+    return default().l2norm_heads(*args, **kw)
+
+
+def brute_force(q, k, v, g, beta, S0=None):
+    """Second formulation, numpy fp64, for one sequence and tiny sizes only.
+
+    Builds each transition matrix M_t = (I - beta_t k_t k_t^T) Diag(alpha_t) as a
+    dense d_k x d_k matrix and expands the state as
+        S_t = Phi_{t,0} S_0 + sum_{s<=t} Phi_{t,s} beta_s k_s v_s^T,
+    Phi_{t,s} = M_t M_{t-1} ... M_{s+1} (Phi_{t,t} = I), reading o_t = S_t^T q_t.
+    Every S_t is formed from scratch from that sum, with no carried state, so a
+    mistake in the carried-state bookkeeping of the C oracle cannot repeat here.
+    Shapes as ``Oracle.recurrence`` with one sequence; returns (o, S_T).
+    """
+    q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((T, H, dv))
+    S_T = np.zeros((H, dk, dv))
+    eye = np.eye(dk)
+    for h in range(H):
+        S0h = np.zeros((dk, dv)) if S0 is None else np.asarray(S0, dtype=np.float64)[h]
+        M = [(eye - beta[t, h] * np.outer(k[t, h], k[t, h])) @ np.diag(np.exp(g[t, h]))
+             for t in range(T)]
+        for t in range(T):
+            # Phi_{t,s} for s = t, t-1, ..., -1 built right to left
+            phi = eye.copy()
+            acc = np.zeros((dk, dv))
+            for s in range(t, -1, -1):
+                acc += phi @ (beta[s, h] * np.outer(k[s, h], v[s, h]))
+                phi = phi @ M[s]
+            St = phi @ S0h + acc
+            o[t, h] = St.T @ q[t, h]
+            if t == T - 1:
+                S_T[h] = St
+    return o, S_T
