@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one pass of the path over one batch of synthetic input: the state
+buffer is initialised (zero fill) and the chunked prefill runs over a Ling-shaped
+KDA layer (B=1, H=64, T=8192, d_k = d_v = 128, chunk 64, bf16 q/k/v, fp32 g,
+beta and state).  ``value`` is that prefill's whole-job throughput in tokens/s,
+inputs resident in HBM.  The batched decode step (B=256 sequences x 64 heads,
+one token each, fp32 128x128 states) is timed in the same run and reported as
+achieved state bandwidth under ``decode``.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+METRIC = "KDA layer tokens/s (H=64,d=128 prefill); decode state GB/s vs HBM peak"
+PREFILL_KERNEL = "prefill_mfma_kernel"
+DECODE_KERNEL = "decode_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+SOURCES = {
+    PREFILL_KERNEL: os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc", "kda_prefill_mfma.hip"),
+    DECODE_KERNEL: os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc", "kda_decode.hip"),
+}
+
+
+def source_sha(kernel):
+    with open(SOURCES[kernel], "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, scaled by
+    the copy-kernel calibration; None if absent or taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(kernel):
+        return None
+    return (rec["fetch_kib"] * 1024 * rec["fetch_scale"] +
+            rec["write_kib"] * 1024 * rec["write_scale"])
+
+
+def prefill_algorithmic(T, H, d, chunk, with_s0, with_sfinal):
+    """Algorithmic HBM bytes and flops of one prefill launch (bf16 q/k/v/o, fp32
+    g/beta/state).  Bytes per token-head: q, k, v 3*2d, g 4d, beta 4, o 2d.
+    Flops per token-head: 6 d^2 (W S, Qt S, Kb^T U) + 5 C d (the C x C products
+    and the two C-wide applications) + C^2 / 3 (triangular inverse)."""
+    th = T * H
+    bytes_ = th * (3 * 2 * d + 4 * d + 4 + 2 * d)
+    state = H * d * d * 4
+    bytes_ += state * (int(with_s0) + int(with_sfinal))
+    flops = th * (6 * d * d + 5 * chunk * d + chunk * chunk / 3.0)
+    return bytes_, flops
+
+
+def decode_algorithmic(B, H, d):
+    """Per (sequence, head): state read + write (2 * 4 d^2) and q, k, v, g, beta, o."""
+    return B * H * (2 * 4 * d * d + 3 * 2 * d + 4 * d + 4 + 2 * d)
+
+
+def cpu_baseline_run(inp):
+    """The oracle's plain fp32 recurrence, as it stands, on every head of the
+    prefill workload, with every host core this process may use."""
+    import numpy as np
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    q = inp.q.float().numpy()
+    k = inp.k.float().numpy()
+    v = inp.v.float().numpy()
+    g = inp.g.numpy()
+    beta = inp.beta.numpy()
+    t0 = time.perf_counter()
+    oracle.recurrence(q, k, v, g, beta, cu_seqlens=inp.cu_seqlens.numpy(), precision="f32",
+                      n_threads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": inp.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole prefill workload (T={inp.T}, H={inp.H}, d={inp.d}), fp32 "
+                      f"sequential recurrence, OpenMP over heads; {dt:.2f} s wall",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run just one kernel (for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the KDA hot path of one GPU's "
+              "share); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_99_amd as kda
+    import workloads
+
+    kda.load()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    if args.only == "copy":
+        # plain copy of a known size: calibrates the profiler's byte counters
+        n = 1 << 28  # 1 GiB of fp32
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(max(1, args.steps)):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4}))
+        return
+
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic"}
+
+    if args.only in (None, "prefill"):
+        inp = workloads.ling_prefill()
+        T, H, d, C = inp.T, inp.H, inp.d, inp.chunk
+        q, k, v, g, beta = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+        cu = inp.cu_seqlens.to(dev)
+        state = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+        o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+        def step(e0=None, e1=None):
+            kda.kda_state_init(state)
+            if e0 is not None:
+                e0.record()
+            kda.kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=cu,
+                                    cu_seqlens_host=inp.cu_seqlens, chunk=C,
+                                    initial_state=state, final_state=state, o=o)
+            if e1 is not None:
+                e1.record()
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        pairs = [(ev(), ev()) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in pairs:
+            step(e0, e1)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in pairs) / len(pairs)
+        ms_per_step = wall * 1e3 / args.steps
+        alg_bytes, alg_flops = prefill_algorithmic(T, H, d, C, True, True)
+        achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+        traffic = measured_traffic(PREFILL_KERNEL)
+        result.update({
+            "value": T * args.steps / wall,
+            "unit": "tokens/s",
+            "ms_per_step": ms_per_step,
+            "config": {"workload": "Ling-shaped KDA layer prefill: B=1, H=64, T=8192, "
+                                   "d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 g/beta/state, "
+                                   "zero initial state",
+                       "global_batch": 1, "seq_len": T, "heads": H, "head_dim": d,
+                       "chunk": C, "parallelism": "none (1 GPU)"},
+            "roofline": {"bound": "hbm", "kernel": PREFILL_KERNEL, "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": traffic, "kernel_ms": kern_ms,
+                         "algorithmic_bytes": alg_bytes},
+            "mfma": {"algorithmic_tflops": alg_flops / (kern_ms * 1e-3) / 1e12,
+                     "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "frac": alg_flops / (kern_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                     "attainable_frac": min(1.0, (alg_flops / alg_bytes) * HBM_PEAK_GBS * 1e9 /
+                                            (BF16_MFMA_PEAK_TFLOPS * 1e12)),
+                     "algorithmic_flops": alg_flops},
+        })
+        del q, k, v, g, beta, o, state
+        if not args.no_cpu_baseline and args.only is None:
+            result["cpu_baseline"] = cpu_baseline_run(inp)
+        del inp
+        torch.cuda.empty_cache()
+
+    if args.only == "decode" or (args.only is None and not args.no_decode):
+        inp = workloads.decode_batch()
+        B, H, d = inp.n_seqs, inp.H, inp.d
+        q, k, v, g, beta = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+        state = inp.S0.to(dev)
+        o = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+        nsteps = args.decode_steps if args.only is None else args.steps
+        for _ in range(args.warmup):
+            kda.kda_decode_step(q, k, v, g, beta, state, o=o)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(nsteps):
+            kda.kda_decode_step(q, k, v, g, beta, state, o=o)
+        e1.record()
+        torch.cuda.synchronize()
+        step_ms = e0.elapsed_time(e1) / nsteps
+        alg = decode_algorithmic(B, H, d)
+        gbs = alg / (step_ms * 1e-3) / 1e9
+        dec = {"workload": "batched decode step: B=256 sequences x H=64 heads, one token "
+                           "each, fp32 128x128 states, bf16 q/k/v",
+               "ms_per_step": step_ms, "tokens_per_s": B / (step_ms * 1e-3),
+               "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL, "achieved": gbs,
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                            "traffic": measured_traffic(DECODE_KERNEL),
+                            "algorithmic_bytes": alg}}
+        if args.only == "decode":
+            result.update({"value": B / (step_ms * 1e-3), "unit": "tokens/s",
+                           "ms_per_step": step_ms})
+        result["decode"] = dec
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,281 @@
+// C ABI of libkda.so: host-side argument checks and kernel dispatch.
+// Every check runs before anything is enqueued; a failed check returns a status
+// and leaves the stream untouched.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_detail[512];
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+kda_status hip_status(hipError_t err, const char* what) {
+    if (err == hipSuccess) return KDA_OK;
+    return fail(KDA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(err), (int)err);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t elem_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+// Common head-shape checks.  Returns KDA_OK or an error with detail set.
+kda_status check_heads(const char* fn, int H, int dk, int dv) {
+    if (H <= 0 || dk <= 0 || dv <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: H, dk, dv must be positive (got %d, %d, %d)",
+                    fn, H, dk, dv);
+    if (dk != dv)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dk != dv (%d, %d) is not implemented", fn, dk, dv);
+    if (!supported_d(dk))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: head dim %d not in {16, 32, 64, 128}", fn, dk);
+    return KDA_OK;
+}
+
+kda_status check_cu(const char* fn, const int32_t* cu_host, int n_seqs, int64_t* T_out) {
+    if (n_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_seqs < 0", fn);
+    if (!cu_host) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens_host is NULL", fn);
+    if (cu_host[0] != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens[0] = %d, expected 0", fn,
+                    cu_host[0]);
+    for (int n = 0; n < n_seqs; ++n)
+        if (cu_host[n + 1] < cu_host[n])
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "%s: cu_seqlens decreases at %d (%d -> %d)", fn, n, cu_host[n],
+                        cu_host[n + 1]);
+    *T_out = cu_host[n_seqs];
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error_detail(void) { return g_detail; }
+
+size_t kda_state_bytes(int H, int dk, int dv) {
+    if (H <= 0 || dk <= 0 || dv <= 0) return 0;
+    return (size_t)4 * (size_t)H * (size_t)dk * (size_t)dv;
+}
+
+kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
+                          const float* src, hipStream_t stream) {
+    g_detail[0] = 0;
+    if (kda_status s = check_heads("kda_state_init", H, dk, dv)) return s;
+    if (n_slots < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_state_init: n_slots < 0");
+    if (n_slots == 0) return KDA_OK;
+    if (!state || !aligned16(state) || (src && !aligned16(src)))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "kda_state_init: state/src must be non-NULL and 16-byte aligned");
+    const size_t bytes = (size_t)n_slots * kda_state_bytes(H, dk, dv);
+    if (src && overlaps(state, bytes, src, bytes))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_state_init: src overlaps state");
+    return hip_status(kda::launch_state_init(state, (int64_t)(bytes / 4), src, stream),
+                      "kda_state_init launch");
+}
+
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, kda_dtype dtype,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               int n_seqs, int H, int dk, int dv, int chunk,
+                               const float* initial_state, float* final_state, void* o,
+                               hipStream_t stream) {
+    const char* fn = "kda_prefill_chunked";
+    g_detail[0] = 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+    if (kda_status s = check_heads(fn, H, dk, dv)) return s;
+    if (chunk != 16 && chunk != 32 && chunk != 64)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: chunk %d not in {16, 32, 64}", fn, chunk);
+    int64_t T = 0;
+    if (kda_status s = check_cu(fn, cu_seqlens_host, n_seqs, &T)) return s;
+    if (n_seqs == 0) return KDA_OK;
+    if (!cu_seqlens_dev) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens_dev is NULL", fn);
+    const int d = dk;
+    const int64_t blocks = (int64_t)n_seqs * H * (d == 128 ? 4 : (d < 32 ? 1 : d / 32));
+    if (blocks > 0x7fffffff)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn,
+                    (long long)blocks);
+    const size_t es = elem_size(dtype);
+    const size_t n_qk = (size_t)T * H * d, n_bt = (size_t)T * H;
+    const size_t sbytes = (size_t)n_seqs * kda_state_bytes(H, dk, dv);
+    if (T > 0) {
+        if (!q || !k || !v || !g || !beta || !o)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: q, k, v, g, beta and o are required", fn);
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+            ((uintptr_t)beta & 3u))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
+        if (overlaps(o, n_qk * es, q, n_qk * es) || overlaps(o, n_qk * es, k, n_qk * es) ||
+            overlaps(o, n_qk * es, v, n_qk * es) || overlaps(o, n_qk * es, g, n_qk * 4) ||
+            overlaps(o, n_qk * es, beta, n_bt * 4) ||
+            overlaps(o, n_qk * es, final_state, sbytes) ||
+            overlaps(o, n_qk * es, initial_state, sbytes))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o overlaps another argument", fn);
+    }
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned state pointer", fn);
+    if (initial_state && final_state && initial_state != final_state &&
+        overlaps(initial_state, sbytes, final_state, sbytes))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "%s: initial_state and final_state overlap without being equal", fn);
+    if (final_state && T > 0 &&
+        (overlaps(final_state, sbytes, q, n_qk * es) || overlaps(final_state, sbytes, k, n_qk * es) ||
+         overlaps(final_state, sbytes, v, n_qk * es) || overlaps(final_state, sbytes, g, n_qk * 4)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state overlaps an input", fn);
+
+    hipError_t err;
+    if (dtype == KDA_BF16 && d == 128 && chunk == 64)
+        err = kda::launch_prefill_mfma(q, k, v, g, beta, cu_seqlens_dev, n_seqs, T, H,
+                                       initial_state, final_state, o, stream);
+    else
+        err = kda::launch_prefill_vector(q, k, v, g, beta, dtype, cu_seqlens_dev, n_seqs, T, H,
+                                         d, chunk, initial_state, final_state, o, stream);
+    return hip_status(err, "kda_prefill_chunked launch");
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                           const int32_t* slot_idx, int B, int H, int dk, int dv, void* o,
+                           hipStream_t stream) {
+    const char* fn = "kda_decode_step";
+    g_detail[0] = 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+    if (kda_status s = check_heads(fn, H, dk, dv)) return s;
+    if (B < 0 || n_slots < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B and n_slots must be >= 0", fn);
+    if (B == 0) return KDA_OK;
+    if (!slot_idx && n_slots < B)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots (%lld) < B (%d) without slot_idx", fn,
+                    (long long)n_slots, B);
+    if ((int64_t)B * H > 0x7fffffff)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: B * H exceeds the grid limit", fn);
+    if (!q || !k || !v || !g || !beta || !o || !state)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: q, k, v, g, beta, state and o are required",
+                    fn);
+    const size_t es = elem_size(dtype);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+        !aligned16(state) || ((uintptr_t)beta & 3u) || ((uintptr_t)slot_idx & 3u))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
+    const size_t nv = (size_t)B * H * dk;
+    const size_t sbytes = (size_t)n_slots * kda_state_bytes(H, dk, dv);
+    if (overlaps(o, nv * es, q, nv * es) || overlaps(o, nv * es, k, nv * es) ||
+        overlaps(o, nv * es, v, nv * es) || overlaps(o, nv * es, g, nv * 4) ||
+        overlaps(o, nv * es, state, sbytes) || overlaps(state, sbytes, q, nv * es) ||
+        overlaps(state, sbytes, k, nv * es) || overlaps(state, sbytes, v, nv * es) ||
+        overlaps(state, sbytes, g, nv * 4) || overlaps(state, sbytes, beta, (size_t)B * H * 4))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state or o overlaps another argument", fn);
+    return hip_status(kda::launch_decode(q, k, v, g, beta, dtype, state, n_slots, slot_idx, B,
+                                         H, dk, o, stream),
+                      "kda_decode_step launch");
+}
+
+static kda_status check_conv_common(const char* fn, const float* w, kda_dtype dtype,
+                                    int channels, int l2_head_dim, float l2_eps) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+    if (channels <= 0 || channels % 2)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: channels must be positive and even", fn);
+    if (!w || !aligned16(w))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: w must be non-NULL and 16-byte aligned", fn);
+    if (l2_head_dim < 0 || (l2_head_dim > 0 && (channels % l2_head_dim || l2_head_dim % 2)))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "%s: l2_head_dim must be 0 or an even divisor of channels", fn);
+    if (l2_head_dim > 256)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: l2_head_dim > 256", fn);
+    if (l2_head_dim == 0 && channels % 128 && channels > 256)
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "%s: without normalisation, channels must be a multiple of 128 or <= 256",
+                    fn);
+    if (!(l2_eps >= 0.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: l2_eps must be >= 0", fn);
+    return KDA_OK;
+}
+
+kda_status kda_short_conv_prefill(const void* x, const float* w, kda_dtype dtype,
+                                  const int32_t* cu_seqlens_dev,
+                                  const int32_t* cu_seqlens_host, int n_seqs, int channels,
+                                  int l2_head_dim, float l2_eps, const void* conv_tail_in,
+                                  void* conv_tail_out, void* y, hipStream_t stream) {
+    const char* fn = "kda_short_conv_prefill";
+    g_detail[0] = 0;
+    if (kda_status s = check_conv_common(fn, w, dtype, channels, l2_head_dim, l2_eps)) return s;
+    int64_t T = 0;
+    if (kda_status s = check_cu(fn, cu_seqlens_host, n_seqs, &T)) return s;
+    if (n_seqs == 0) return KDA_OK;
+    if (!cu_seqlens_dev) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens_dev is NULL", fn);
+    if ((T + 15) / 16 > 0x7fffffff)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+    const size_t es = elem_size(dtype);
+    const size_t nx = (size_t)T * channels * es, nt = (size_t)n_seqs * 3 * channels * es;
+    if (T > 0) {
+        if (!x || !y) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: x and y are required", fn);
+        if (!aligned16(x) || !aligned16(y))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned x or y", fn);
+        if (overlaps(x, nx, y, nx) || overlaps(y, nx, conv_tail_in, nt) ||
+            overlaps(y, nx, conv_tail_out, nt) || overlaps(x, nx, conv_tail_out, nt))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: y or conv_tail_out overlaps an input", fn);
+    }
+    if ((conv_tail_in && !aligned16(conv_tail_in)) || (conv_tail_out && !aligned16(conv_tail_out)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned conv tail", fn);
+    if (conv_tail_in && conv_tail_out && conv_tail_in != conv_tail_out &&
+        overlaps(conv_tail_in, nt, conv_tail_out, nt))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: conv tails overlap without being equal", fn);
+    return hip_status(kda::launch_short_conv_prefill(x, w, dtype, cu_seqlens_dev, n_seqs, T,
+                                                     channels, l2_head_dim, l2_eps,
+                                                     conv_tail_in, conv_tail_out, y, stream),
+                      "kda_short_conv_prefill launch");
+}
+
+kda_status kda_short_conv_decode(const void* x, const float* w, kda_dtype dtype,
+                                 void* conv_tail, int64_t n_slots, const int32_t* slot_idx,
+                                 int B, int channels, int l2_head_dim, float l2_eps, void* y,
+                                 hipStream_t stream) {
+    const char* fn = "kda_short_conv_decode";
+    g_detail[0] = 0;
+    if (kda_status s = check_conv_common(fn, w, dtype, channels, l2_head_dim, l2_eps)) return s;
+    if (B < 0 || n_slots < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B and n_slots must be >= 0", fn);
+    if (B == 0) return KDA_OK;
+    if (!slot_idx && n_slots < B)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots < B without slot_idx", fn);
+    if (!x || !y || !conv_tail)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: x, y and conv_tail are required", fn);
+    if (!aligned16(x) || !aligned16(y) || !aligned16(conv_tail) || ((uintptr_t)slot_idx & 3u))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned pointer", fn);
+    const size_t es = elem_size(dtype);
+    const size_t nx = (size_t)B * channels * es, nt = (size_t)n_slots * 3 * channels * es;
+    if (overlaps(x, nx, y, nx) || overlaps(y, nx, conv_tail, nt) || overlaps(x, nx, conv_tail, nt))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: x, y and conv_tail must not overlap", fn);
+    return hip_status(kda::launch_short_conv_decode(x, w, dtype, conv_tail, n_slots, slot_idx, B,
+                                                    channels, l2_head_dim, l2_eps, y, stream),
+                      "kda_short_conv_decode launch");
+}
+
+}  // extern "C"

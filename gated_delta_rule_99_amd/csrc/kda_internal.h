@@ -1,0 +1,114 @@
+// Internal declarations shared by the HIP sources of libkda.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16_t {
+    uint16_t bits;
+};
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Load n consecutive input elements (fp32 or bf16) as fp32.
+template <typename Tin>
+struct In;
+
+template <>
+struct In<float> {
+    static __device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
+        float4 v = *reinterpret_cast<const float4*>(p);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    }
+    static __device__ __forceinline__ float load1(const float* p) { return *p; }
+    static __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
+    static __device__ __forceinline__ void store4(float* p, const float (&x)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+};
+
+template <>
+struct In<bf16_t> {
+    static __device__ __forceinline__ void load4(const bf16_t* p, float (&x)[4]) {
+        uint2 v = *reinterpret_cast<const uint2*>(p);
+        x[0] = bf16_bits_to_f32(v.x & 0xffffu);
+        x[1] = bf16_bits_to_f32(v.x >> 16);
+        x[2] = bf16_bits_to_f32(v.y & 0xffffu);
+        x[3] = bf16_bits_to_f32(v.y >> 16);
+    }
+    static __device__ __forceinline__ float load1(const bf16_t* p) {
+        return bf16_bits_to_f32(p->bits);
+    }
+    static __device__ __forceinline__ void store1(bf16_t* p, float x) {
+        p->bits = f32_to_bf16_bits(x);
+    }
+    static __device__ __forceinline__ void store4(bf16_t* p, const float (&x)[4]) {
+        uint2 v;
+        v.x = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+        v.y = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+        *reinterpret_cast<uint2*>(p) = v;
+    }
+};
+
+// Clamp a sequence's [begin, end) to [0, T) so that a device copy of
+// cu_seqlens that disagrees with the validated host copy can never send an
+// access outside the buffers.
+__device__ __forceinline__ void seq_range(const int32_t* cu, int n, int64_t T, int64_t& b,
+                                          int64_t& e) {
+    int64_t lo = cu[n], hi = cu[n + 1];
+    lo = lo < 0 ? 0 : (lo > T ? T : lo);
+    hi = hi < lo ? lo : (hi > T ? T : hi);
+    b = lo;
+    e = hi;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already checked.
+hipError_t launch_state_init(float* state, int64_t n_floats, const float* src,
+                             hipStream_t stream);
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                         const int32_t* slot_idx, int B, int H, int d, void* o,
+                         hipStream_t stream);
+
+hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, kda_dtype dtype, const int32_t* cu,
+                                 int n_seqs, int64_t T, int H, int d, int chunk,
+                                 const float* s0, float* s_final, void* o, hipStream_t stream);
+
+// bf16, d = 128, chunk = 64.
+hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const int32_t* cu, int n_seqs, int64_t T,
+                               int H, const float* s0, float* s_final, void* o,
+                               hipStream_t stream);
+
+hipError_t launch_short_conv_prefill(const void* x, const float* w, kda_dtype dtype,
+                                     const int32_t* cu, int n_seqs, int64_t T, int channels,
+                                     int l2_head_dim, float l2_eps, const void* tail_in,
+                                     void* tail_out, void* y, hipStream_t stream);
+
+hipError_t launch_short_conv_decode(const void* x, const float* w, kda_dtype dtype,
+                                    void* tail, int64_t n_slots, const int32_t* slot_idx, int B,
+                                    int channels, int l2_head_dim, float l2_eps, void* y,
+                                    hipStream_t stream);
+
+}  // namespace kda

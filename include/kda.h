@@ -1,0 +1,177 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) implementation of the Kimi
+ * Delta Attention (KDA) gated delta-rule token mixer.
+ *
+ * The operation (page "Ling-3.1-flash: a 560B hybrid-attention MoE, counted
+ * from its safetensors headers", section "How KDA and MLA split the work"):
+ * every head keeps a d_k x d_v state S, decayed per key channel by
+ * alpha_t = exp(g_t) and written with a per-head scalar strength beta_t,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,
+ *
+ * with q, k, v first passed through a width-4 causal depthwise convolution.
+ * The state is fixed-size per sequence and 128 x 128 fp32 per head in the layer
+ * those pages describe (page "Ling-3.1-flash and the 7:1 hybrid: how much KV
+ * cache does a 560B model need at 1M tokens?", section "How big is the cache
+ * per token, exactly?").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are device pointers to contiguous row-major memory,
+ *   16-byte aligned, owned by the caller.  The library never allocates device
+ *   memory and keeps no per-call state; it caches device properties only.
+ * - Layouts: q, k, g  [tokens, H, d_k];  v, o  [tokens, H, d_v];
+ *   beta [tokens, H];  state [slots, H, d_k, d_v] (d_v contiguous: row i of a
+ *   head's state belongs to key channel i).
+ * - q, k, v and o share one dtype (KDA_F32 or KDA_BF16).  g (the log of the
+ *   decay, alpha = exp(g)), beta and the state are always fp32.  No query scale
+ *   is applied: a caller that wants one scales q.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
+ *   call returns at once.  Arguments are checked on the host before anything is
+ *   enqueued: a failed check returns a non-zero status and enqueues nothing.
+ *   Device-side errors surface at the caller's next synchronisation, as for any
+ *   HIP kernel.
+ * - Thread safety: calls may come from several host threads; the only shared
+ *   state is the read-only device-property cache and a thread-local error text.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad cu_seqlens */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k != d_v) */
+    KDA_ERR_HIP = 3               /* a HIP runtime call failed; see kda_last_error_detail */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/* Text for a status code (static storage). */
+const char* kda_status_string(kda_status s);
+
+/* Human-readable detail of the last failure on the calling thread ("" if none).
+ * Valid until the next call into the library from that thread. */
+const char* kda_last_error_detail(void);
+
+/* Bytes of one sequence's state for one layer: 4 * H * d_k * d_v.
+ * 4 194 304 for H = 64, d_k = d_v = 128; 0 for non-positive sizes. */
+size_t kda_state_bytes(int H, int dk, int dv);
+
+/*
+ * kda_state_init -- set n_slots sequence states to zero (src == NULL) or to a
+ * copy of src.  This is the state the recurrence starts from (S_0).
+ *   state : [n_slots, H, dk, dv] fp32, written.
+ *   src   : [n_slots, H, dk, dv] fp32 or NULL; must not overlap state.
+ * Uses a fill/copy kernel (no memset node), so it may be captured in a graph.
+ */
+kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
+                          const float* src, hipStream_t stream);
+
+/*
+ * kda_prefill_chunked -- run the recurrence over n_seqs packed sequences,
+ * chunk tokens at a time (the chunked/WY form, exact up to rounding).
+ *
+ *   q, k            : [T, H, dk] dtype       v, o : [T, H, dv] dtype
+ *   g               : [T, H, dk] fp32 (log decay; alpha = exp(g))
+ *   beta            : [T, H] fp32
+ *   cu_seqlens_dev  : [n_seqs + 1] int32 on the device
+ *   cu_seqlens_host : the same values in host memory (validated: cu[0] = 0,
+ *                     non-decreasing; T = cu[n_seqs]).  The kernels clamp
+ *                     every index to [0, T), so a device copy that disagrees
+ *                     with the host copy gives wrong results, never an access
+ *                     outside the buffers.
+ *   chunk           : 16, 32 or 64 tokens; the result does not depend on it
+ *                     beyond rounding.
+ *   initial_state   : [n_seqs, H, dk, dv] fp32, or NULL for zeros.
+ *   final_state     : [n_seqs, H, dk, dv] fp32, or NULL (not written).  May be
+ *                     the same pointer as initial_state (in-place update).
+ *   o               : [T, H, dv] dtype, written; must not overlap any input.
+ * Supported: dk == dv in {16, 32, 64, 128}.  bf16 inputs with dk = dv = 128 and
+ * chunk = 64 run the MFMA kernel (bf16 operands, fp32 accumulation, fp32
+ * state); every other case runs the fp32 vector kernel.  T = 0 or n_seqs = 0 is
+ * valid: final states of empty sequences equal their initial states.
+ * Numerical range: the per-chunk sum of g on any channel must stay above about
+ * -80 (exp of its negative must be finite in fp32).
+ */
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, kda_dtype dtype,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               int n_seqs, int H, int dk, int dv, int chunk,
+                               const float* initial_state, float* final_state, void* o,
+                               hipStream_t stream);
+
+/*
+ * kda_decode_step -- advance B sequences by one token each, in place.
+ *
+ *   q, k     : [B, H, dk] dtype        v, o : [B, H, dv] dtype
+ *   g        : [B, H, dk] fp32         beta : [B, H] fp32
+ *   state    : [n_slots, H, dk, dv] fp32, read and written in place.
+ *   slot_idx : [B] int32 on the device giving each sequence's state slot, or
+ *              NULL for slot b = b (then n_slots >= B).  Slots must be
+ *              distinct.  A slot outside [0, n_slots) is not touched and that
+ *              sequence's output is set to NaN.
+ * Supported: dk == dv in {16, 32, 64, 128}.  Each state is read once and
+ * written once (fused form of one recurrence step).
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                           const int32_t* slot_idx, int B, int H, int dk, int dv, void* o,
+                           hipStream_t stream);
+
+/*
+ * kda_short_conv_prefill -- width-4 causal depthwise convolution over packed
+ * sequences, optionally followed by a per-head L2 normalisation (the front end
+ * that q, k and v pass through before the recurrence):
+ *
+ *     y_t[c] = sum_{j=0..3} w[c][j] * x_{t-3+j}[c]      (w[c][3]: current token)
+ *     y_t[head] <- y_t[head] / sqrt(sum y_t[head]^2 + l2_eps)   if l2_head_dim > 0
+ *
+ *   x, y            : [T, channels] dtype (one stream, e.g. the 8192 q channels)
+ *   w               : [channels, 4] fp32
+ *   cu_seqlens_dev/host : as in kda_prefill_chunked
+ *   conv_tail_in    : [n_seqs, 3, channels] dtype: inputs x_{-3}, x_{-2}, x_{-1}
+ *                     before each sequence, or NULL for zero history.
+ *   conv_tail_out   : [n_seqs, 3, channels] dtype, or NULL: receives the last
+ *                     three inputs of each sequence (history included for
+ *                     sequences shorter than three).  May equal conv_tail_in.
+ *   l2_head_dim     : 0 (no normalisation) or a divisor of channels, at most
+ *                     256 and a multiple of 2.
+ * Math is fp32; y is rounded to dtype.  y must not overlap x.
+ */
+kda_status kda_short_conv_prefill(const void* x, const float* w, kda_dtype dtype,
+                                  const int32_t* cu_seqlens_dev,
+                                  const int32_t* cu_seqlens_host, int n_seqs, int channels,
+                                  int l2_head_dim, float l2_eps, const void* conv_tail_in,
+                                  void* conv_tail_out, void* y, hipStream_t stream);
+
+/*
+ * kda_short_conv_decode -- the same convolution for one token per sequence,
+ * shifting each sequence's tail in place.
+ *   x, y      : [B, channels] dtype
+ *   conv_tail : [n_slots, 3, channels] dtype, read and written in place.
+ *   slot_idx  : [B] int32 device array or NULL (slot b = b; then n_slots >= B).
+ *               Out-of-range slots are skipped and their y set to NaN.
+ */
+kda_status kda_short_conv_decode(const void* x, const float* w, kda_dtype dtype,
+                                 void* conv_tail, int64_t n_slots, const int32_t* slot_idx,
+                                 int B, int channels, int l2_head_dim, float l2_eps, void* y,
+                                 hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,164 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/kda.h declares, and rejects bad arguments on the host before anything
+is enqueued.  Fake (never dereferenced) device addresses are used, and every
+call here fails validation, so no HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_99_amd as kda_pkg
+from gated_delta_rule_99_amd.kda import (KDA_BF16, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED,
+                                          KDA_F32)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+A = 0x10000  # fake 16-byte-aligned addresses, never dereferenced
+Bp = 0x20000000
+Cp = 0x40000000
+Dp = 0x60000000
+Ep = 0x80000000
+Fp = 0xA0000000
+Gp = 0xC0000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda_pkg.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(kda_pkg.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_state_bytes(lib):
+    assert lib.kda_state_bytes(64, 128, 128) == 4194304
+    assert lib.kda_state_bytes(0, 128, 128) == 0
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+
+
+def cu_arr(vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def prefill(lib, **kw):
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, cu_dev=Fp, cu_host=cu_arr([0, 8]),
+             n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, o=Gp, stream=None)
+    a.update(kw)
+    return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
+                                   a["cu_dev"], a["cu_host"], a["n"], a["H"], a["dk"], a["dv"],
+                                   a["chunk"], a["s0"], a["sf"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dk=96, dv=96), KDA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dk=128, dv=64), KDA_ERR_UNSUPPORTED, "dk != dv"),
+    (dict(H=0), KDA_ERR_INVALID_ARGUMENT, "positive"),
+    (dict(chunk=48), KDA_ERR_INVALID_ARGUMENT, "chunk"),
+    (dict(dtype=7), KDA_ERR_INVALID_ARGUMENT, "dtype"),
+    (dict(n=-1), KDA_ERR_INVALID_ARGUMENT, "n_seqs"),
+    (dict(cu_host=None), KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host"),
+    (dict(cu_host=cu_arr([1, 8])), KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0]"),
+    (dict(cu_host=cu_arr([0, 8, 4]), n=2), KDA_ERR_INVALID_ARGUMENT, "decreases"),
+    (dict(cu_dev=None), KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_dev"),
+    (dict(q=None), KDA_ERR_INVALID_ARGUMENT, "required"),
+    (dict(k=Bp + 8), KDA_ERR_INVALID_ARGUMENT, "misaligned"),
+    (dict(o=A + 64), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(s0=0x7000000, sf=0x7000040), KDA_ERR_INVALID_ARGUMENT, "overlap"),
+    (dict(sf=A), KDA_ERR_INVALID_ARGUMENT, "overlap"),
+])
+def test_prefill_rejects(lib, kw, status, needle):
+    assert prefill(lib, **kw) == status
+    assert needle in lib.kda_last_error_detail().decode()
+
+
+def test_prefill_nothing_to_do(lib):
+    """n_seqs = 0 is valid and enqueues nothing."""
+    assert prefill(lib, n=0, cu_host=cu_arr([0]), q=None, k=None, v=None, g=None, beta=None,
+                   o=None) == 0
+
+
+def decode(lib, **kw):
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_F32, state=Fp, n_slots=4, slot=None, B=4,
+             H=2, dk=64, dv=64, o=Gp, stream=None)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"], a["state"],
+                               a["n_slots"], a["slot"], a["B"], a["H"], a["dk"], a["dv"], a["o"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dk=48, dv=48), KDA_ERR_UNSUPPORTED, "head dim"),
+    (dict(B=-1), KDA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(n_slots=3), KDA_ERR_INVALID_ARGUMENT, "n_slots"),
+    (dict(state=None), KDA_ERR_INVALID_ARGUMENT, "required"),
+    (dict(state=Fp + 4), KDA_ERR_INVALID_ARGUMENT, "misaligned"),
+    (dict(slot=Gp + 2, n_slots=8), KDA_ERR_INVALID_ARGUMENT, "misaligned"),
+    (dict(o=A), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(state=Dp), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
+])
+def test_decode_rejects(lib, kw, status, needle):
+    assert decode(lib, **kw) == status
+    assert needle in lib.kda_last_error_detail().decode()
+
+
+def test_state_init_rejects(lib):
+    assert lib.kda_state_init(None, 2, 2, 64, 64, None, None) == KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_state_init(A, 2, 2, 64, 32, None, None) == KDA_ERR_UNSUPPORTED
+    assert lib.kda_state_init(A, -1, 2, 64, 64, None, None) == KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_state_init(A, 2, 2, 64, 64, A + 16, None) == KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_state_init(A, 0, 2, 64, 64, None, None) == 0
+
+
+def conv(lib, **kw):
+    a = dict(x=A, w=Bp, dtype=KDA_BF16, cu_dev=Cp, cu_host=cu_arr([0, 10]), n=1, ch=256, l2=128,
+             eps=1e-6, tin=None, tout=None, y=Dp, stream=None)
+    a.update(kw)
+    return lib.kda_short_conv_prefill(a["x"], a["w"], a["dtype"], a["cu_dev"], a["cu_host"], a["n"],
+                                      a["ch"], a["l2"], a["eps"], a["tin"], a["tout"], a["y"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(ch=255), KDA_ERR_INVALID_ARGUMENT, "even"),
+    (dict(l2=96), KDA_ERR_INVALID_ARGUMENT, "l2_head_dim"),
+    (dict(ch=1024, l2=512), KDA_ERR_UNSUPPORTED, "256"),
+    (dict(w=None), KDA_ERR_INVALID_ARGUMENT, "w must"),
+    (dict(eps=-1.0), KDA_ERR_INVALID_ARGUMENT, "l2_eps"),
+    (dict(y=A), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(tin=Ep, tout=Ep + 16), KDA_ERR_INVALID_ARGUMENT, "overlap"),
+    (dict(cu_host=cu_arr([0, 5, 2]), n=2), KDA_ERR_INVALID_ARGUMENT, "decreases"),
+])
+def test_conv_prefill_rejects(lib, kw, status, needle):
+    assert conv(lib, **kw) == status
+    assert needle in lib.kda_last_error_detail().decode()
+
+
+def test_conv_decode_rejects(lib):
+    f = lib.kda_short_conv_decode
+    assert f(A, Bp, KDA_BF16, None, 4, None, 2, 256, 128, 1e-6, Dp, None) == \
+        KDA_ERR_INVALID_ARGUMENT
+    assert f(A, Bp, KDA_BF16, Cp, 1, None, 2, 256, 128, 1e-6, Dp, None) == \
+        KDA_ERR_INVALID_ARGUMENT
+    assert f(A, Bp, KDA_BF16, Cp, 4, None, 2, 256, 128, 1e-6, A, None) == \
+        KDA_ERR_INVALID_ARGUMENT
+
+
+def test_python_binding_raises_on_error():
+    """The binding turns a non-OK status into KdaError (no fallback)."""
+    import torch
+    q = torch.zeros((4, 2, 96))
+    with pytest.raises(kda_pkg.KdaError) as ei:
+        kda_pkg.kda_prefill_chunked(q, q, q, q, torch.zeros((4, 2)), chunk=64, stream=0)
+    assert ei.value.status == KDA_ERR_UNSUPPORTED

@@ -1,0 +1,104 @@
+"""Properties of the GPU path that hold at any size: chunk-size invariance,
+packing, state handoff, value-column separability, run-to-run determinism."""
+import pytest
+import torch
+
+import workloads
+from kda_testutil import TOL_BF16, dev, gpu_or_skip, gpu_prefill, np64, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+
+def kda():
+    gpu_or_skip()
+    import gated_delta_rule_99_amd as m
+    m.load()
+    return m
+
+
+def test_chunk_invariance_f32():
+    """fp32: chunk 16, 32 and 64 agree to fp32 rounding (the chunked form is exact)."""
+    kda()
+    inp = workloads.recurrence_inputs([200, 77], H=2, d=64, dtype="f32", s0_std=0.3, seed=21)
+    res = [gpu_prefill(inp, chunk=c) for c in (16, 32, 64)]
+    for o, S in res[1:]:
+        assert rel_fro(np64(o), np64(res[0][0])) < 1e-5
+        assert rel_fro(np64(S), np64(res[0][1])) < 1e-5
+
+
+def test_chunk_invariance_mfma_vs_vector():
+    """bf16 d=128: the matrix-core kernel (chunk 64) and the vector kernel (chunk
+    16, fp32 math on the same bf16 inputs) agree within the bf16 budget."""
+    kda()
+    inp = workloads.recurrence_inputs([500], H=4, d=128, dtype="bf16", g_mu=3.0, g_sigma=1.0,
+                                      seed=22)
+    o64, S64 = gpu_prefill(inp, chunk=64)
+    o16, S16 = gpu_prefill(inp, chunk=16)
+    e = max(rel_fro(np64(o64), np64(o16)), rel_fro(np64(S64), np64(S16)))
+    print(f"mfma vs vector: {e:.2e}")
+    assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (32, "f32")])
+def test_packing_is_exact(d, dtype):
+    """A packed call equals separate per-sequence calls, bit for bit."""
+    kda()
+    lens = [70, 3, 130]
+    inp = workloads.recurrence_inputs(lens, H=8, d=d, dtype=dtype, s0_std=0.2, seed=23)
+    o, S = gpu_prefill(inp)
+    cu = inp.cu_seqlens.tolist()
+    for n in range(len(lens)):
+        sl = slice(cu[n], cu[n + 1])
+        sub = workloads.RecurrenceInputs(inp.q[sl], inp.k[sl], inp.v[sl], inp.g[sl],
+                                         inp.beta[sl],
+                                         torch.tensor([0, lens[n]], dtype=torch.int32),
+                                         inp.S0[n:n + 1], dtype, inp.chunk)
+        on, Sn = gpu_prefill(sub)
+        assert torch.equal(on, o[sl]) and torch.equal(Sn[0], S[n])
+
+
+def test_handoff_prefill_prefill():
+    """prefill(T1) then prefill(T2) from its final state equals prefill(T1 + T2)."""
+    kda()
+    inp = workloads.recurrence_inputs([300], H=4, d=128, dtype="bf16", s0_std=0.1, seed=24)
+    o, S = gpu_prefill(inp)
+    T1 = 137
+    a = workloads.RecurrenceInputs(inp.q[:T1], inp.k[:T1], inp.v[:T1], inp.g[:T1],
+                                   inp.beta[:T1], torch.tensor([0, T1], dtype=torch.int32),
+                                   inp.S0, "bf16", 64)
+    oa, Sa = gpu_prefill(a)
+    b = workloads.RecurrenceInputs(inp.q[T1:], inp.k[T1:], inp.v[T1:], inp.g[T1:],
+                                   inp.beta[T1:],
+                                   torch.tensor([0, 300 - T1], dtype=torch.int32), Sa.cpu(),
+                                   "bf16", 64)
+    ob, Sb = gpu_prefill(b)
+    e = max(rel_fro(np64(torch.cat([oa, ob])), np64(o)), rel_fro(np64(Sb), np64(S)))
+    print(f"handoff: {e:.2e}")
+    assert e <= TOL_BF16
+
+
+def test_value_column_separability():
+    """Columns of o and S depend only on the same columns of v and S_0: changing
+    v and S_0 in value columns 64..127 leaves columns 0..63 unchanged, bit for bit
+    (the kernels slice the state by value columns)."""
+    kda()
+    inp = workloads.recurrence_inputs([150], H=2, d=128, dtype="bf16", s0_std=0.2, seed=25)
+    o1, S1 = gpu_prefill(inp)
+    v2 = inp.v.clone()
+    v2[..., 64:] = -v2[..., 64:] * 3
+    S02 = inp.S0.clone()
+    S02[..., 64:] = 1.0
+    inp2 = workloads.RecurrenceInputs(inp.q, inp.k, v2, inp.g, inp.beta, inp.cu_seqlens, S02,
+                                      "bf16", 64)
+    o2, S2 = gpu_prefill(inp2)
+    assert torch.equal(o1[..., :64], o2[..., :64])
+    assert torch.equal(S1[..., :64], S2[..., :64])
+
+
+def test_determinism():
+    """Two identical runs give identical bytes (no race on LDS)."""
+    kda()
+    inp = workloads.recurrence_inputs([257, 64], H=8, d=128, dtype="bf16", s0_std=0.1, seed=26)
+    o1, S1 = gpu_prefill(inp)
+    o2, S2 = gpu_prefill(inp)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)

@@ -1,0 +1,149 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times.  Where the oracle cannot afford every head, it runs on a sample
+of heads (the recurrence is independent per head) and those heads are compared
+in full: every token's output and every sequence's final state.
+
+Tolerances: max relative Frobenius error of outputs and final states <= 1e-4 for
+fp32 inputs, <= 2e-2 for bf16 inputs with fp32 state."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, gpu_prefill, np64, oracle_on,
+                          per_seq_errors, rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+
+def kda():
+    gpu_or_skip()
+    import gated_delta_rule_99_amd as m
+    m.load()
+    return m
+
+
+def test_config_tiny_f32():
+    kda()
+    inp = workloads.tiny_f32()
+    o, S = gpu_prefill(inp)
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
+    print(f"tiny f32: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL_F32 and es <= TOL_F32
+
+
+def test_config_ling_prefill():
+    """B=1, H=64, T=8192, d=128, chunk 64, bf16; every head checked."""
+    kda()
+    inp = workloads.ling_prefill()
+    o, S = gpu_prefill(inp)
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
+    # per-head worst case as a diagnostic
+    ph = max(rel_fro(np64(o[:, h]), o_ref[:, h]) for h in range(inp.H))
+    print(f"ling prefill: o {eo:.2e} S {es:.2e} worst head o {ph:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_config_decode_batch():
+    """B=256 x H=64 decode step from random N(0, 0.02) states; every state checked."""
+    m = kda()
+    inp = workloads.decode_batch()
+    state = dev(inp.S0)
+    o = m.kda_decode_step(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), state)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = per_seq_errors(np64(o), o_ref, np64(state), S_ref, inp.cu_seqlens)
+    print(f"decode batch: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+PACKED_HEADS = (0, 21, 42, 63)
+
+
+def test_config_packed_long():
+    """Sequences of 131072, 65536, 16384 and 1000 tokens, nonzero initial states;
+    every sequence's outputs and final state on four sampled heads."""
+    kda()
+    inp = workloads.packed_long()
+    o, S = gpu_prefill(inp)
+    heads = list(PACKED_HEADS)
+    o_s = np64(o[:, heads])
+    S_s = np64(S[:, heads])
+    del o, S
+    o_ref, S_ref = oracle_on(inp, heads=heads)
+    eo, es = per_seq_errors(o_s, o_ref, S_s, S_ref, inp.cu_seqlens)
+    # early outputs carry the initial state's influence: check them on their own
+    e_early = max(rel_fro(o_s[c:c + 64], o_ref[c:c + 64]) for c in inp.cu_seqlens[:-1].tolist())
+    print(f"packed long: o {eo:.2e} S {es:.2e} first-64-token o {e_early:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and e_early <= TOL_BF16
+
+
+MIXER_HEADS = (0, 31, 63)
+
+
+def run_mixer_gpu(m, mi):
+    """Conv + L2 front end, chunked prefill, then recurrent decode steps, all
+    through the C ABI.  Returns (o_prefill, o_decode, final_state)."""
+    H, d, Tp = mi.H, mi.d, mi.t_prefill
+    Cch = H * d
+    w = {s: dev(getattr(mi, "w_" + s)) for s in "qkv"}
+    x = {s: getattr(mi, "x_" + s) for s in "qkv"}
+    tails = {s: torch.empty((1, 3, Cch), dtype=torch.bfloat16, device="cuda") for s in "qkv"}
+    y = {}
+    for s in "qkv":
+        y[s] = m.kda_short_conv_prefill(dev(x[s][:Tp]), w[s], l2_head_dim=0 if s == "v" else d,
+                                        l2_eps=1e-6, conv_tail_out=tails[s])
+    g = dev(mi.g)
+    beta = dev(mi.beta)
+    o_pre, S = m.kda_prefill_chunked(y["q"].view(Tp, H, d), y["k"].view(Tp, H, d),
+                                     y["v"].view(Tp, H, d), g[:Tp].contiguous(),
+                                     beta[:Tp].contiguous(), chunk=mi.chunk)
+    outs = []
+    xd = {s: dev(x[s][Tp:]) for s in "qkv"}
+    for t in range(mi.n_decode):
+        yd = {}
+        for s in "qkv":
+            yd[s] = m.kda_short_conv_decode(xd[s][t:t + 1], w[s], tails[s],
+                                            l2_head_dim=0 if s == "v" else d, l2_eps=1e-6)
+        outs.append(m.kda_decode_step(yd["q"].view(1, H, d), yd["k"].view(1, H, d),
+                                      yd["v"].view(1, H, d), g[Tp + t:Tp + t + 1],
+                                      beta[Tp + t:Tp + t + 1], S))
+    torch.cuda.synchronize()
+    return o_pre, torch.cat(outs), S
+
+
+def oracle_mixer(mi, heads):
+    """Oracle: conv (fp64) over all prefill + decode tokens of the sampled heads'
+    channels, L2 per head on q and k, one recurrence over every token."""
+    d = mi.d
+    cols = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
+    streams = {}
+    for s in "qkv":
+        xs = np64(getattr(mi, "x_" + s)[:, cols])
+        ws = np64(getattr(mi, "w_" + s)[cols])
+        ys, _ = oracle.short_conv(xs, ws)
+        if s != "v":
+            ys = oracle.l2norm_heads(ys, d, eps=1e-6)
+        streams[s] = ys.reshape(ys.shape[0], len(heads), d)
+    g = np64(mi.g[:, list(heads)])
+    beta = np64(mi.beta[:, list(heads)])
+    return oracle.recurrence(streams["q"], streams["k"], streams["v"], g, beta)
+
+
+def test_config_mixer_handoff():
+    """Conv + L2 + prefill of 32768 tokens, then 512 decode steps continuing from
+    the prefill state and conv tails, against one 33280-token oracle run."""
+    m = kda()
+    mi = workloads.mixer()
+    o_pre, o_dec, S = run_mixer_gpu(m, mi)
+    heads = list(MIXER_HEADS)
+    o_ref, S_ref = oracle_mixer(mi, heads)
+    Tp = mi.t_prefill
+    e_pre = rel_fro(np64(o_pre[:, heads]), o_ref[:Tp])
+    e_dec = rel_fro(np64(o_dec[:, heads]), o_ref[Tp:])
+    e_S = rel_fro(np64(S[0, heads]), S_ref[0])
+    print(f"mixer: prefill o {e_pre:.2e} decode o {e_dec:.2e} S {e_S:.2e}")
+    assert e_pre <= TOL_BF16 and e_dec <= TOL_BF16 and e_S <= TOL_BF16
