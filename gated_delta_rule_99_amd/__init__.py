@@ -13,6 +13,7 @@ from .kda import (  # noqa: F401
     KdaError,
     kda_decode_step,
     kda_prefill_chunked,
+    kda_prefill_workspace_bytes,
     kda_short_conv_decode,
     kda_short_conv_prefill,
     kda_state_bytes,

@@ -34,6 +34,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// Shapes that run on the matrix cores.
+bool mfma_shape(kda_dtype dtype, int dk, int dv, int chunk) {
+    return dtype == KDA_BF16 && dk == 128 && dv == 128 && chunk == 64;
+}
+
 size_t elem_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
 
 // Common head-shape checks.  Returns KDA_OK or an error with detail set.
@@ -105,7 +110,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
                                const float* initial_state, float* final_state, void* o,
-                               hipStream_t stream) {
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const char* fn = "kda_prefill_chunked";
     g_detail[0] = 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16)
@@ -149,14 +154,45 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
          overlaps(final_state, sbytes, v, n_qk * es) || overlaps(final_state, sbytes, g, n_qk * 4)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state overlaps an input", fn);
 
+    const bool mfma = mfma_shape(dtype, dk, dv, chunk);
+    const size_t ws_need = mfma ? kda::prefill_split_workspace_bytes(n_seqs, H) : 0;
+    if (mfma && workspace) {
+        if (workspace_bytes < ws_need)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes, %zu needed", fn,
+                        workspace_bytes, ws_need);
+        if (!aligned16(workspace))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned workspace", fn);
+        if (overlaps(workspace, ws_need, q, n_qk * es) || overlaps(workspace, ws_need, k, n_qk * es) ||
+            overlaps(workspace, ws_need, v, n_qk * es) || overlaps(workspace, ws_need, g, n_qk * 4) ||
+            overlaps(workspace, ws_need, beta, n_bt * 4) || overlaps(workspace, ws_need, o, n_qk * es) ||
+            overlaps(workspace, ws_need, initial_state, sbytes) ||
+            overlaps(workspace, ws_need, final_state, sbytes))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps another argument", fn);
+    }
+
     hipError_t err;
-    if (dtype == KDA_BF16 && d == 128 && chunk == 64)
+    if (mfma && workspace) {
+        int max_chunks = 0;
+        for (int n = 0; n < n_seqs; ++n) {
+            const int nc = (int)(((int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n] + 63) / 64);
+            max_chunks = nc > max_chunks ? nc : max_chunks;
+        }
+        err = kda::launch_prefill_split(q, k, v, g, beta, cu_seqlens_dev, n_seqs, T, H,
+                                        max_chunks, initial_state, final_state, o, workspace,
+                                        stream);
+    } else if (mfma)
         err = kda::launch_prefill_mfma(q, k, v, g, beta, cu_seqlens_dev, n_seqs, T, H,
                                        initial_state, final_state, o, stream);
     else
         err = kda::launch_prefill_vector(q, k, v, g, beta, dtype, cu_seqlens_dev, n_seqs, T, H,
                                          d, chunk, initial_state, final_state, o, stream);
     return hip_status(err, "kda_prefill_chunked launch");
+}
+
+size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
+                                   kda_dtype dtype) {
+    if (n_seqs <= 0 || H <= 0 || !mfma_shape(dtype, dk, dv, chunk)) return 0;
+    return kda::prefill_split_workspace_bytes(n_seqs, H);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,

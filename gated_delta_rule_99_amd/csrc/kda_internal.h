@@ -101,6 +101,16 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                int H, const float* s0, float* s_final, void* o,
                                hipStream_t stream);
 
+// bf16, d = 128, chunk = 64, two kernels through a caller workspace of
+// prefill_split_workspace_bytes(n_seqs, H) bytes; max_chunks = the longest
+// sequence's chunk count.
+int prefill_split_window(int n_seqs, int H);
+size_t prefill_split_workspace_bytes(int n_seqs, int H);
+hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const int32_t* cu, int n_seqs, int64_t T,
+                                int H, int max_chunks, const float* s0, float* s_final, void* o,
+                                void* workspace, hipStream_t stream);
+
 hipError_t launch_short_conv_prefill(const void* x, const float* w, kda_dtype dtype,
                                      const int32_t* cu, int n_seqs, int64_t T, int channels,
                                      int l2_head_dim, float l2_eps, const void* tail_in,

@@ -38,7 +38,8 @@ _SIGNATURES = {
     "kda_state_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
     "kda_state_init": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
-                                   _i32, _i32, _vp, _vp, _vp, _vp]),
+                                   _i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32,
                                _i32, _vp, _vp]),
     "kda_short_conv_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _vp,
@@ -120,11 +121,35 @@ def kda_state_init(state: torch.Tensor, src: torch.Tensor | None = None, stream=
     return state
 
 
+def kda_prefill_workspace_bytes(n_seqs: int, H: int, dk: int, dv: int, chunk: int,
+                                dtype: torch.dtype) -> int:
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_prefill_workspace_bytes(n_seqs, H, dk, dv, chunk, code))
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    """A cached uint8 device buffer of at least nbytes (one per device; reused by
+    later calls, which the ABI allows when they are ordered on one stream)."""
+    key = torch.device(device)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
 def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
                         initial_state=None, final_state=None, o=None,
-                        output_final_state: bool = True, cu_seqlens_host=None, stream=None):
+                        output_final_state: bool = True, cu_seqlens_host=None,
+                        workspace="auto", stream=None):
     """Chunked prefill over packed sequences.  q, k, g: [T, H, dk]; v: [T, H, dv];
-    beta: [T, H].  Returns (o, final_state or None)."""
+    beta: [T, H].  Returns (o, final_state or None).
+
+    workspace: "auto" (a cached device buffer of kda_prefill_workspace_bytes),
+    a uint8 device tensor, or None (no workspace: the fused kernel)."""
     T, H, dk = q.shape
     dv = v.shape[2]
     cu_dev, cu_host = _cu_pair(cu_seqlens, cu_seqlens_host, T, q.device)
@@ -133,10 +158,16 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', a tensor or None")
+        need = kda_prefill_workspace_bytes(n_seqs, H, dk, dv, chunk, q.dtype)
+        workspace = _workspace(need, q.device) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kda_prefill_chunked(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _ptr(cu_dev),
         cu_host.data_ptr(), n_seqs, H, dk, dv, int(chunk), _ptr(initial_state),
-        _ptr(final_state), _ptr(o), _stream(stream)))
+        _ptr(final_state), _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
     return o, final_state
 
 

@@ -20,7 +20,8 @@
  * ---------------------------------------
  * - All tensor arguments are device pointers to contiguous row-major memory,
  *   16-byte aligned, owned by the caller.  The library never allocates device
- *   memory and keeps no per-call state; it caches device properties only.
+ *   memory and keeps no per-call state: scratch memory, where a path uses
+ *   some, is a workspace argument that the caller provides.
  * - Layouts: q, k, g  [tokens, H, d_k];  v, o  [tokens, H, d_v];
  *   beta [tokens, H];  state [slots, H, d_k, d_v] (d_v contiguous: row i of a
  *   head's state belongs to key channel i).
@@ -99,19 +100,45 @@ kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
  *   final_state     : [n_seqs, H, dk, dv] fp32, or NULL (not written).  May be
  *                     the same pointer as initial_state (in-place update).
  *   o               : [T, H, dv] dtype, written; must not overlap any input.
+ *   workspace       : device scratch of at least workspace_bytes =
+ *                     kda_prefill_workspace_bytes(...) bytes, 16-byte aligned,
+ *                     owned by the caller, not overlapping any other argument;
+ *                     or NULL.  Its contents on entry do not matter and on
+ *                     return are unspecified.  Calls that share one workspace
+ *                     must be ordered (same stream, or synchronised).
  * Supported: dk == dv in {16, 32, 64, 128}.  bf16 inputs with dk = dv = 128 and
- * chunk = 64 run the MFMA kernel (bf16 operands, fp32 accumulation, fp32
- * state); every other case runs the fp32 vector kernel.  T = 0 or n_seqs = 0 is
- * valid: final states of empty sequences equal their initial states.
+ * chunk = 64 run on the matrix cores (bf16 operands, fp32 accumulation, fp32
+ * state): with a workspace, a chunk-parallel kernel first forms every chunk's
+ * state-independent operands (decay-scaled keys and queries, the inverse
+ * (I + N)^{-1}, the causal query-key products) and a second kernel runs the
+ * sequential state pass over them; with workspace == NULL one fused kernel does
+ * both (slower: its per-chunk work is repeated for every quarter of the value
+ * dimension).  Every other case runs the fp32 vector kernel and ignores the
+ * workspace.  T = 0 or n_seqs = 0 is valid: final states of empty sequences
+ * equal their initial states.
  * Numerical range: the per-chunk sum of g on any channel must stay above about
  * -80 (exp of its negative must be finite in fp32).
+ * Errors: KDA_ERR_INVALID_ARGUMENT also for a non-NULL workspace smaller than
+ * kda_prefill_workspace_bytes or overlapping another argument.
  */
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
                                const float* g, const float* beta, kda_dtype dtype,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
                                const float* initial_state, float* final_state, void* o,
-                               hipStream_t stream);
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_prefill_workspace_bytes -- size of the workspace that lets
+ * kda_prefill_chunked use its two-kernel matrix-core path for this shape; 0 when
+ * the shape runs a path that needs none.  Depends only on n_seqs and H for the
+ * matrix-core shapes: a fixed-size state carry (64 KiB per sequence and head)
+ * plus per-chunk operand tiles for a window of at most 32 chunks per sequence,
+ * the window sized to keep the tiles within about 100 MiB where the batch allows
+ * (at least one chunk per sequence and head: 66 304 bytes each).
+ */
+size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
+                                   kda_dtype dtype);
 
 /*
  * kda_decode_step -- advance B sequences by one token each, in place.

@@ -66,13 +66,15 @@ def oracle_on(inp, heads=None, precision="f64"):
                              precision=precision)
 
 
-def gpu_prefill(inp, chunk=None):
+def gpu_prefill(inp, chunk=None, workspace="auto"):
+    """Prefill through the binding; workspace None selects the fused matrix-core
+    kernel, "auto" the two-kernel path (bf16, d = 128, chunk 64)."""
     import gated_delta_rule_99_amd as kda
 
     o, S = kda.kda_prefill_chunked(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g),
                                    dev(inp.beta), cu_seqlens=dev(inp.cu_seqlens),
                                    cu_seqlens_host=inp.cu_seqlens,
                                    chunk=inp.chunk if chunk is None else chunk,
-                                   initial_state=dev(inp.S0))
+                                   initial_state=dev(inp.S0), workspace=workspace)
     torch.cuda.synchronize()
     return o, S

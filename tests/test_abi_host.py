@@ -54,11 +54,13 @@ def cu_arr(vals):
 
 def prefill(lib, **kw):
     a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, cu_dev=Fp, cu_host=cu_arr([0, 8]),
-             n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, o=Gp, stream=None)
+             n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, o=Gp, ws=None, ws_bytes=0,
+             stream=None)
     a.update(kw)
     return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
                                    a["cu_dev"], a["cu_host"], a["n"], a["H"], a["dk"], a["dv"],
-                                   a["chunk"], a["s0"], a["sf"], a["o"], a["stream"])
+                                   a["chunk"], a["s0"], a["sf"], a["o"], a["ws"], a["ws_bytes"],
+                                   a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -77,10 +79,29 @@ def prefill(lib, **kw):
     (dict(o=A + 64), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(s0=0x7000000, sf=0x7000040), KDA_ERR_INVALID_ARGUMENT, "overlap"),
     (dict(sf=A), KDA_ERR_INVALID_ARGUMENT, "overlap"),
+    (dict(ws=0x9000000, ws_bytes=1024), KDA_ERR_INVALID_ARGUMENT, "needed"),
+    (dict(ws=0x9000008, ws_bytes=1 << 30), KDA_ERR_INVALID_ARGUMENT, "misaligned workspace"),
+    (dict(ws=A - 4096, ws_bytes=1 << 30), KDA_ERR_INVALID_ARGUMENT, "workspace overlaps"),
 ])
 def test_prefill_rejects(lib, kw, status, needle):
     assert prefill(lib, **kw) == status
     assert needle in lib.kda_last_error_detail().decode()
+
+
+def test_prefill_workspace_bytes(lib):
+    """State carry (64 KiB per sequence and head) plus a window of 66 304-byte
+    chunk tiles; 0 for shapes that run without a workspace."""
+    f = lib.kda_prefill_workspace_bytes
+    # one sequence, 64 heads: the 100 MiB tile budget allows a 24-chunk window
+    assert f(1, 64, 128, 128, 64, KDA_BF16) == 64 * 65536 + 24 * 64 * 66304
+    # small batches stop at 32 chunks per window
+    assert f(3, 2, 128, 128, 64, KDA_BF16) == 6 * 65536 + 3 * 32 * 2 * 66304
+    # large batches keep one chunk per sequence and head
+    assert f(256, 64, 128, 128, 64, KDA_BF16) == 256 * 64 * (65536 + 66304)
+    assert f(1, 64, 128, 128, 64, KDA_F32) == 0
+    assert f(1, 64, 64, 64, 64, KDA_BF16) == 0
+    assert f(1, 64, 128, 128, 32, KDA_BF16) == 0
+    assert f(0, 64, 128, 128, 64, KDA_BF16) == 0
 
 
 def test_prefill_nothing_to_do(lib):

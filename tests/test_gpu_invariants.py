@@ -39,13 +39,14 @@ def test_chunk_invariance_mfma_vs_vector():
     assert e <= TOL_BF16
 
 
-@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (32, "f32")])
-def test_packing_is_exact(d, dtype):
+@pytest.mark.parametrize("d,dtype,ws", [(128, "bf16", "auto"), (128, "bf16", None),
+                                         (32, "f32", None)])
+def test_packing_is_exact(d, dtype, ws):
     """A packed call equals separate per-sequence calls, bit for bit."""
     kda()
     lens = [70, 3, 130]
     inp = workloads.recurrence_inputs(lens, H=8, d=d, dtype=dtype, s0_std=0.2, seed=23)
-    o, S = gpu_prefill(inp)
+    o, S = gpu_prefill(inp, workspace=ws)
     cu = inp.cu_seqlens.tolist()
     for n in range(len(lens)):
         sl = slice(cu[n], cu[n + 1])
@@ -53,8 +54,21 @@ def test_packing_is_exact(d, dtype):
                                          inp.beta[sl],
                                          torch.tensor([0, lens[n]], dtype=torch.int32),
                                          inp.S0[n:n + 1], dtype, inp.chunk)
-        on, Sn = gpu_prefill(sub)
+        on, Sn = gpu_prefill(sub, workspace=ws)
         assert torch.equal(on, o[sl]) and torch.equal(Sn[0], S[n])
+
+
+def test_split_and_fused_agree():
+    """The two matrix-core paths compute the same chunked form: they agree far
+    inside the bf16 budget on a multi-chunk, multi-head input."""
+    kda()
+    inp = workloads.recurrence_inputs([700, 300], H=8, d=128, dtype="bf16", g_mu=3.0,
+                                      g_sigma=1.0, s0_std=0.3, seed=24)
+    o1, S1 = gpu_prefill(inp, workspace="auto")
+    o2, S2 = gpu_prefill(inp, workspace=None)
+    e = max(rel_fro(np64(o1), np64(o2)), rel_fro(np64(S1), np64(S2)))
+    print(f"split vs fused: {e:.2e}")
+    assert e <= TOL_BF16 / 4
 
 
 def test_handoff_prefill_prefill():

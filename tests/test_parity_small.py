@@ -69,28 +69,58 @@ def test_prefill_ragged(d, chunk, dtype):
     assert eo <= tol and es <= tol
 
 
+# workspace argument of the binding: "auto" runs the two-kernel matrix-core path
+# (chunk-parallel operand kernel, then the state pass), None the fused kernel
+PATHS = {"split": "auto", "fused": None}
+
+
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("H", [8, 3])
-def test_mfma_prefill_multichunk(H):
-    """bf16, d=128, chunk 64 (matrix-core kernel): lengths around chunk multiples,
+def test_mfma_prefill_multichunk(H, path):
+    """bf16, d=128, chunk 64 (matrix-core kernels): lengths around chunk multiples,
     nonzero states; H=8 uses the XCD-grouped placement, H=3 the plain one."""
     kda()
     inp = workloads.recurrence_inputs([64, 65, 127, 128, 1, 300], H=H, d=128, dtype="bf16",
                                       chunk=64, g_mu=3.0, g_sigma=1.0, s0_std=0.5, seed=99 + H)
-    o, S = gpu_prefill(inp)
+    o, S = gpu_prefill(inp, workspace=PATHS[path])
     o_ref, S_ref = oracle_on(inp)
     eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
-    print(f"mfma H={H}: o {eo:.2e} S {es:.2e}")
+    print(f"mfma {path} H={H}: o {eo:.2e} S {es:.2e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
-def test_prefill_empty_sequences_keep_state():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_mfma_prefill_multiwindow(path):
+    """Sequences longer than one 32-chunk window of the two-kernel path (state
+    carried across windows), next to empty, 1-token and ragged ones."""
+    kda()
+    inp = workloads.recurrence_inputs([4480, 2100, 64, 0, 1, 130], H=2, d=128, dtype="bf16",
+                                      chunk=64, g_mu=3.0, g_sigma=1.0, s0_std=0.5, seed=123)
+    o, S = gpu_prefill(inp, workspace=PATHS[path])
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
+    print(f"mfma {path} multiwindow: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_prefill_empty_sequences_keep_state(path):
     """Zero-length sequences: final state equals the initial state, bit for bit."""
     kda()
     inp = workloads.recurrence_inputs([0, 5, 0], H=2, d=128, dtype="bf16", chunk=64,
                                       s0_std=1.0, seed=5)
-    o, S = gpu_prefill(inp)
+    o, S = gpu_prefill(inp, workspace=PATHS[path])
     S0 = inp.S0
     assert torch.equal(S.cpu()[0], S0[0]) and torch.equal(S.cpu()[2], S0[2])
+
+
+def test_prefill_all_empty():
+    """Only empty sequences (T = 0): final states are copies of the initial ones."""
+    kda()
+    inp = workloads.recurrence_inputs([0, 0], H=2, d=128, dtype="bf16", chunk=64,
+                                      s0_std=1.0, seed=6)
+    o, S = gpu_prefill(inp)
+    assert o.numel() == 0 and torch.equal(S.cpu(), inp.S0)
 
 
 def test_state_init():
