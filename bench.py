@@ -26,11 +26,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "KDA layer tokens/s (H=64,d=128 prefill); decode state GB/s vs HBM peak"
-PREFILL_KERNEL = "prefill_mfma_kernel"
+# The prefill is one call of kda_prefill_chunked: per window of up to 32 chunks, a
+# chunk-parallel operand kernel (prep_kernel) then the state pass (state_kernel).
+# Its roofline is taken over the whole call.
+PREFILL_KERNEL = "prefill"
+PREFILL_KERNELS = "prep_kernel + state_kernel (kda_prefill_split.hip), all windows of one call"
 DECODE_KERNEL = "decode_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SOURCES = {
-    PREFILL_KERNEL: os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc", "kda_prefill_mfma.hip"),
+    PREFILL_KERNEL: os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc", "kda_prefill_split.hip"),
     DECODE_KERNEL: os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc", "kda_decode.hip"),
 }
 
@@ -41,8 +45,9 @@ def source_sha(kernel):
 
 
 def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, scaled by
-    the copy-kernel calibration; None if absent or taken on other kernel source."""
+    """HBM bytes per launch (for the prefill: per call, summed over its dispatches)
+    from the committed rocprofv3 counter summary, scaled by the copy-kernel
+    calibration; None if absent or taken on other kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)[kernel]
@@ -180,7 +185,7 @@ def main():
                                    "zero initial state",
                        "global_batch": 1, "seq_len": T, "heads": H, "head_dim": d,
                        "chunk": C, "parallelism": "none (1 GPU)"},
-            "roofline": {"bound": "hbm", "kernel": PREFILL_KERNEL, "achieved": achieved,
+            "roofline": {"bound": "hbm", "kernel": PREFILL_KERNELS, "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "traffic": traffic, "kernel_ms": kern_ms,
                          "algorithmic_bytes": alg_bytes},

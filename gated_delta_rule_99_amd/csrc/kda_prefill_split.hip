@@ -12,9 +12,8 @@
 // the exact lane order of the state pass's MFMA operands (each lane later
 // reads one contiguous 16-byte fragment).  state_kernel then runs the serial
 // chain per (sequence, head, 32-column slice), streaming those fragments.
-// The sequence is processed in windows of W chunks (prep for the window, then
-// the state pass over it), so one window's tiles stay small enough for the
-// MI355X's 256 MB last-level cache and the workspace stays bounded; the fp32
+// The sequence is processed in windows of up to 32 chunks (prep for the
+// window, then the state pass over it), which bounds the workspace; the fp32
 // state is carried between windows in the workspace.
 //
 // Workspace tile of one (sequence, window chunk, head), byte offsets:
@@ -34,7 +33,7 @@ namespace sp {
 
 constexpr int D = 128, C = 64, DVS = 32, NS = D / DVS;
 constexpr int MAX_WIN = 32;                 // chunks per window, at most
-constexpr size_t TILE_BUDGET = 100u << 20;  // bytes of one window's tiles, at most
+constexpr size_t TILE_BUDGET = 192u << 20;  // bytes of one window's tiles, at most
 constexpr int LDK = 136, LDT = 72, LDO = 40, LDV = 68;
 constexpr int TILE = 66304;
 constexpr int OFF_KT = 0, OFF_QT = 16384, OFF_KBT = 32768, OFF_T = 49152, OFF_P = 57344,
@@ -405,6 +404,7 @@ struct StateSmem {
 struct Frags {
     bf16x8 K[4], Q[4], Kb[2][2], T[2], P[2];
     float4 bet, gam[2];
+    uint4 v;  // this thread's 8 bf16 of the chunk's V slice
 };
 
 __global__ void __launch_bounds__(256)
@@ -462,35 +462,29 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
     const size_t hoff = (size_t)h * D;
     const int rowb = (int)(row * 2);
     const int vrow = tid >> 2, vcol = 8 * (tid & 3), voff_v = vrow * rowb + vcol * 2;
+    // Rows of chunk c inside this window, 0 outside it.  Every load and store
+    // below is issued unconditionally through a buffer window of that many rows
+    // (a zero-size window turns it into a no-op), so the number of memory
+    // operations in flight is the same on every path and the waits before the
+    // first use of each prefetched set stay partial.
     auto chunk_len = [&](int c) -> int {
+        if (c < c_beg || c >= c_end) return 0;
         const int64_t rem = te - (tb + (int64_t)c * C);
         return rem < C ? (int)rem : C;
     };
-    auto tile_of = [&](int c) {
-        return window(ws_tiles + ((size_t)(n * win + (c - w0)) * H + h) * TILE, TILE);
+    // Fragment loads of chunk c, in four groups so that they can be spread over
+    // the segments of a step (a group is ~5 loads of 1 KB per wave).
+    auto tile_rsrc = [&](int c) {
+        const int cc = c < c_end ? c : c_beg;  // keep the address inside the workspace
+        return window(ws_tiles + ((size_t)(n * win + (cc - w0)) * H + h) * TILE,
+                      c < c_end ? TILE : 0);
     };
-    auto load_frags = [&](int c, Frags& f, uint4& vraw) {
-        const auto rt = tile_of(c);
+    auto load_a = [&](int c, Frags& f) {  // K, beta, Gam, V
+        const auto rt = tile_rsrc(c);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 4; ++kk)
             f.K[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
                 rt, OFF_KT + ((cw * 4 + kk) * 64 + lane) * 16, 0, 0));
-            f.Q[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
-                rt, OFF_QT + ((cw * 4 + kk) * 64 + lane) * 16, 0, 0));
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                f.Kb[a][kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
-                    rt, OFF_KBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16, 0, 0));
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            f.T[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
-                rt, OFF_T + ((cw * 2 + kk) * 64 + lane) * 16, 0, 0));
-            f.P[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
-                rt, OFF_P + ((cw * 2 + kk) * 64 + lane) * 16, 0, 0));
-        }
         const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rt, OFF_BETA + (16 * cw + 4 * q4) * 4,
                                                               0, 0);
         f.bet = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]),
@@ -502,44 +496,80 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
             f.gam[a] = make_float4(__uint_as_float(gg[0]), __uint_as_float(gg[1]),
                                    __uint_as_float(gg[2]), __uint_as_float(gg[3]));
         }
-        const auto rv = window(v + (size_t)(tb + (int64_t)c * C) * row + hoff + j0,
+        const int cc = c < c_end ? c : c_beg;
+        const auto rv = window(v + (size_t)(tb + (int64_t)cc * C) * row + hoff + j0,
                                chunk_len(c) * rowb);
         const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, 0, 0);
-        vraw = make_uint4(x[0], x[1], x[2], x[3]);
+        f.v = make_uint4(x[0], x[1], x[2], x[3]);
+    };
+    auto load_b = [&](int c, Frags& f) {  // Q
+        const auto rt = tile_rsrc(c);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            f.Q[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
+                rt, OFF_QT + ((cw * 4 + kk) * 64 + lane) * 16, 0, 0));
+    };
+    auto load_c = [&](int c, Frags& f) {  // Kb^T
+        const auto rt = tile_rsrc(c);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                f.Kb[a][kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
+                    rt, OFF_KBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16, 0, 0));
+    };
+    auto load_d = [&](int c, Frags& f) {  // T, P
+        const auto rt = tile_rsrc(c);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            f.T[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
+                rt, OFF_T + ((cw * 2 + kk) * 64 + lane) * 16, 0, 0));
+            f.P[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
+                rt, OFF_P + ((cw * 2 + kk) * 64 + lane) * 16, 0, 0));
+        }
+    };
+    auto load_frags = [&](int c, Frags& f) {
+        load_a(c, f);
+        load_b(c, f);
+        load_c(c, f);
+        load_d(c, f);
     };
     auto flush_o = [&](int c) {
-        const auto ro = window(o + (size_t)(tb + (int64_t)c * C) * row + hoff + j0,
+        const int cc = c >= c_beg ? c : c_beg;
+        const auto ro = window(o + (size_t)(tb + (int64_t)cc * C) * row + hoff + j0,
                                chunk_len(c) * rowb);
         const uint4 x = *reinterpret_cast<const uint4*>(sm.O + vrow * LDO + vcol);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, ro, voff_v, 0, 0);
     };
 
-    Frags cur, nxt;
-    uint4 vcur, vnxt;
-    load_frags(c_beg, cur, vcur);
+    // Three fragment sets in rotation: while chunk c runs, the loads of chunk
+    // c + 1 are in flight since one chunk and those of c + 2 are being issued.
+    Frags F0, F1, F2;
+    load_frags(c_beg, F0);
+    load_frags(c_beg + 1, F1);
     // G = Gam * S for the first chunk of the window
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            S[a][jb][0] *= cur.gam[a].x; S[a][jb][1] *= cur.gam[a].y;
-            S[a][jb][2] *= cur.gam[a].z; S[a][jb][3] *= cur.gam[a].w;
+            S[a][jb][0] *= F0.gam[a].x; S[a][jb][1] *= F0.gam[a].y;
+            S[a][jb][2] *= F0.gam[a].z; S[a][jb][3] *= F0.gam[a].w;
             st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, S[a][jb]);
         }
 
-    for (int c = c_beg; c < c_end; ++c) {
+    auto step = [&](int c, const Frags& cur, const Frags& nxt, Frags& later) {
         const bool more = c + 1 < c_end;
-        // ---- segment 0: V into LDS, previous output out, prefetch the next chunk
+        // ---- segment 0: V into LDS, previous output out, prefetch chunk c + 2
         {
-            const uint32_t w4[4] = {vcur.x, vcur.y, vcur.z, vcur.w};
+            const uint32_t w4[4] = {cur.v.x, cur.v.y, cur.v.z, cur.v.w};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 sm.Vt[(vcol + 2 * m) * LDV + vrow] = bf_lo(w4[m]);
                 sm.Vt[(vcol + 2 * m + 1) * LDV + vrow] = bf_hi(w4[m]);
             }
         }
-        if (c > c_beg) flush_o(c - 1);
-        if (more) load_frags(c + 1, nxt, vnxt);
+        flush_o(c - 1);
+        load_a(c + 2, later);
         __syncthreads();
         // ---- segment 1: Y = Kt G, Z = Qt G, R = diag(beta)(V - Y)
         f32x4 Y[2] = {Z4, Z4}, Zc[2] = {Z4, Z4};
@@ -552,6 +582,7 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
             Zc[0] = mma32(cur.Q[kk], b0, Zc[0]);
             Zc[1] = mma32(cur.Q[kk], b1, Zc[1]);
         }
+        load_b(c + 2, later);
         {
             const float bb[4] = {cur.bet.x, cur.bet.y, cur.bet.z, cur.bet.w};
 #pragma unroll
@@ -573,6 +604,7 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
             if (cw >= 2) u = mma32(cur.T[1], ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4), u);
             st4(sm.Ut + (16 * jb + r) * LDT + 16 * cw + 4 * q4, u);
         }
+        load_c(c + 2, later);
         __syncthreads();
         // ---- segment 3: O = Z + P U; S <- G + Kb^T U; next G
 #pragma unroll
@@ -598,12 +630,17 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
                 S[a][jb] = s;
             }
         }
+        load_d(c + 2, later);
         __syncthreads();
-        if (more) {
-            cur = nxt;
-            vcur = vnxt;
-        }
+    };
+    int c = c_beg;
+    for (; c + 3 <= c_end; c += 3) {
+        step(c, F0, F1, F2);
+        step(c + 1, F1, F2, F0);
+        step(c + 2, F2, F0, F1);
     }
+    if (c < c_end) step(c, F0, F1, F2);
+    if (c + 1 < c_end) step(c + 1, F1, F2, F0);
     flush_o(c_end - 1);
     if (s_out) {
 #pragma unroll
@@ -624,11 +661,16 @@ int prefill_split_window(int n_seqs, int H) {
     return w < 1 ? 1 : (w > (size_t)MAX_WIN ? MAX_WIN : (int)w);
 }
 
+// State carry, then the tiles of one window.
 size_t prefill_split_workspace_bytes(int n_seqs, int H) {
     return (size_t)n_seqs * H * D * D * 4 +
            (size_t)n_seqs * prefill_split_window(n_seqs, H) * H * TILE;
 }
 
+// Windows run one after the other on the caller's stream: operand kernel, then
+// state pass.  (Running the operand kernel of the next window concurrently on a
+// second stream was measured slower: both kernels then share the HBM bandwidth
+// that the tile round trip already saturates.)
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const int32_t* cu, int n_seqs, int64_t T,
                                 int H, int max_chunks, const float* s0, float* s_final, void* o,
@@ -637,21 +679,21 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, con
     if (n_pairs == 0) return hipSuccess;
     const int win = prefill_split_window(n_seqs, H);
     float* ws_state = reinterpret_cast<float*>(workspace);
-    uint8_t* ws_tiles = reinterpret_cast<uint8_t*>(workspace) + (size_t)n_pairs * D * D * 4;
+    uint8_t* tiles = reinterpret_cast<uint8_t*>(workspace) + (size_t)n_pairs * D * D * 4;
     const int n_win = max_chunks > 0 ? (max_chunks + win - 1) / win : 1;
     for (int w = 0; w < n_win; ++w) {
         const int w0 = w * win;
         const int rows = max_chunks - w0 < win ? max_chunks - w0 : win;
         if (rows > 0) {
-            hipLaunchKernelGGL(prep_kernel, dim3((unsigned)n_pairs, (unsigned)rows),
-                               dim3(256), 0, stream, (const bf16_t*)q, (const bf16_t*)k, g, beta,
-                               cu, T, H, w0, win, ws_tiles);
+            hipLaunchKernelGGL(prep_kernel, dim3((unsigned)n_pairs, (unsigned)rows), dim3(256), 0,
+                               stream, (const bf16_t*)q, (const bf16_t*)k, g, beta, cu, T, H, w0,
+                               win, tiles);
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;
         }
         hipLaunchKernelGGL(state_kernel, dim3((unsigned)(n_pairs * NS)), dim3(256), 0, stream,
-                           (const bf16_t*)v, cu, T, H, (int)n_pairs, w0, win, ws_tiles, ws_state,
-                           s0, s_final, (bf16_t*)o);
+                           (const bf16_t*)v, cu, T, H, (int)n_pairs, w0, win, tiles, ws_state, s0,
+                           s_final, (bf16_t*)o);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

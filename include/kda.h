@@ -34,7 +34,7 @@
  *   Device-side errors surface at the caller's next synchronisation, as for any
  *   HIP kernel.
  * - Thread safety: calls may come from several host threads; the only shared
- *   state is the read-only device-property cache and a thread-local error text.
+ *   state is a thread-local error text.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -132,10 +132,10 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
  * kda_prefill_workspace_bytes -- size of the workspace that lets
  * kda_prefill_chunked use its two-kernel matrix-core path for this shape; 0 when
  * the shape runs a path that needs none.  Depends only on n_seqs and H for the
- * matrix-core shapes: a fixed-size state carry (64 KiB per sequence and head)
- * plus per-chunk operand tiles for a window of at most 32 chunks per sequence,
- * the window sized to keep the tiles within about 100 MiB where the batch allows
- * (at least one chunk per sequence and head: 66 304 bytes each).
+ * matrix-core shapes: a state carry (64 KiB per sequence and head) plus the
+ * per-chunk operand tiles (66 304 bytes per chunk and head) of a window of at
+ * most 32 chunks per sequence, sized to about 192 MiB where the batch allows
+ * (at least one chunk per sequence and head).
  */
 size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
                                    kda_dtype dtype);

@@ -92,10 +92,10 @@ def test_prefill_workspace_bytes(lib):
     """State carry (64 KiB per sequence and head) plus a window of 66 304-byte
     chunk tiles; 0 for shapes that run without a workspace."""
     f = lib.kda_prefill_workspace_bytes
-    # one sequence, 64 heads: the 100 MiB tile budget allows a 24-chunk window
-    assert f(1, 64, 128, 128, 64, KDA_BF16) == 64 * 65536 + 24 * 64 * 66304
-    # small batches stop at 32 chunks per window
-    assert f(3, 2, 128, 128, 64, KDA_BF16) == 6 * 65536 + 3 * 32 * 2 * 66304
+    # one sequence, 64 heads: a full 32-chunk window fits the 192 MiB budget
+    assert f(1, 64, 128, 128, 64, KDA_BF16) == 64 * 65536 + 32 * 64 * 66304
+    # four sequences, 64 heads: 11 chunks per window
+    assert f(4, 64, 128, 128, 64, KDA_BF16) == 4 * 64 * 65536 + 4 * 11 * 64 * 66304
     # large batches keep one chunk per sequence and head
     assert f(256, 64, 128, 128, 64, KDA_BF16) == 256 * 64 * (65536 + 66304)
     assert f(1, 64, 128, 128, 64, KDA_F32) == 0
