@@ -33,15 +33,21 @@ PREFILL_KERNEL = "prefill"
 PREFILL_KERNELS = "prep_kernel + state_kernel (kda_prefill_split.hip), all windows of one call"
 DECODE_KERNEL = "decode_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+_CSRC = os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc")
 SOURCES = {
-    PREFILL_KERNEL: os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc", "kda_prefill_split.hip"),
-    DECODE_KERNEL: os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc", "kda_decode.hip"),
+    PREFILL_KERNEL: [os.path.join(_CSRC, "kda_prefill_split.hip"),
+                     os.path.join(_CSRC, "kda_chunk_ops.h")],
+    DECODE_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
 }
 
 
 def source_sha(kernel):
-    with open(SOURCES[kernel], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of sha256 over the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for path in SOURCES[kernel]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel):

@@ -181,8 +181,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                                         max_chunks, initial_state, final_state, o, workspace,
                                         stream);
     } else if (mfma)
-        err = kda::launch_prefill_mfma(q, k, v, g, beta, cu_seqlens_dev, n_seqs, T, H,
-                                       initial_state, final_state, o, stream);
+        err = kda::launch_prefill_fused(q, k, v, g, beta, cu_seqlens_dev, n_seqs, T, H,
+                                        initial_state, final_state, o, stream);
     else
         err = kda::launch_prefill_vector(q, k, v, g, beta, dtype, cu_seqlens_dev, n_seqs, T, H,
                                          d, chunk, initial_state, final_state, o, stream);

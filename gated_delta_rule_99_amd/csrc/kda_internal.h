@@ -95,11 +95,11 @@ hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, co
                                  int n_seqs, int64_t T, int H, int d, int chunk,
                                  const float* s0, float* s_final, void* o, hipStream_t stream);
 
-// bf16, d = 128, chunk = 64.
-hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, const int32_t* cu, int n_seqs, int64_t T,
-                               int H, const float* s0, float* s_final, void* o,
-                               hipStream_t stream);
+// bf16, d = 128, chunk = 64, one fused kernel (no workspace).
+hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const int32_t* cu, int n_seqs, int64_t T,
+                                int H, const float* s0, float* s_final, void* o,
+                                hipStream_t stream);
 
 // bf16, d = 128, chunk = 64, two kernels through a caller workspace of
 // prefill_split_workspace_bytes(n_seqs, H) bytes; max_chunks = the longest
