@@ -78,9 +78,10 @@ def prefill_algorithmic(T, H, d, chunk, with_s0, with_sfinal):
     return bytes_, flops
 
 
-def decode_algorithmic(B, H, d):
-    """Per (sequence, head): state read + write (2 * 4 d^2) and q, k, v, g, beta, o."""
-    return B * H * (2 * 4 * d * d + 3 * 2 * d + 4 * d + 4 + 2 * d)
+def decode_algorithmic(B, H, d, n_tok=1):
+    """Per (sequence, head): state read + write once (2 * 4 d^2) and, per token,
+    q, k, v, g, beta, o."""
+    return B * H * (2 * 4 * d * d + n_tok * (3 * 2 * d + 4 * d + 4 + 2 * d))
 
 
 def cpu_baseline_run(inp):
@@ -238,6 +239,34 @@ def main():
             result.update({"value": B / (step_ms * 1e-3), "unit": "tokens/s",
                            "ms_per_step": step_ms})
         result["decode"] = dec
+        del q, k, v, g, beta, state, o, inp
+
+        # speculative-decoding verification: 4 tokens per sequence in one call
+        n_tok = 4
+        inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", chunk=64,
+                                          g_mu=2.0, g_sigma=0.5, s0_std=0.02, seed=1006)
+        tk = lambda x: x.reshape((B, n_tok) + tuple(x.shape[1:])).to(dev).contiguous()
+        q, k, v, g, beta = (tk(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+        state = inp.S0.to(dev)
+        o = torch.empty((B, n_tok, H, d), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.warmup):
+            kda.kda_decode_tokens(q, k, v, g, beta, state, o=o)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(nsteps):
+            kda.kda_decode_tokens(q, k, v, g, beta, state, o=o)
+        e1.record()
+        torch.cuda.synchronize()
+        mtp_ms = e0.elapsed_time(e1) / nsteps
+        alg = decode_algorithmic(B, H, d, n_tok)
+        gbs = alg / (mtp_ms * 1e-3) / 1e9
+        result["decode_tokens"] = {
+            "workload": f"speculative-decoding verification: B={B} sequences x H={H} heads, "
+                        f"{n_tok} tokens each per call, fp32 128x128 states, bf16 q/k/v",
+            "ms_per_step": mtp_ms, "tokens_per_s": B * n_tok / (mtp_ms * 1e-3),
+            "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL, "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "algorithmic_bytes": alg}}
     print(json.dumps(result), flush=True)
 
 

@@ -24,7 +24,7 @@ kda_status hip_status(hipError_t err, const char* what) {
     return fail(KDA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(err), (int)err);
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }  // NULL counts as aligned
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
@@ -195,17 +195,20 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
     return kda::prefill_split_workspace_bytes(n_seqs, H);
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
-                           const int32_t* slot_idx, int B, int H, int dk, int dv, void* o,
-                           hipStream_t stream) {
-    const char* fn = "kda_decode_step";
+// Shared by kda_decode_step (n_tok = 1, no snapshots) and kda_decode_tokens.
+static kda_status decode_common(const char* fn, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, kda_dtype dtype, float* state,
+                                int64_t n_slots, const int32_t* slot_idx, int B, int n_tok,
+                                int H, int dk, int dv, void* o, float* token_states,
+                                hipStream_t stream) {
     g_detail[0] = 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
     if (kda_status s = check_heads(fn, H, dk, dv)) return s;
     if (B < 0 || n_slots < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B and n_slots must be >= 0", fn);
+    if (n_tok < 1 || n_tok > 64)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_tok = %d, expected 1..64", fn, n_tok);
     if (B == 0) return KDA_OK;
     if (!slot_idx && n_slots < B)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots (%lld) < B (%d) without slot_idx", fn,
@@ -217,19 +220,43 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
                     fn);
     const size_t es = elem_size(dtype);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
-        !aligned16(state) || ((uintptr_t)beta & 3u) || ((uintptr_t)slot_idx & 3u))
+        !aligned16(state) || ((uintptr_t)beta & 3u) || ((uintptr_t)slot_idx & 3u) ||
+        !aligned16(token_states))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
-    const size_t nv = (size_t)B * H * dk;
+    const size_t nv = (size_t)B * n_tok * H * dk, nb = (size_t)B * n_tok * H * 4;
     const size_t sbytes = (size_t)n_slots * kda_state_bytes(H, dk, dv);
+    const size_t tbytes = (size_t)B * n_tok * kda_state_bytes(H, dk, dv);
     if (overlaps(o, nv * es, q, nv * es) || overlaps(o, nv * es, k, nv * es) ||
         overlaps(o, nv * es, v, nv * es) || overlaps(o, nv * es, g, nv * 4) ||
         overlaps(o, nv * es, state, sbytes) || overlaps(state, sbytes, q, nv * es) ||
         overlaps(state, sbytes, k, nv * es) || overlaps(state, sbytes, v, nv * es) ||
-        overlaps(state, sbytes, g, nv * 4) || overlaps(state, sbytes, beta, (size_t)B * H * 4))
+        overlaps(state, sbytes, g, nv * 4) || overlaps(state, sbytes, beta, nb))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state or o overlaps another argument", fn);
+    if (token_states &&
+        (overlaps(token_states, tbytes, state, sbytes) || overlaps(token_states, tbytes, o, nv * es) ||
+         overlaps(token_states, tbytes, q, nv * es) || overlaps(token_states, tbytes, k, nv * es) ||
+         overlaps(token_states, tbytes, v, nv * es) || overlaps(token_states, tbytes, g, nv * 4) ||
+         overlaps(token_states, tbytes, beta, nb)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: token_states overlaps another argument", fn);
     return hip_status(kda::launch_decode(q, k, v, g, beta, dtype, state, n_slots, slot_idx, B,
-                                         H, dk, o, stream),
-                      "kda_decode_step launch");
+                                         n_tok, H, dk, token_states, o, stream),
+                      "decode launch");
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                           const int32_t* slot_idx, int B, int H, int dk, int dv, void* o,
+                           hipStream_t stream) {
+    return decode_common("kda_decode_step", q, k, v, g, beta, dtype, state, n_slots, slot_idx, B,
+                         1, H, dk, dv, o, nullptr, stream);
+}
+
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                             const int32_t* slot_idx, int B, int n_tok, int H, int dk, int dv,
+                             void* o, float* token_states, hipStream_t stream) {
+    return decode_common("kda_decode_tokens", q, k, v, g, beta, dtype, state, n_slots, slot_idx,
+                         B, n_tok, H, dk, dv, o, token_states, stream);
 }
 
 static kda_status check_conv_common(const char* fn, const float* w, kda_dtype dtype,

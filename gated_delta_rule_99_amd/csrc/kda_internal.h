@@ -85,10 +85,11 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int64_t T, i
 hipError_t launch_state_init(float* state, int64_t n_floats, const float* src,
                              hipStream_t stream);
 
+// n_tok consecutive tokens per sequence; token_states may be NULL.
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
-                         const int32_t* slot_idx, int B, int H, int d, void* o,
-                         hipStream_t stream);
+                         const int32_t* slot_idx, int B, int n_tok, int H, int d,
+                         float* token_states, void* o, hipStream_t stream);
 
 hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, kda_dtype dtype, const int32_t* cu,

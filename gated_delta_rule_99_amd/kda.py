@@ -42,6 +42,8 @@ _SIGNATURES = {
     "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32,
                                _i32, _vp, _vp]),
+    "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _vp, _vp, _vp]),
     "kda_short_conv_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp, _vp]),
     "kda_short_conv_decode": (_i32, [_vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _f32,
@@ -182,6 +184,25 @@ def kda_decode_step(q, k, v, g, beta, state, slot_idx=None, o=None, stream=None)
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _ptr(state),
         state.shape[0], _ptr(slot_idx), B, H, dk, dv, _ptr(o), _stream(stream)))
     return o
+
+
+def kda_decode_tokens(q, k, v, g, beta, state, slot_idx=None, o=None, token_states=None,
+                      stream=None):
+    """n_tok consecutive tokens per sequence.  q, k, g: [B, n_tok, H, dk];
+    v: [B, n_tok, H, dv]; beta: [B, n_tok, H]; state [n_slots, H, dk, dv] fp32
+    updated in place.  token_states: None, True (allocate [B, n_tok, H, dk, dv])
+    or a tensor of that shape.  Returns (o [B, n_tok, H, dv], token_states)."""
+    B, n_tok, H, dk = q.shape
+    dv = v.shape[3]
+    if o is None:
+        o = torch.empty((B, n_tok, H, dv), dtype=q.dtype, device=q.device)
+    if token_states is True:
+        token_states = torch.empty((B, n_tok, H, dk, dv), dtype=torch.float32, device=q.device)
+    _check(load().kda_decode_tokens(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _ptr(state),
+        state.shape[0], _ptr(slot_idx), B, n_tok, H, dk, dv, _ptr(o),
+        _ptr(token_states) if token_states is not None else None, _stream(stream)))
+    return o, token_states
 
 
 def kda_short_conv_prefill(x, w, cu_seqlens=None, l2_head_dim: int = 0, l2_eps: float = 1e-6,

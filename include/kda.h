@@ -159,6 +159,38 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
                            hipStream_t stream);
 
 /*
+ * kda_decode_tokens -- advance B sequences by n_tok consecutive tokens each, in
+ * place: the recurrence above applied to tokens 0, 1, ..., n_tok - 1 of every
+ * sequence in order, with each state read once and written once.  This is the
+ * verification step of speculative decoding: the serving recipe on page
+ * "Ling-3.1-flash and the 7:1 hybrid: how much KV cache does a 560B model need
+ * at 1M tokens?" (section "What does that mean for serving?") drafts three
+ * tokens per step with the model's multi-token-prediction layer, and page
+ * "Ling-3.1-flash: a 560B hybrid-attention MoE, counted from its safetensors
+ * headers" (section "The serving numbers are not one experiment") reports an
+ * average of about 2-2.6 accepted tokens per step.  The verifier advances every
+ * sequence by the drafted tokens at once.
+ *
+ *   q, k         : [B, n_tok, H, dk] dtype    v, o : [B, n_tok, H, dv] dtype
+ *   g            : [B, n_tok, H, dk] fp32     beta : [B, n_tok, H] fp32
+ *   state        : [n_slots, H, dk, dv] fp32, read and written in place; on
+ *                  return it holds the state after the last token.
+ *   slot_idx     : as in kda_decode_step.
+ *   token_states : [B, n_tok, H, dk, dv] fp32, or NULL.  When given, entry
+ *                  [b, j] receives sequence b's state after token j, so that
+ *                  a caller that accepts only the first m drafts can restore
+ *                  the state after token m - 1 (kda_state_init copies it).
+ *                  Must not overlap any other argument.
+ * n_tok in 1..64; n_tok = 1 without token_states is exactly kda_decode_step.
+ * Out-of-range slots leave every state untouched and set all n_tok outputs of
+ * that sequence to NaN.
+ */
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                             const int32_t* slot_idx, int B, int n_tok, int H, int dk, int dv,
+                             void* o, float* token_states, hipStream_t stream);
+
+/*
  * kda_short_conv_prefill -- width-4 causal depthwise convolution over packed
  * sequences, optionally followed by a per-head L2 normalisation (the front end
  * that q, k and v pass through before the recurrence):

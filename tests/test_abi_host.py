@@ -134,6 +134,28 @@ def test_decode_rejects(lib, kw, status, needle):
     assert needle in lib.kda_last_error_detail().decode()
 
 
+def decode_tokens(lib, **kw):
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, state=Fp, n_slots=4, slot=None, B=4,
+             n_tok=3, H=2, dk=128, dv=128, o=Gp, snaps=None, stream=None)
+    a.update(kw)
+    return lib.kda_decode_tokens(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
+                                 a["state"], a["n_slots"], a["slot"], a["B"], a["n_tok"], a["H"],
+                                 a["dk"], a["dv"], a["o"], a["snaps"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(n_tok=0), KDA_ERR_INVALID_ARGUMENT, "n_tok"),
+    (dict(n_tok=65), KDA_ERR_INVALID_ARGUMENT, "n_tok"),
+    (dict(snaps=0x9000008), KDA_ERR_INVALID_ARGUMENT, "misaligned"),
+    (dict(snaps=Fp + 4096), KDA_ERR_INVALID_ARGUMENT, "token_states overlaps"),
+    (dict(dk=96, dv=96), KDA_ERR_UNSUPPORTED, "head dim"),
+    (dict(n_slots=3), KDA_ERR_INVALID_ARGUMENT, "n_slots"),
+])
+def test_decode_tokens_rejects(lib, kw, status, needle):
+    assert decode_tokens(lib, **kw) == status
+    assert needle in lib.kda_last_error_detail().decode()
+
+
 def test_state_init_rejects(lib):
     assert lib.kda_state_init(None, 2, 2, 64, 64, None, None) == KDA_ERR_INVALID_ARGUMENT
     assert lib.kda_state_init(A, 2, 2, 64, 32, None, None) == KDA_ERR_UNSUPPORTED

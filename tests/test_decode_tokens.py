@@ -1,0 +1,117 @@
+"""GPU parity of multi-token decode (kda_decode_tokens: n_tok consecutive tokens
+per sequence, one state read and one write) against the CPU oracle, through the
+C ABI.  The oracle runs the same tokens as packed sequences of n_tok tokens, so
+its packed layout [B * n_tok, H, d] is the decode layout [B, n_tok, H, d]."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, np64, oracle_on, per_seq_errors,
+                          rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+
+def kda():
+    gpu_or_skip()
+    import gated_delta_rule_99_amd as m
+    m.load()
+    return m
+
+
+def as_tokens(x, B, n_tok):
+    """[B * n_tok, ...] packed sequence-major -> [B, n_tok, ...]."""
+    return x.reshape((B, n_tok) + tuple(x.shape[1:]))
+
+
+def run_tokens(m, inp, B, n_tok, state, slot_idx=None, token_states=None):
+    t = lambda x: dev(as_tokens(x, B, n_tok))
+    return m.kda_decode_tokens(t(inp.q), t(inp.k), t(inp.v), t(inp.g), t(inp.beta), state,
+                               slot_idx=slot_idx, token_states=token_states)
+
+
+@pytest.mark.parametrize("n_tok", [1, 4])
+@pytest.mark.parametrize("d,dtype", [(32, "f32"), (64, "bf16"), (128, "bf16")])
+def test_decode_tokens_matches_oracle(d, dtype, n_tok):
+    """B sequences advanced by n_tok tokens through a slot permutation into a
+    larger pool: outputs of every token and the final states match the oracle;
+    every other slot is untouched, bit for bit."""
+    m = kda()
+    B, H, n_slots = 5, 3, 9
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype=dtype, s0_std=0.3,
+                                      seed=60 + d + n_tok)
+    pool = torch.randn((n_slots, H, d, d), generator=torch.Generator().manual_seed(d)) * 0.3
+    slots = torch.tensor([7, 0, 4, 2, 8], dtype=torch.int32)
+    pool[slots.long()] = inp.S0
+    state = dev(pool)
+    o, _ = run_tokens(m, inp, B, n_tok, state, slot_idx=dev(slots))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_on(inp)
+    st = state.cpu()
+    eo, es = per_seq_errors(np64(o).reshape(B * n_tok, H, d), o_ref, np64(st[slots.long()]),
+                            S_ref, inp.cu_seqlens)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    print(f"decode_tokens d={d} {dtype} n_tok={n_tok}: o {eo:.2e} S {es:.2e}")
+    assert eo <= tol and es <= tol
+    untouched = [s for s in range(n_slots) if s not in slots.tolist()]
+    assert torch.equal(st[untouched], pool[untouched])
+
+
+def test_decode_tokens_snapshots_match_prefixes():
+    """token_states[b, j] is sequence b's state after token j: it matches the
+    oracle run on the first j + 1 tokens, and the last one is the final state."""
+    m = kda()
+    B, n_tok, H, d = 3, 4, 2, 128
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", s0_std=0.3, seed=71)
+    state = dev(inp.S0)
+    o, snaps = run_tokens(m, inp, B, n_tok, state, token_states=True)
+    torch.cuda.synchronize()
+    snaps = snaps.cpu()
+    for j in range(n_tok):
+        rows = torch.tensor([b * n_tok + i for b in range(B) for i in range(j + 1)])
+        pre = workloads.RecurrenceInputs(inp.q[rows], inp.k[rows], inp.v[rows], inp.g[rows],
+                                         inp.beta[rows],
+                                         torch.arange(0, B * (j + 1) + 1, j + 1,
+                                                      dtype=torch.int32),
+                                         inp.S0, "bf16", inp.chunk)
+        _, S_ref = oracle_on(pre)
+        err = max(rel_fro(np64(snaps[b, j]), S_ref[b]) for b in range(B))
+        print(f"snapshot after token {j}: {err:.2e}")
+        assert err <= TOL_BF16
+    assert torch.equal(snaps[:, -1], state.cpu())
+
+
+def test_decode_tokens_equals_single_steps():
+    """One call over n_tok tokens equals n_tok single-token decode steps, bit for
+    bit: the state is kept in fp32 registers between tokens, exactly the values
+    a round trip through memory would hold."""
+    m = kda()
+    B, n_tok, H, d = 4, 3, 2, 128
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", s0_std=0.3, seed=72)
+    s_multi = dev(inp.S0)
+    o_multi, _ = run_tokens(m, inp, B, n_tok, s_multi)
+    s_single = dev(inp.S0)
+    outs = []
+    for j in range(n_tok):
+        rows = torch.arange(B) * n_tok + j
+        outs.append(m.kda_decode_step(dev(inp.q[rows]), dev(inp.k[rows]), dev(inp.v[rows]),
+                                      dev(inp.g[rows]), dev(inp.beta[rows]), s_single))
+    torch.cuda.synchronize()
+    assert torch.equal(o_multi, torch.stack(outs, dim=1))
+    assert torch.equal(s_multi, s_single)
+
+
+def test_decode_tokens_out_of_range_slot():
+    """A slot outside the pool: all n_tok outputs of that sequence are NaN and no
+    state changes."""
+    m = kda()
+    B, n_tok, H, d = 2, 3, 2, 64
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", seed=73)
+    state = torch.randn((2, H, d, d), device="cuda")
+    before = state.clone()
+    slots = torch.tensor([1, 5], dtype=torch.int32, device="cuda")
+    o, _ = run_tokens(m, inp, B, n_tok, state, slot_idx=slots)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1].float()).all() and not torch.isnan(o[0].float()).any()
+    assert torch.equal(state[0], before[0])
