@@ -116,3 +116,45 @@ def test_determinism():
     o1, S1 = gpu_prefill(inp)
     o2, S2 = gpu_prefill(inp)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_graph_capture_replays():
+    """The whole hot path (state init, two-kernel prefill, a decode step, a
+    two-token decode) captured in one HIP graph and replayed several times, with
+    eager work in between: every replay equals the eager run, bit for bit."""
+    m = kda()
+    inp = workloads.recurrence_inputs([200, 77], H=4, d=128, dtype="bf16", s0_std=0.3, seed=31)
+    dec = workloads.recurrence_inputs([1, 1], H=4, d=128, dtype="bf16", seed=32)
+    two = workloads.recurrence_inputs([2, 2], H=4, d=128, dtype="bf16", seed=33)
+    q, k, v, g, beta = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    dq, dk, dv, dg, db = (dev(x) for x in (dec.q, dec.k, dec.v, dec.g, dec.beta))
+    t2 = lambda x: dev(x.reshape((2, 2) + tuple(x.shape[1:])))
+    tq, tk, tv, tg, tb = (t2(x) for x in (two.q, two.k, two.v, two.g, two.beta))
+    cu, s0 = dev(inp.cu_seqlens), dev(inp.S0)
+    state = torch.empty_like(s0)
+    o, od, ot = torch.empty_like(q), torch.empty_like(dq), torch.empty_like(tv)
+    ws = torch.empty(m.kda_prefill_workspace_bytes(2, 4, 128, 128, 64, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def run():
+        m.kda_state_init(state, s0)
+        m.kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=cu, cu_seqlens_host=inp.cu_seqlens,
+                              initial_state=state, final_state=state, o=o, workspace=ws)
+        m.kda_decode_step(dq, dk, dv, dg, db, state, o=od)
+        m.kda_decode_tokens(tq, tk, tv, tg, tb, state, o=ot)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (o, od, ot, state)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for _ in range(4):
+        for x in (o, od, ot, state):
+            x.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip((o, od, ot, state), ref):
+            assert torch.equal(x, y)

@@ -104,6 +104,22 @@ def test_mfma_prefill_multiwindow(path):
 
 
 @pytest.mark.parametrize("path", list(PATHS))
+def test_mfma_prefill_many_short_sequences(path):
+    """600 packed sequences of 0..600 tokens, H=2: the two-kernel path's window
+    shrinks to 2 chunks (the tile budget is shared by every sequence and head),
+    so most sequences span several windows; every sequence checked."""
+    kda()
+    lens = np.random.default_rng(5).integers(0, 601, size=600).tolist()
+    inp = workloads.recurrence_inputs(lens, H=2, d=128, dtype="bf16", chunk=64, g_mu=3.0,
+                                      g_sigma=1.0, s0_std=0.3, seed=125)
+    o, S = gpu_prefill(inp, workspace=PATHS[path])
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
+    print(f"mfma {path} 600 sequences: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("path", list(PATHS))
 def test_prefill_empty_sequences_keep_state(path):
     """Zero-length sequences: final state equals the initial state, bit for bit."""
     kda()
