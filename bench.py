@@ -32,12 +32,14 @@ METRIC = "KDA layer tokens/s (H=64,d=128 prefill); decode state GB/s vs HBM peak
 PREFILL_KERNEL = "prefill"
 PREFILL_KERNELS = "prep_kernel + state_kernel (kda_prefill_split.hip), all windows of one call"
 DECODE_KERNEL = "decode_kernel"
+DECODE_TOKENS_KERNEL = "decode_kernel_4tok"  # traffic record of the 4-token decode
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc")
 SOURCES = {
     PREFILL_KERNEL: [os.path.join(_CSRC, "kda_prefill_split.hip"),
                      os.path.join(_CSRC, "kda_chunk_ops.h")],
     DECODE_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
+    DECODE_TOKENS_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
 }
 
 
@@ -114,8 +116,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
-                    help="run just one kernel (for profiler runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_tokens", "copy"],
+                    default=None, help="run just one kernel (for profiler runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -209,17 +211,18 @@ def main():
         del inp
         torch.cuda.empty_cache()
 
+    B, H, d = 256, 64, 128  # the batched decode workload's shape
+    nsteps = args.decode_steps if args.only is None else args.steps
+    e0, e1 = ev(), ev()
     if args.only == "decode" or (args.only is None and not args.no_decode):
         inp = workloads.decode_batch()
-        B, H, d = inp.n_seqs, inp.H, inp.d
+        assert (inp.n_seqs, inp.H, inp.d) == (B, H, d)
         q, k, v, g, beta = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
         state = inp.S0.to(dev)
         o = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
-        nsteps = args.decode_steps if args.only is None else args.steps
         for _ in range(args.warmup):
             kda.kda_decode_step(q, k, v, g, beta, state, o=o)
         torch.cuda.synchronize()
-        e0, e1 = ev(), ev()
         e0.record()
         for _ in range(nsteps):
             kda.kda_decode_step(q, k, v, g, beta, state, o=o)
@@ -241,6 +244,7 @@ def main():
         result["decode"] = dec
         del q, k, v, g, beta, state, o, inp
 
+    if args.only == "decode_tokens" or (args.only is None and not args.no_decode):
         # speculative-decoding verification: 4 tokens per sequence in one call
         n_tok = 4
         inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", chunk=64,
@@ -264,9 +268,14 @@ def main():
             "workload": f"speculative-decoding verification: B={B} sequences x H={H} heads, "
                         f"{n_tok} tokens each per call, fp32 128x128 states, bf16 q/k/v",
             "ms_per_step": mtp_ms, "tokens_per_s": B * n_tok / (mtp_ms * 1e-3),
-            "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL, "achieved": gbs,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (4 tokens per sequence)",
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(DECODE_TOKENS_KERNEL),
                          "algorithmic_bytes": alg}}
+        if args.only == "decode_tokens":
+            result.update({"value": B * n_tok / (mtp_ms * 1e-3), "unit": "tokens/s",
+                           "ms_per_step": mtp_ms})
     print(json.dumps(result), flush=True)
 
 

@@ -106,7 +106,7 @@ kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
 }
 
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, kda_dtype dtype,
+                               const float* beta, kda_dtype dtype, kda_gate gate,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
                                const float* initial_state, float* final_state, void* o,
@@ -115,6 +115,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     g_detail[0] = 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate layout %d", fn, (int)gate);
     if (kda_status s = check_heads(fn, H, dk, dv)) return s;
     if (chunk != 16 && chunk != 32 && chunk != 64)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: chunk %d not in {16, 32, 64}", fn, chunk);
@@ -129,6 +131,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                     (long long)blocks);
     const size_t es = elem_size(dtype);
     const size_t n_qk = (size_t)T * H * d, n_bt = (size_t)T * H;
+    const size_t n_g = gate == KDA_GATE_HEAD ? n_bt : n_qk;  // g elements
     const size_t sbytes = (size_t)n_seqs * kda_state_bytes(H, dk, dv);
     if (T > 0) {
         if (!q || !k || !v || !g || !beta || !o)
@@ -137,7 +140,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
             ((uintptr_t)beta & 3u))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
         if (overlaps(o, n_qk * es, q, n_qk * es) || overlaps(o, n_qk * es, k, n_qk * es) ||
-            overlaps(o, n_qk * es, v, n_qk * es) || overlaps(o, n_qk * es, g, n_qk * 4) ||
+            overlaps(o, n_qk * es, v, n_qk * es) || overlaps(o, n_qk * es, g, n_g * 4) ||
             overlaps(o, n_qk * es, beta, n_bt * 4) ||
             overlaps(o, n_qk * es, final_state, sbytes) ||
             overlaps(o, n_qk * es, initial_state, sbytes))
@@ -151,7 +154,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                     "%s: initial_state and final_state overlap without being equal", fn);
     if (final_state && T > 0 &&
         (overlaps(final_state, sbytes, q, n_qk * es) || overlaps(final_state, sbytes, k, n_qk * es) ||
-         overlaps(final_state, sbytes, v, n_qk * es) || overlaps(final_state, sbytes, g, n_qk * 4)))
+         overlaps(final_state, sbytes, v, n_qk * es) || overlaps(final_state, sbytes, g, n_g * 4)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state overlaps an input", fn);
 
     const bool mfma = mfma_shape(dtype, dk, dv, chunk);
@@ -163,7 +166,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
         if (!aligned16(workspace))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned workspace", fn);
         if (overlaps(workspace, ws_need, q, n_qk * es) || overlaps(workspace, ws_need, k, n_qk * es) ||
-            overlaps(workspace, ws_need, v, n_qk * es) || overlaps(workspace, ws_need, g, n_qk * 4) ||
+            overlaps(workspace, ws_need, v, n_qk * es) || overlaps(workspace, ws_need, g, n_g * 4) ||
             overlaps(workspace, ws_need, beta, n_bt * 4) || overlaps(workspace, ws_need, o, n_qk * es) ||
             overlaps(workspace, ws_need, initial_state, sbytes) ||
             overlaps(workspace, ws_need, final_state, sbytes))
@@ -177,14 +180,15 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
             const int nc = (int)(((int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n] + 63) / 64);
             max_chunks = nc > max_chunks ? nc : max_chunks;
         }
-        err = kda::launch_prefill_split(q, k, v, g, beta, cu_seqlens_dev, n_seqs, T, H,
-                                        max_chunks, initial_state, final_state, o, workspace,
-                                        stream);
+        err = kda::launch_prefill_split(q, k, v, g, beta, gate == KDA_GATE_HEAD, cu_seqlens_dev,
+                                        n_seqs, T, H, max_chunks, initial_state, final_state, o,
+                                        workspace, stream);
     } else if (mfma)
-        err = kda::launch_prefill_fused(q, k, v, g, beta, cu_seqlens_dev, n_seqs, T, H,
-                                        initial_state, final_state, o, stream);
+        err = kda::launch_prefill_fused(q, k, v, g, beta, gate == KDA_GATE_HEAD, cu_seqlens_dev,
+                                        n_seqs, T, H, initial_state, final_state, o, stream);
     else
-        err = kda::launch_prefill_vector(q, k, v, g, beta, dtype, cu_seqlens_dev, n_seqs, T, H,
+        err = kda::launch_prefill_vector(q, k, v, g, beta, dtype, gate == KDA_GATE_HEAD,
+                                         cu_seqlens_dev, n_seqs, T, H,
                                          d, chunk, initial_state, final_state, o, stream);
     return hip_status(err, "kda_prefill_chunked launch");
 }
@@ -197,13 +201,16 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
 
 // Shared by kda_decode_step (n_tok = 1, no snapshots) and kda_decode_tokens.
 static kda_status decode_common(const char* fn, const void* q, const void* k, const void* v,
-                                const float* g, const float* beta, kda_dtype dtype, float* state,
+                                const float* g, const float* beta, kda_dtype dtype, kda_gate gate,
+                                float* state,
                                 int64_t n_slots, const int32_t* slot_idx, int B, int n_tok,
                                 int H, int dk, int dv, void* o, float* token_states,
                                 hipStream_t stream) {
     g_detail[0] = 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate layout %d", fn, (int)gate);
     if (kda_status s = check_heads(fn, H, dk, dv)) return s;
     if (B < 0 || n_slots < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B and n_slots must be >= 0", fn);
@@ -224,39 +231,41 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
         !aligned16(token_states))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
     const size_t nv = (size_t)B * n_tok * H * dk, nb = (size_t)B * n_tok * H * 4;
+    const size_t ng = gate == KDA_GATE_HEAD ? (size_t)B * n_tok * H : nv;  // g elements
     const size_t sbytes = (size_t)n_slots * kda_state_bytes(H, dk, dv);
     const size_t tbytes = (size_t)B * n_tok * kda_state_bytes(H, dk, dv);
     if (overlaps(o, nv * es, q, nv * es) || overlaps(o, nv * es, k, nv * es) ||
-        overlaps(o, nv * es, v, nv * es) || overlaps(o, nv * es, g, nv * 4) ||
+        overlaps(o, nv * es, v, nv * es) || overlaps(o, nv * es, g, ng * 4) ||
         overlaps(o, nv * es, state, sbytes) || overlaps(state, sbytes, q, nv * es) ||
         overlaps(state, sbytes, k, nv * es) || overlaps(state, sbytes, v, nv * es) ||
-        overlaps(state, sbytes, g, nv * 4) || overlaps(state, sbytes, beta, nb))
+        overlaps(state, sbytes, g, ng * 4) || overlaps(state, sbytes, beta, nb))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state or o overlaps another argument", fn);
     if (token_states &&
         (overlaps(token_states, tbytes, state, sbytes) || overlaps(token_states, tbytes, o, nv * es) ||
          overlaps(token_states, tbytes, q, nv * es) || overlaps(token_states, tbytes, k, nv * es) ||
-         overlaps(token_states, tbytes, v, nv * es) || overlaps(token_states, tbytes, g, nv * 4) ||
+         overlaps(token_states, tbytes, v, nv * es) || overlaps(token_states, tbytes, g, ng * 4) ||
          overlaps(token_states, tbytes, beta, nb)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: token_states overlaps another argument", fn);
-    return hip_status(kda::launch_decode(q, k, v, g, beta, dtype, state, n_slots, slot_idx, B,
-                                         n_tok, H, dk, token_states, o, stream),
+    return hip_status(kda::launch_decode(q, k, v, g, beta, dtype, gate == KDA_GATE_HEAD, state,
+                                         n_slots, slot_idx, B, n_tok, H, dk, token_states, o,
+                                         stream),
                       "decode launch");
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
-                           const int32_t* slot_idx, int B, int H, int dk, int dv, void* o,
-                           hipStream_t stream) {
-    return decode_common("kda_decode_step", q, k, v, g, beta, dtype, state, n_slots, slot_idx, B,
-                         1, H, dk, dv, o, nullptr, stream);
+                           const float* beta, kda_dtype dtype, kda_gate gate, float* state,
+                           int64_t n_slots, const int32_t* slot_idx, int B, int H, int dk, int dv,
+                           void* o, hipStream_t stream) {
+    return decode_common("kda_decode_step", q, k, v, g, beta, dtype, gate, state, n_slots,
+                         slot_idx, B, 1, H, dk, dv, o, nullptr, stream);
 }
 
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
-                             const int32_t* slot_idx, int B, int n_tok, int H, int dk, int dv,
-                             void* o, float* token_states, hipStream_t stream) {
-    return decode_common("kda_decode_tokens", q, k, v, g, beta, dtype, state, n_slots, slot_idx,
-                         B, n_tok, H, dk, dv, o, token_states, stream);
+                             const float* beta, kda_dtype dtype, kda_gate gate, float* state,
+                             int64_t n_slots, const int32_t* slot_idx, int B, int n_tok, int H,
+                             int dk, int dv, void* o, float* token_states, hipStream_t stream) {
+    return decode_common("kda_decode_tokens", q, k, v, g, beta, dtype, gate, state, n_slots,
+                         slot_idx, B, n_tok, H, dk, dv, o, token_states, stream);
 }
 
 static kda_status check_conv_common(const char* fn, const float* w, kda_dtype dtype,

@@ -105,7 +105,9 @@ struct ChunkIn {
 };
 
 // Issue the loads of chunk rows [c0, c0 + L) of head h; rows past L (and every
-// row when L = 0) read as zero, i.e. alpha = 1 and k = q = 0.
+// row when L = 0) read as zero, i.e. alpha = 1 and k = q = 0.  With GH (per-head
+// decay), g holds one value per (token, head), broadcast here to the channels.
+template <bool GH>
 __device__ __forceinline__ void load_chunk(ChunkIn& in, const bf16_t* q, const bf16_t* k,
                                            const float* g, const float* beta, int64_t c0, int L,
                                            int H, int h, int p, int lane) {
@@ -114,15 +116,21 @@ __device__ __forceinline__ void load_chunk(ChunkIn& in, const bf16_t* q, const b
     const int64_t cc0 = L > 0 ? c0 : 0;  // keep the base address inside the tensors
     const size_t base = (size_t)cc0 * row + (size_t)h * D;
     const int rowb2 = (int)(row * 2), rowb4 = (int)(row * 4);
-    const auto rg = window(g + base, L * rowb4);
+    const auto rg = GH ? window(g + (size_t)cc0 * H + h, L * H * 4) : window(g + base, L * rowb4);
     const auto rk = window(k + base, L * rowb2);
     const auto rq = window(q + base, L * rowb2);
     const int vkq = 8 * tg * rowb2 + ch0 * 2, vg = 8 * tg * rowb4 + ch0 * 4;
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rg, vg, rr * rowb4, 0);
-        in.g[rr] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]),
-                               __uint_as_float(x[2]), __uint_as_float(x[3]));
+        if constexpr (GH) {
+            const float x = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rg, 8 * tg * H * 4, rr * H * 4, 0));
+            in.g[rr] = make_float4(x, x, x, x);
+        } else {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rg, vg, rr * rowb4, 0);
+            in.g[rr] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]),
+                                   __uint_as_float(x[2]), __uint_as_float(x[3]));
+        }
         const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(rk, vkq, rr * rowb2, 0);
         const u32x2 z = __builtin_amdgcn_raw_buffer_load_b64(rq, vkq, rr * rowb2, 0);
         in.k[rr] = make_uint2(y[0], y[1]);

@@ -78,8 +78,9 @@ template <int D, typename Tin>
 __global__ void __launch_bounds__(DecodeShape<D>::NT)
 decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
-              float* __restrict__ state, int64_t n_slots, const int32_t* __restrict__ slot_idx,
-              int H, int n_tok, float* __restrict__ token_states, Tin* __restrict__ o) {
+              int g_head, float* __restrict__ state, int64_t n_slots,
+              const int32_t* __restrict__ slot_idx, int H, int n_tok,
+              float* __restrict__ token_states, Tin* __restrict__ o) {
     using S = DecodeShape<D>;
     constexpr int NT = S::NT, CG = S::CG, RG = S::RG, RPT = S::RPT;
     constexpr int NWAVE = (NT + 63) / 64;
@@ -123,7 +124,7 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
         // 2. gate vectors (small, cooperative)
         float qk_part = 0.f;
         for (int i = tid; i < D; i += NT) {
-            const float a = __expf(g[vec + i]);
+            const float a = __expf(g_head ? g[row] : g[vec + i]);
             const float kv = In<Tin>::load1(k + vec + i);
             const float qv = In<Tin>::load1(q + vec + i);
             s_a[i] = a;
@@ -203,28 +204,29 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
 
 template <int D, typename Tin>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, float* state, int64_t n_slots,
+                                  const float* beta, bool g_head, float* state, int64_t n_slots,
                                   const int32_t* slot_idx, int B, int n_tok, int H,
                                   float* token_states, void* o, hipStream_t stream) {
     const int64_t blocks = (int64_t)B * H;
     if (blocks == 0 || n_tok == 0) return hipSuccess;
     hipLaunchKernelGGL((decode_kernel<D, Tin>), dim3((unsigned)blocks),
                        dim3(DecodeShape<D>::NT), 0, stream, (const Tin*)q, (const Tin*)k,
-                       (const Tin*)v, g, beta, state, n_slots, slot_idx, H, n_tok, token_states,
-                       (Tin*)o);
+                       (const Tin*)v, g, beta, (int)g_head, state, n_slots, slot_idx, H, n_tok,
+                       token_states, (Tin*)o);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                         const float* beta, kda_dtype dtype, bool g_head, float* state,
+                         int64_t n_slots,
                          const int32_t* slot_idx, int B, int n_tok, int H, int d,
                          float* token_states, void* o, hipStream_t stream) {
 #define KDA_DEC(D)                                                                          \
     if (d == D) {                                                                           \
         if (dtype == KDA_BF16)                                                              \
-            return launch_decode_t<D, bf16_t>(q, k, v, g, beta, state, n_slots, slot_idx, B, \
-                                              n_tok, H, token_states, o, stream);           \
-        return launch_decode_t<D, float>(q, k, v, g, beta, state, n_slots, slot_idx, B,      \
+            return launch_decode_t<D, bf16_t>(q, k, v, g, beta, g_head, state, n_slots, slot_idx, \
+                                              B, n_tok, H, token_states, o, stream);        \
+        return launch_decode_t<D, float>(q, k, v, g, beta, g_head, state, n_slots, slot_idx, B, \
                                          n_tok, H, token_states, o, stream);                 \
     }
     KDA_DEC(16)

@@ -86,19 +86,22 @@ hipError_t launch_state_init(float* state, int64_t n_floats, const float* src,
                              hipStream_t stream);
 
 // n_tok consecutive tokens per sequence; token_states may be NULL.
+// g_head: g holds one value per (token, head) instead of one per key channel.
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                         const float* beta, kda_dtype dtype, bool g_head, float* state,
+                         int64_t n_slots,
                          const int32_t* slot_idx, int B, int n_tok, int H, int d,
                          float* token_states, void* o, hipStream_t stream);
 
 hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
-                                 const float* beta, kda_dtype dtype, const int32_t* cu,
+                                 const float* beta, kda_dtype dtype, bool g_head, const int32_t* cu,
                                  int n_seqs, int64_t T, int H, int d, int chunk,
                                  const float* s0, float* s_final, void* o, hipStream_t stream);
 
 // bf16, d = 128, chunk = 64, one fused kernel (no workspace).
 hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, const int32_t* cu, int n_seqs, int64_t T,
+                                const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+                                int64_t T,
                                 int H, const float* s0, float* s_final, void* o,
                                 hipStream_t stream);
 
@@ -108,7 +111,8 @@ hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, con
 int prefill_split_window(int n_seqs, int H);
 size_t prefill_split_workspace_bytes(int n_seqs, int H);
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, const int32_t* cu, int n_seqs, int64_t T,
+                                const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+                                int64_t T,
                                 int H, int max_chunks, const float* s0, float* s_final, void* o,
                                 void* workspace, hipStream_t stream);
 

@@ -46,6 +46,8 @@ using namespace sp;
 // ---------------------------------------------------------------- prep
 // grid (n_seqs * H, chunks in the window): one workgroup of 4 waves per
 // (sequence, head, window chunk) runs the operand stages and exports the tile.
+// GH: g holds one log decay per (token, head) instead of one per key channel.
+template <bool GH>
 __global__ void __launch_bounds__(256, 2)
 prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             const float* __restrict__ g, const float* __restrict__ beta,
@@ -66,7 +68,7 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
     zero_tp(sm, tid, 256);
     ChunkIn in;
-    load_chunk(in, q, k, g, beta, c0, L, H, h, p, lane);
+    load_chunk<GH>(in, q, k, g, beta, c0, L, H, h, p, lane);
     if (p == 0)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(in.beta), rt, OFF_BETA + 4 * lane, 0,
                                               0);
@@ -408,7 +410,8 @@ size_t prefill_split_workspace_bytes(int n_seqs, int H) {
 // second stream was measured slower: both kernels then share the HBM bandwidth
 // that the tile round trip already saturates.)
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, const int32_t* cu, int n_seqs, int64_t T,
+                                const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+                                int64_t T,
                                 int H, int max_chunks, const float* s0, float* s_final, void* o,
                                 void* workspace, hipStream_t stream) {
     const int64_t n_pairs = (int64_t)n_seqs * H;
@@ -421,9 +424,10 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, con
         const int w0 = w * win;
         const int rows = max_chunks - w0 < win ? max_chunks - w0 : win;
         if (rows > 0) {
-            hipLaunchKernelGGL(prep_kernel, dim3((unsigned)n_pairs, (unsigned)rows), dim3(256), 0,
-                               stream, (const bf16_t*)q, (const bf16_t*)k, g, beta, cu, T, H, w0,
-                               win, tiles);
+            hipLaunchKernelGGL(g_head ? prep_kernel<true> : prep_kernel<false>,
+                               dim3((unsigned)n_pairs, (unsigned)rows), dim3(256), 0, stream,
+                               (const bf16_t*)q, (const bf16_t*)k, g, beta, cu, T, H, w0, win,
+                               tiles);
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;
         }

@@ -37,7 +37,7 @@ template <int D, int C, typename Tin>
 __global__ void __launch_bounds__(256)
 prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                       const Tin* __restrict__ v, const float* __restrict__ g,
-                      const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                      const float* __restrict__ beta, int g_head, const int32_t* __restrict__ cu,
                       int64_t T, int H, const float* __restrict__ s0,
                       float* __restrict__ s_final, Tin* __restrict__ o) {
     using SH = VecShape<D, C>;
@@ -77,7 +77,7 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
             if (t < L) {
                 const size_t off = (size_t)(c0 + t) * rowk + (size_t)h * D + i;
                 kv = In<Tin>::load1(k + off);
-                gv = g[off];
+                gv = g_head ? g[(size_t)(c0 + t) * H + h] : g[off];
                 qv = In<Tin>::load1(q + off);
             }
             sKt[t * LD + i] = kv;
@@ -171,7 +171,8 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
 
 template <int D, int C, typename Tin>
 static hipError_t launch_vec_t(const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, const int32_t* cu, int n_seqs, int64_t T,
+                               const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+                               int64_t T,
                                int H, const float* s0, float* s_final, void* o,
                                hipStream_t stream) {
     using SH = VecShape<D, C>;
@@ -183,35 +184,35 @@ static hipError_t launch_vec_t(const void* q, const void* k, const void* v, cons
                                          (int)SH::BYTES);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(SH::NT), SH::BYTES, stream,
-                       (const Tin*)q, (const Tin*)k, (const Tin*)v, g, beta, cu, T, H, s0,
-                       s_final, (Tin*)o);
+                       (const Tin*)q, (const Tin*)k, (const Tin*)v, g, beta, (int)g_head, cu, T, H,
+                       s0, s_final, (Tin*)o);
     return hipGetLastError();
 }
 
 template <int D, typename Tin>
 static hipError_t launch_vec_c(int chunk, const void* q, const void* k, const void* v,
-                               const float* g, const float* beta, const int32_t* cu,
+                               const float* g, const float* beta, bool g_head, const int32_t* cu,
                                int n_seqs, int64_t T, int H, const float* s0, float* s_final,
                                void* o, hipStream_t stream) {
     switch (chunk) {
-        case 16: return launch_vec_t<D, 16, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, stream);
-        case 32: return launch_vec_t<D, 32, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, stream);
-        case 64: return launch_vec_t<D, 64, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, stream);
+        case 16: return launch_vec_t<D, 16, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, stream);
+        case 32: return launch_vec_t<D, 32, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, stream);
+        case 64: return launch_vec_t<D, 64, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
-                                 const float* beta, kda_dtype dtype, const int32_t* cu,
+                                 const float* beta, kda_dtype dtype, bool g_head, const int32_t* cu,
                                  int n_seqs, int64_t T, int H, int d, int chunk,
                                  const float* s0, float* s_final, void* o, hipStream_t stream) {
 #define KDA_VEC(D)                                                                            \
     if (d == D) {                                                                             \
         if (dtype == KDA_BF16)                                                                \
-            return launch_vec_c<D, bf16_t>(chunk, q, k, v, g, beta, cu, n_seqs, T, H, s0,     \
-                                           s_final, o, stream);                               \
-        return launch_vec_c<D, float>(chunk, q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, \
-                                      o, stream);                                             \
+            return launch_vec_c<D, bf16_t>(chunk, q, k, v, g, beta, g_head, cu, n_seqs, T, H, \
+                                           s0, s_final, o, stream);                           \
+        return launch_vec_c<D, float>(chunk, q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0,  \
+                                      s_final, o, stream);                                    \
     }
     KDA_VEC(16)
     KDA_VEC(32)

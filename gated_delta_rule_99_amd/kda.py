@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
 
 
 class KdaError(RuntimeError):
@@ -37,13 +38,13 @@ _SIGNATURES = {
     "kda_last_error_detail": (ctypes.c_char_p, []),
     "kda_state_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
     "kda_state_init": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp]),
-    "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
-                                   _i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
+                                   _i32, _i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32,
-                               _i32, _vp, _vp]),
-    "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32,
-                                 _i32, _i32, _vp, _vp, _vp]),
+    "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i64, _vp, _i32, _i32,
+                               _i32, _i32, _vp, _vp]),
+    "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i64, _vp, _i32, _i32,
+                                 _i32, _i32, _i32, _vp, _vp, _vp]),
     "kda_short_conv_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp, _vp]),
     "kda_short_conv_decode": (_i32, [_vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _f32,
@@ -83,6 +84,15 @@ def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return KDA_BF16
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _gate_code(g, q) -> int:
+    """Per-channel log decay has q's shape; per-head decay drops the channel axis."""
+    if g.dim() == q.dim():
+        return KDA_GATE_CHANNEL
+    if g.dim() == q.dim() - 1:
+        return KDA_GATE_HEAD
+    raise ValueError(f"g must have shape {tuple(q.shape)} or {tuple(q.shape[:-1])}")
 
 
 def _ptr(t):
@@ -147,8 +157,9 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
                         initial_state=None, final_state=None, o=None,
                         output_final_state: bool = True, cu_seqlens_host=None,
                         workspace="auto", stream=None):
-    """Chunked prefill over packed sequences.  q, k, g: [T, H, dk]; v: [T, H, dv];
-    beta: [T, H].  Returns (o, final_state or None).
+    """Chunked prefill over packed sequences.  q, k: [T, H, dk]; v: [T, H, dv];
+    g: [T, H, dk] (per-channel decay) or [T, H] (per-head decay); beta: [T, H].
+    Returns (o, final_state or None).
 
     workspace: "auto" (a cached device buffer of kda_prefill_workspace_bytes),
     a uint8 device tensor, or None (no workspace: the fused kernel)."""
@@ -167,30 +178,32 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
         workspace = _workspace(need, q.device) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kda_prefill_chunked(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _ptr(cu_dev),
-        cu_host.data_ptr(), n_seqs, H, dk, dv, int(chunk), _ptr(initial_state),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
+        _ptr(cu_dev), cu_host.data_ptr(), n_seqs, H, dk, dv, int(chunk), _ptr(initial_state),
         _ptr(final_state), _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
     return o, final_state
 
 
 def kda_decode_step(q, k, v, g, beta, state, slot_idx=None, o=None, stream=None):
-    """One token per sequence.  q, k, g: [B, H, dk]; v: [B, H, dv]; beta: [B, H];
+    """One token per sequence.  q, k: [B, H, dk]; g: [B, H, dk] or [B, H];
+    v: [B, H, dv]; beta: [B, H];
     state [n_slots, H, dk, dv] fp32 updated in place.  Returns o [B, H, dv]."""
     B, H, dk = q.shape
     dv = v.shape[2]
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     _check(load().kda_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _ptr(state),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
+        _ptr(state),
         state.shape[0], _ptr(slot_idx), B, H, dk, dv, _ptr(o), _stream(stream)))
     return o
 
 
 def kda_decode_tokens(q, k, v, g, beta, state, slot_idx=None, o=None, token_states=None,
                       stream=None):
-    """n_tok consecutive tokens per sequence.  q, k, g: [B, n_tok, H, dk];
-    v: [B, n_tok, H, dv]; beta: [B, n_tok, H]; state [n_slots, H, dk, dv] fp32
-    updated in place.  token_states: None, True (allocate [B, n_tok, H, dk, dv])
+    """n_tok consecutive tokens per sequence.  q, k: [B, n_tok, H, dk]; g: the same
+    shape or [B, n_tok, H]; v: [B, n_tok, H, dv]; beta: [B, n_tok, H]; state
+    [n_slots, H, dk, dv] fp32 updated in place.  token_states: None, True (allocate [B, n_tok, H, dk, dv])
     or a tensor of that shape.  Returns (o [B, n_tok, H, dv], token_states)."""
     B, n_tok, H, dk = q.shape
     dv = v.shape[3]
@@ -199,7 +212,8 @@ def kda_decode_tokens(q, k, v, g, beta, state, slot_idx=None, o=None, token_stat
     if token_states is True:
         token_states = torch.empty((B, n_tok, H, dk, dv), dtype=torch.float32, device=q.device)
     _check(load().kda_decode_tokens(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _ptr(state),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
+        _ptr(state),
         state.shape[0], _ptr(slot_idx), B, n_tok, H, dk, dv, _ptr(o),
         _ptr(token_states) if token_states is not None else None, _stream(stream)))
     return o, token_states

@@ -26,8 +26,10 @@
  *   beta [tokens, H];  state [slots, H, d_k, d_v] (d_v contiguous: row i of a
  *   head's state belongs to key channel i).
  * - q, k, v and o share one dtype (KDA_F32 or KDA_BF16).  g (the log of the
- *   decay, alpha = exp(g)), beta and the state are always fp32.  No query scale
- *   is applied: a caller that wants one scales q.
+ *   decay, alpha = exp(g)), beta and the state are always fp32.  g is per key
+ *   channel ([..., H, d_k], KDA_GATE_CHANNEL) or per head ([..., H],
+ *   KDA_GATE_HEAD, alpha broadcast over the channels).  No query scale is
+ *   applied: a caller that wants one scales q.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
  *   call returns at once.  Arguments are checked on the host before anything is
  *   enqueued: a failed check returns a non-zero status and enqueues nothing.
@@ -60,6 +62,16 @@ typedef enum kda_dtype {
     KDA_BF16 = 1
 } kda_dtype;
 
+/* Layout of the log decay g.  KDA decays every key channel separately; its
+ * special case with one decay per head and token is Gated DeltaNet, which
+ * page "Ling-3.1-flash and the 7:1 hybrid: how much KV cache does a 560B model
+ * need at 1M tokens?" (section "Why would a model keep only 9 full-attention
+ * layers?") names as the layer KDA extends with finer-grained gating. */
+typedef enum kda_gate {
+    KDA_GATE_CHANNEL = 0, /* g [tokens, H, d_k]: alpha_t per key channel (KDA) */
+    KDA_GATE_HEAD = 1     /* g [tokens, H]: one alpha_t per head, all channels */
+} kda_gate;
+
 /* Text for a status code (static storage). */
 const char* kda_status_string(kda_status s);
 
@@ -86,7 +98,8 @@ kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
  * chunk tokens at a time (the chunked/WY form, exact up to rounding).
  *
  *   q, k            : [T, H, dk] dtype       v, o : [T, H, dv] dtype
- *   g               : [T, H, dk] fp32 (log decay; alpha = exp(g))
+ *   g               : [T, H, dk] fp32 (log decay; alpha = exp(g)), or [T, H]
+ *                     with gate = KDA_GATE_HEAD
  *   beta            : [T, H] fp32
  *   cu_seqlens_dev  : [n_seqs + 1] int32 on the device
  *   cu_seqlens_host : the same values in host memory (validated: cu[0] = 0,
@@ -122,7 +135,7 @@ kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
  * kda_prefill_workspace_bytes or overlapping another argument.
  */
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
-                               const float* g, const float* beta, kda_dtype dtype,
+                               const float* g, const float* beta, kda_dtype dtype, kda_gate gate,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
                                const float* initial_state, float* final_state, void* o,
@@ -144,7 +157,7 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
  * kda_decode_step -- advance B sequences by one token each, in place.
  *
  *   q, k     : [B, H, dk] dtype        v, o : [B, H, dv] dtype
- *   g        : [B, H, dk] fp32         beta : [B, H] fp32
+ *   g        : [B, H, dk] fp32 ([B, H] with KDA_GATE_HEAD)    beta : [B, H] fp32
  *   state    : [n_slots, H, dk, dv] fp32, read and written in place.
  *   slot_idx : [B] int32 on the device giving each sequence's state slot, or
  *              NULL for slot b = b (then n_slots >= B).  Slots must be
@@ -154,7 +167,8 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
  * written once (fused form of one recurrence step).
  */
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                           const float* beta, kda_dtype dtype, kda_gate gate, float* state,
+                           int64_t n_slots,
                            const int32_t* slot_idx, int B, int H, int dk, int dv, void* o,
                            hipStream_t stream);
 
@@ -172,7 +186,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
  * sequence by the drafted tokens at once.
  *
  *   q, k         : [B, n_tok, H, dk] dtype    v, o : [B, n_tok, H, dv] dtype
- *   g            : [B, n_tok, H, dk] fp32     beta : [B, n_tok, H] fp32
+ *   g            : [B, n_tok, H, dk] fp32 ([B, n_tok, H] with KDA_GATE_HEAD)
+ *   beta         : [B, n_tok, H] fp32
  *   state        : [n_slots, H, dk, dv] fp32, read and written in place; on
  *                  return it holds the state after the last token.
  *   slot_idx     : as in kda_decode_step.
@@ -186,7 +201,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
  * that sequence to NaN.
  */
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, kda_dtype dtype, float* state, int64_t n_slots,
+                             const float* beta, kda_dtype dtype, kda_gate gate, float* state,
+                             int64_t n_slots,
                              const int32_t* slot_idx, int B, int n_tok, int H, int dk, int dv,
                              void* o, float* token_states, hipStream_t stream);
 

@@ -60,6 +60,8 @@ def oracle_on(inp, heads=None, precision="f64"):
     k = np64(inp.k[:, sel])
     v = np64(inp.v[:, sel])
     g = np64(inp.g[:, sel])
+    if g.ndim == 2:  # one decay per head: the same alpha on every key channel
+        g = np.repeat(g[:, :, None], q.shape[2], axis=2)
     beta = np64(inp.beta[:, sel])
     S0 = None if inp.S0 is None else np64(inp.S0[:, sel])
     return oracle.recurrence(q, k, v, g, beta, cu_seqlens=inp.cu_seqlens.numpy(), S0=S0,

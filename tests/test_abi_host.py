@@ -53,12 +53,13 @@ def cu_arr(vals):
 
 
 def prefill(lib, **kw):
-    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, cu_dev=Fp, cu_host=cu_arr([0, 8]),
-             n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, o=Gp, ws=None, ws_bytes=0,
-             stream=None)
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=0, cu_dev=Fp,
+             cu_host=cu_arr([0, 8]), n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, o=Gp,
+             ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
-                                   a["cu_dev"], a["cu_host"], a["n"], a["H"], a["dk"], a["dv"],
+                                   a["gate"], a["cu_dev"], a["cu_host"], a["n"], a["H"], a["dk"],
+                                   a["dv"],
                                    a["chunk"], a["s0"], a["sf"], a["o"], a["ws"], a["ws_bytes"],
                                    a["stream"])
 
@@ -69,6 +70,7 @@ def prefill(lib, **kw):
     (dict(H=0), KDA_ERR_INVALID_ARGUMENT, "positive"),
     (dict(chunk=48), KDA_ERR_INVALID_ARGUMENT, "chunk"),
     (dict(dtype=7), KDA_ERR_INVALID_ARGUMENT, "dtype"),
+    (dict(gate=2), KDA_ERR_INVALID_ARGUMENT, "gate layout"),
     (dict(n=-1), KDA_ERR_INVALID_ARGUMENT, "n_seqs"),
     (dict(cu_host=None), KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host"),
     (dict(cu_host=cu_arr([1, 8])), KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0]"),
@@ -111,16 +113,17 @@ def test_prefill_nothing_to_do(lib):
 
 
 def decode(lib, **kw):
-    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_F32, state=Fp, n_slots=4, slot=None, B=4,
-             H=2, dk=64, dv=64, o=Gp, stream=None)
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_F32, gate=0, state=Fp, n_slots=4,
+             slot=None, B=4, H=2, dk=64, dv=64, o=Gp, stream=None)
     a.update(kw)
-    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"], a["state"],
-                               a["n_slots"], a["slot"], a["B"], a["H"], a["dk"], a["dv"], a["o"],
-                               a["stream"])
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"], a["gate"],
+                               a["state"], a["n_slots"], a["slot"], a["B"], a["H"], a["dk"],
+                               a["dv"], a["o"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(dk=48, dv=48), KDA_ERR_UNSUPPORTED, "head dim"),
+    (dict(gate=-1), KDA_ERR_INVALID_ARGUMENT, "gate layout"),
     (dict(B=-1), KDA_ERR_INVALID_ARGUMENT, ">= 0"),
     (dict(n_slots=3), KDA_ERR_INVALID_ARGUMENT, "n_slots"),
     (dict(state=None), KDA_ERR_INVALID_ARGUMENT, "required"),
@@ -135,12 +138,13 @@ def test_decode_rejects(lib, kw, status, needle):
 
 
 def decode_tokens(lib, **kw):
-    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, state=Fp, n_slots=4, slot=None, B=4,
-             n_tok=3, H=2, dk=128, dv=128, o=Gp, snaps=None, stream=None)
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=1, state=Fp, n_slots=4,
+             slot=None, B=4, n_tok=3, H=2, dk=128, dv=128, o=Gp, snaps=None, stream=None)
     a.update(kw)
     return lib.kda_decode_tokens(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
-                                 a["state"], a["n_slots"], a["slot"], a["B"], a["n_tok"], a["H"],
-                                 a["dk"], a["dv"], a["o"], a["snaps"], a["stream"])
+                                 a["gate"], a["state"], a["n_slots"], a["slot"], a["B"],
+                                 a["n_tok"], a["H"], a["dk"], a["dv"], a["o"], a["snaps"],
+                                 a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,needle", [

@@ -13,7 +13,8 @@ sigma):
   norm in fp32, then rounded to the input dtype.
 * v ~ N(0, 1), rounded to the input dtype.
 * g = log(sigmoid(N(mu_g, sigma_g))) per (token, head, key channel), fp32; the
-  decay is alpha = exp(g) in (0, 1).
+  decay is alpha = exp(g) in (0, 1).  The per-head-decay variant draws one g
+  per (token, head) from the same recipe.
 * beta = sigmoid(N(0, 1)) per (token, head), fp32.
 * initial states ~ N(0, s0_std) fp32 where a workload has one, else zero.
 * mixer workload: pre-convolution streams x_q, x_k, x_v ~ N(0, 1) rounded to
@@ -91,7 +92,7 @@ class RecurrenceInputs:
     q: torch.Tensor          # [T, H, dk]  dtype
     k: torch.Tensor          # [T, H, dk]  dtype
     v: torch.Tensor          # [T, H, dv]  dtype
-    g: torch.Tensor          # [T, H, dk]  fp32 (log of the decay)
+    g: torch.Tensor          # [T, H, dk] or [T, H]  fp32 (log of the decay)
     beta: torch.Tensor       # [T, H]      fp32
     cu_seqlens: torch.Tensor  # [n+1] int32
     S0: torch.Tensor | None  # [n, H, dk, dv] fp32
@@ -116,15 +117,20 @@ class RecurrenceInputs:
 
 
 def recurrence_inputs(seqlens, H, d, dtype="bf16", chunk=64, g_mu=2.0, g_sigma=0.5,
-                      s0_std=0.0, seed=0, dv=None) -> RecurrenceInputs:
+                      s0_std=0.0, seed=0, dv=None, gate="channel") -> RecurrenceInputs:
+    """gate "channel": g [T, H, d], one log decay per key channel; "head":
+    g [T, H], one per head (drawn from the same recipe)."""
     dv = d if dv is None else dv
+    if gate not in ("channel", "head"):
+        raise ValueError(gate)
     seqlens = [int(s) for s in seqlens]
     T = sum(seqlens)
     cu = torch.tensor([0] + list(np.cumsum(seqlens)), dtype=torch.int32)
     q = to_dtype(_unit_rows(normal((T, H, d), seed, TID["q"])), dtype)
     k = to_dtype(_unit_rows(normal((T, H, d), seed, TID["k"])), dtype)
     v = to_dtype(normal((T, H, dv), seed, TID["v"]), dtype)
-    g = torch.nn.functional.logsigmoid(normal((T, H, d), seed, TID["g"], g_mu, g_sigma))
+    g_shape = (T, H, d) if gate == "channel" else (T, H)
+    g = torch.nn.functional.logsigmoid(normal(g_shape, seed, TID["g"], g_mu, g_sigma))
     beta = torch.sigmoid(normal((T, H), seed, TID["beta"]))
     S0 = None
     if s0_std > 0:
