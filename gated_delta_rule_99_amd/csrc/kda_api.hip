@@ -110,6 +110,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
                                const float* initial_state, float* final_state, void* o,
+                               float* snapshots, int snap_interval, int snap_capacity,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const char* fn = "kda_prefill_chunked";
     g_detail[0] = 0;
@@ -157,6 +158,28 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
          overlaps(final_state, sbytes, v, n_qk * es) || overlaps(final_state, sbytes, g, n_g * 4)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state overlaps an input", fn);
 
+    // snapshots: [n_seqs, snap_capacity, H, dk, dv] fp32
+    if (snapshots) {
+        if (snap_interval <= 0 || snap_interval % chunk)
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "%s: snap_interval %d must be a positive multiple of chunk %d", fn,
+                        snap_interval, chunk);
+        if (snap_capacity < 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: snap_capacity < 0", fn);
+        if (!aligned16(snapshots))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned snapshots", fn);
+        const size_t snb = (size_t)n_seqs * snap_capacity * kda_state_bytes(H, dk, dv);
+        if (overlaps(snapshots, snb, q, n_qk * es) || overlaps(snapshots, snb, k, n_qk * es) ||
+            overlaps(snapshots, snb, v, n_qk * es) || overlaps(snapshots, snb, g, n_g * 4) ||
+            overlaps(snapshots, snb, beta, n_bt * 4) || overlaps(snapshots, snb, o, n_qk * es) ||
+            overlaps(snapshots, snb, initial_state, sbytes) ||
+            overlaps(snapshots, snb, final_state, sbytes) ||
+            overlaps(snapshots, snb, workspace, workspace ? workspace_bytes : 0))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: snapshots overlap another argument", fn);
+        if (snap_capacity == 0) snapshots = nullptr;
+    }
+    const kda::Snapshots snap{snapshots, snapshots ? snap_interval : 0, snap_capacity};
+
     const bool mfma = mfma_shape(dtype, dk, dv, chunk);
     const size_t ws_need = mfma ? kda::prefill_split_workspace_bytes(n_seqs, H) : 0;
     if (mfma && workspace) {
@@ -182,14 +205,14 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
         }
         err = kda::launch_prefill_split(q, k, v, g, beta, gate == KDA_GATE_HEAD, cu_seqlens_dev,
                                         n_seqs, T, H, max_chunks, initial_state, final_state, o,
-                                        workspace, stream);
+                                        snap, workspace, stream);
     } else if (mfma)
         err = kda::launch_prefill_fused(q, k, v, g, beta, gate == KDA_GATE_HEAD, cu_seqlens_dev,
-                                        n_seqs, T, H, initial_state, final_state, o, stream);
+                                        n_seqs, T, H, initial_state, final_state, o, snap, stream);
     else
         err = kda::launch_prefill_vector(q, k, v, g, beta, dtype, gate == KDA_GATE_HEAD,
-                                         cu_seqlens_dev, n_seqs, T, H,
-                                         d, chunk, initial_state, final_state, o, stream);
+                                         cu_seqlens_dev, n_seqs, T, H, d, chunk, initial_state,
+                                         final_state, o, snap, stream);
     return hip_status(err, "kda_prefill_chunked launch");
 }
 

@@ -80,6 +80,26 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int64_t T, i
     e = hi;
 }
 
+// ---------------------------------------------------------------- snapshots
+// Chunk-aligned state snapshots of a prefill: entry [n][j] of ptr
+// ([n_seqs, capacity, H, D, D] fp32) is sequence n's state after its first
+// (j + 1) * interval tokens.  ptr == nullptr: none taken.
+struct Snapshots {
+    float* ptr;
+    int interval;  // tokens, a multiple of the chunk
+    int capacity;  // snapshots per sequence in the buffer
+};
+
+// Head h's D x D state of snapshot j of sequence n, or nullptr when no snapshot
+// is taken after `done` tokens of a sequence of `len` tokens.
+__device__ __forceinline__ float* snapshot_at(const Snapshots& sn, int n, int h, int H, int D,
+                                              int64_t done, int64_t len) {
+    if (!sn.ptr || done > len || done % sn.interval) return nullptr;
+    const int64_t j = done / sn.interval - 1;
+    if (j < 0 || j >= sn.capacity) return nullptr;
+    return sn.ptr + (((size_t)n * sn.capacity + j) * H + h) * (size_t)D * D;
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already checked.
 hipError_t launch_state_init(float* state, int64_t n_floats, const float* src,
@@ -96,14 +116,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, kda_dtype dtype, bool g_head, const int32_t* cu,
                                  int n_seqs, int64_t T, int H, int d, int chunk,
-                                 const float* s0, float* s_final, void* o, hipStream_t stream);
+                                 const float* s0, float* s_final, void* o, Snapshots snap,
+                                 hipStream_t stream);
 
 // bf16, d = 128, chunk = 64, one fused kernel (no workspace).
 hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, bool g_head, const int32_t* cu, int n_seqs,
-                                int64_t T,
-                                int H, const float* s0, float* s_final, void* o,
-                                hipStream_t stream);
+                                int64_t T, int H, const float* s0, float* s_final, void* o,
+                                Snapshots snap, hipStream_t stream);
 
 // bf16, d = 128, chunk = 64, two kernels through a caller workspace of
 // prefill_split_workspace_bytes(n_seqs, H) bytes; max_chunks = the longest
@@ -112,9 +132,9 @@ int prefill_split_window(int n_seqs, int H);
 size_t prefill_split_workspace_bytes(int n_seqs, int H);
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, bool g_head, const int32_t* cu, int n_seqs,
-                                int64_t T,
-                                int H, int max_chunks, const float* s0, float* s_final, void* o,
-                                void* workspace, hipStream_t stream);
+                                int64_t T, int H, int max_chunks, const float* s0,
+                                float* s_final, void* o, Snapshots snap, void* workspace,
+                                hipStream_t stream);
 
 hipError_t launch_short_conv_prefill(const void* x, const float* w, kda_dtype dtype,
                                      const int32_t* cu, int n_seqs, int64_t T, int channels,

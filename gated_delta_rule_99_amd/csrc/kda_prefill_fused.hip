@@ -56,7 +56,7 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const bf16_t* __restrict__ v, const float* __restrict__ g,
                      const float* __restrict__ beta, const int32_t* __restrict__ cu,
                      int64_t T, int H, int n_pairs, const float* __restrict__ s0,
-                     float* __restrict__ s_final, bf16_t* __restrict__ o) {
+                     float* __restrict__ s_final, bf16_t* __restrict__ o, Snapshots snap) {
     __shared__ __attribute__((aligned(16))) FusedLds sm;
     int pair, slice;
     {
@@ -214,7 +214,8 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 st4(sm.Ut + (16 * jb + r) * LDT + 16 * cw + 4 * q4, u);
             }
             __syncthreads();  // B2
-            // ---- [C] S <- G + Kb^T U; next G = Gam(s+1) * S
+            // ---- [C] S <- G + Kb^T U (a snapshot when one falls here); next G = Gam(s+1) * S
+            float* snp = snapshot_at(snap, n, h, H, D, (int64_t)(s + 1) * C, te - tb);
             float4 gm[2];
 #pragma unroll
             for (int a = 0; a < 2; ++a)
@@ -226,6 +227,11 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
                 for (int a = 0; a < 2; ++a) {
                     f32x4 st = mma32(Kb[a][1], u1, mma32(Kb[a][0], u0, S[a][jb]));
+                    if (snp) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            snp[(size_t)(32 * cw + 16 * a + 4 * q4 + e) * D + j0 + 16 * jb + r] = st[e];
+                    }
                     if (next) {
                         st[0] *= gm[a].x; st[1] *= gm[a].y; st[2] *= gm[a].z; st[3] *= gm[a].w;
                         st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, st);
@@ -297,15 +303,14 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
 hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, bool g_head, const int32_t* cu, int n_seqs,
-                                int64_t T,
-                                int H, const float* s0, float* s_final, void* o,
-                                hipStream_t stream) {
+                                int64_t T, int H, const float* s0, float* s_final, void* o,
+                                Snapshots snap, hipStream_t stream) {
     const int64_t n_pairs = (int64_t)n_seqs * H;
     if (n_pairs == 0) return hipSuccess;
     hipLaunchKernelGGL(g_head ? prefill_fused_kernel<true> : prefill_fused_kernel<false>,
                        dim3((unsigned)(n_pairs * NS)), dim3(768), 0, stream, (const bf16_t*)q,
                        (const bf16_t*)k, (const bf16_t*)v, g, beta, cu, T, H, (int)n_pairs, s0,
-                       s_final, (bf16_t*)o);
+                       s_final, (bf16_t*)o, snap);
     return hipGetLastError();
 }
 

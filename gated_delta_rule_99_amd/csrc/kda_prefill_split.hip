@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(512)
 state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64_t T, int H,
              int n_pairs, int w0, int win, const uint8_t* __restrict__ ws_tiles,
              float* __restrict__ ws_state, const float* __restrict__ s0,
-             float* __restrict__ s_final, bf16_t* __restrict__ o) {
+             float* __restrict__ s_final, bf16_t* __restrict__ o, Snapshots snap) {
     __shared__ __attribute__((aligned(16))) StateSmem sm;
     int pair, slice;
     {
@@ -301,7 +301,8 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
                 st4(sm.Ut + (16 * jb + r) * LDT + 16 * cw + 4 * q4, u);
             }
             __syncthreads();
-            // ---- S <- G + Kb^T U; next G
+            // ---- S <- G + Kb^T U (a snapshot when one falls here); next G
+            float* snp = snapshot_at(snap, n, h, H, D, (int64_t)(c + 1) * C, te - tb);
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb) {
                 const bf16x8 u0 = ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4);
@@ -309,6 +310,11 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
 #pragma unroll
                 for (int a = 0; a < 2; ++a) {
                     f32x4 s = mma32(cur.Kb[a][1], u1, mma32(cur.Kb[a][0], u0, S[a][jb]));
+                    if (snp) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            snp[(size_t)(32 * cw + 16 * a + 4 * q4 + e) * D + j0 + 16 * jb + r] = s[e];
+                    }
                     if (more) {
                         s[0] *= nxt.gam[a].x; s[1] *= nxt.gam[a].y;
                         s[2] *= nxt.gam[a].z; s[3] *= nxt.gam[a].w;
@@ -411,9 +417,9 @@ size_t prefill_split_workspace_bytes(int n_seqs, int H) {
 // that the tile round trip already saturates.)
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, bool g_head, const int32_t* cu, int n_seqs,
-                                int64_t T,
-                                int H, int max_chunks, const float* s0, float* s_final, void* o,
-                                void* workspace, hipStream_t stream) {
+                                int64_t T, int H, int max_chunks, const float* s0,
+                                float* s_final, void* o, Snapshots snap, void* workspace,
+                                hipStream_t stream) {
     const int64_t n_pairs = (int64_t)n_seqs * H;
     if (n_pairs == 0) return hipSuccess;
     const int win = prefill_split_window(n_seqs, H);
@@ -433,7 +439,7 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, con
         }
         hipLaunchKernelGGL(state_kernel, dim3((unsigned)(n_pairs * NS)), dim3(512), 0, stream,
                            (const bf16_t*)v, cu, T, H, (int)n_pairs, w0, win, tiles, ws_state, s0,
-                           s_final, (bf16_t*)o);
+                           s_final, (bf16_t*)o, snap);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

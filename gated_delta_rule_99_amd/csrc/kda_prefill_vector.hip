@@ -39,7 +39,7 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                       const Tin* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, int g_head, const int32_t* __restrict__ cu,
                       int64_t T, int H, const float* __restrict__ s0,
-                      float* __restrict__ s_final, Tin* __restrict__ o) {
+                      float* __restrict__ s_final, Tin* __restrict__ o, Snapshots snap) {
     using SH = VecShape<D, C>;
     constexpr int DVS = SH::DVS, NS = SH::NS, LD = SH::LD, NT = SH::NT;
     extern __shared__ float smem[];
@@ -151,13 +151,15 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
             In<Tin>::store1(o + (size_t)(c0 + t) * rowk + (size_t)h * D + j0 + j, acc);
         }
         __syncthreads();
-        // S <- Gam * S + (Kh * Gam)^T U
+        // S <- Gam * S + (Kh * Gam)^T U (and the snapshot when one falls here)
+        float* snp = snapshot_at(snap, n, h, H, D, c0 + L - tb, te - tb);
         for (int e = tid; e < D * DVS; e += NT) {
             const int i = e / DVS, j = e % DVS;
             const float gm = sGam[i];
             float acc = 0.f;
             for (int t = 0; t < C; ++t) acc += (sKh[t * LD + i] * gm) * sU[t * DVS + j];
             sS[e] = gm * sS[e] + acc;
+            if (snp) snp[(size_t)i * D + j0 + j] = sS[e];
         }
     }
     __syncthreads();
@@ -172,9 +174,8 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
 template <int D, int C, typename Tin>
 static hipError_t launch_vec_t(const void* q, const void* k, const void* v, const float* g,
                                const float* beta, bool g_head, const int32_t* cu, int n_seqs,
-                               int64_t T,
-                               int H, const float* s0, float* s_final, void* o,
-                               hipStream_t stream) {
+                               int64_t T, int H, const float* s0, float* s_final, void* o,
+                               Snapshots snap, hipStream_t stream) {
     using SH = VecShape<D, C>;
     const int64_t blocks = (int64_t)n_seqs * H * SH::NS;
     if (blocks == 0) return hipSuccess;
@@ -185,7 +186,7 @@ static hipError_t launch_vec_t(const void* q, const void* k, const void* v, cons
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(SH::NT), SH::BYTES, stream,
                        (const Tin*)q, (const Tin*)k, (const Tin*)v, g, beta, (int)g_head, cu, T, H,
-                       s0, s_final, (Tin*)o);
+                       s0, s_final, (Tin*)o, snap);
     return hipGetLastError();
 }
 
@@ -193,11 +194,11 @@ template <int D, typename Tin>
 static hipError_t launch_vec_c(int chunk, const void* q, const void* k, const void* v,
                                const float* g, const float* beta, bool g_head, const int32_t* cu,
                                int n_seqs, int64_t T, int H, const float* s0, float* s_final,
-                               void* o, hipStream_t stream) {
+                               void* o, Snapshots snap, hipStream_t stream) {
     switch (chunk) {
-        case 16: return launch_vec_t<D, 16, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, stream);
-        case 32: return launch_vec_t<D, 32, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, stream);
-        case 64: return launch_vec_t<D, 64, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, stream);
+        case 16: return launch_vec_t<D, 16, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
+        case 32: return launch_vec_t<D, 32, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
+        case 64: return launch_vec_t<D, 64, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -205,14 +206,15 @@ static hipError_t launch_vec_c(int chunk, const void* q, const void* k, const vo
 hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, kda_dtype dtype, bool g_head, const int32_t* cu,
                                  int n_seqs, int64_t T, int H, int d, int chunk,
-                                 const float* s0, float* s_final, void* o, hipStream_t stream) {
+                                 const float* s0, float* s_final, void* o, Snapshots snap,
+                                 hipStream_t stream) {
 #define KDA_VEC(D)                                                                            \
     if (d == D) {                                                                             \
         if (dtype == KDA_BF16)                                                                \
             return launch_vec_c<D, bf16_t>(chunk, q, k, v, g, beta, g_head, cu, n_seqs, T, H, \
-                                           s0, s_final, o, stream);                           \
+                                           s0, s_final, o, snap, stream);                     \
         return launch_vec_c<D, float>(chunk, q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0,  \
-                                      s_final, o, stream);                                    \
+                                      s_final, o, snap, stream);                              \
     }
     KDA_VEC(16)
     KDA_VEC(32)

@@ -39,7 +39,8 @@ _SIGNATURES = {
     "kda_state_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
     "kda_state_init": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
-                                   _i32, _i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+                                   _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+                                   ctypes.c_size_t, _vp]),
     "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i64, _vp, _i32, _i32,
                                _i32, _i32, _vp, _vp]),
@@ -156,17 +157,30 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
                         initial_state=None, final_state=None, o=None,
                         output_final_state: bool = True, cu_seqlens_host=None,
-                        workspace="auto", stream=None):
+                        workspace="auto", snapshots=None, snap_interval: int = 0,
+                        stream=None):
     """Chunked prefill over packed sequences.  q, k: [T, H, dk]; v: [T, H, dv];
     g: [T, H, dk] (per-channel decay) or [T, H] (per-head decay); beta: [T, H].
-    Returns (o, final_state or None).
+    Returns (o, final_state or None), or (o, final_state, snapshots) when
+    snapshots is given.
 
     workspace: "auto" (a cached device buffer of kda_prefill_workspace_bytes),
-    a uint8 device tensor, or None (no workspace: the fused kernel)."""
+    a uint8 device tensor, or None (no workspace: the fused kernel).
+    snapshots: None, True (allocate [n_seqs, longest // snap_interval, H, dk, dv]
+    fp32 zeros) or such a tensor; entry [n, j] receives sequence n's state after
+    (j + 1) * snap_interval tokens where it has that many."""
     T, H, dk = q.shape
     dv = v.shape[2]
     cu_dev, cu_host = _cu_pair(cu_seqlens, cu_seqlens_host, T, q.device)
     n_seqs = cu_host.numel() - 1
+    want_snaps = snapshots is not None
+    if snapshots is True:
+        if snap_interval <= 0:
+            raise ValueError("snap_interval must be positive")
+        lens = cu_host[1:] - cu_host[:-1]
+        cap = int(lens.max()) // snap_interval if n_seqs else 0
+        snapshots = torch.zeros((n_seqs, cap, H, dk, dv), dtype=torch.float32, device=q.device)
+    snap_cap = 0 if snapshots is None else int(snapshots.shape[1])
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
@@ -180,7 +194,10 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     _check(load().kda_prefill_chunked(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
         _ptr(cu_dev), cu_host.data_ptr(), n_seqs, H, dk, dv, int(chunk), _ptr(initial_state),
-        _ptr(final_state), _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(final_state), _ptr(o), _ptr(snapshots), int(snap_interval), snap_cap,
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    if want_snaps:
+        return o, final_state, snapshots
     return o, final_state
 
 

@@ -113,6 +113,22 @@ kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
  *   final_state     : [n_seqs, H, dk, dv] fp32, or NULL (not written).  May be
  *                     the same pointer as initial_state (in-place update).
  *   o               : [T, H, dv] dtype, written; must not overlap any input.
+ *   snapshots       : [n_seqs, snap_capacity, H, dk, dv] fp32, or NULL.  Entry
+ *                     [n, j] receives sequence n's state after its first
+ *                     (j + 1) * snap_interval tokens, for every j below
+ *                     snap_capacity with (j + 1) * snap_interval <= its
+ *                     length; other entries are left untouched.  These are the
+ *                     chunk-aligned states a prefix cache keeps for recurrent
+ *                     layers (page "Ling-3.1-flash and the 7:1 hybrid: how much
+ *                     KV cache does a 560B model need at 1M tokens?", section
+ *                     "How should I decide whether a hybrid fits my workload?":
+ *                     the serving engine manages the linear state like
+ *                     recurrent-model state, block-aligned, and prefix caching
+ *                     behaves differently for it).  Must not overlap any other
+ *                     argument.
+ *   snap_interval   : tokens between snapshots, a positive multiple of chunk
+ *                     (ignored when snapshots is NULL).
+ *   snap_capacity   : snapshots per sequence that the buffer holds (>= 0).
  *   workspace       : device scratch of at least workspace_bytes =
  *                     kda_prefill_workspace_bytes(...) bytes, 16-byte aligned,
  *                     owned by the caller, not overlapping any other argument;
@@ -139,6 +155,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
                                const float* initial_state, float* final_state, void* o,
+                               float* snapshots, int snap_interval, int snap_capacity,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -21,6 +21,7 @@ Dp = 0x60000000
 Ep = 0x80000000
 Fp = 0xA0000000
 Gp = 0xC0000000
+Hp = 0xE0000000
 
 
 @pytest.fixture(scope="module")
@@ -55,12 +56,13 @@ def cu_arr(vals):
 def prefill(lib, **kw):
     a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=0, cu_dev=Fp,
              cu_host=cu_arr([0, 8]), n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, o=Gp,
-             ws=None, ws_bytes=0, stream=None)
+             snaps=None, snap_interval=0, snap_capacity=0, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
                                    a["gate"], a["cu_dev"], a["cu_host"], a["n"], a["H"], a["dk"],
                                    a["dv"],
-                                   a["chunk"], a["s0"], a["sf"], a["o"], a["ws"], a["ws_bytes"],
+                                   a["chunk"], a["s0"], a["sf"], a["o"], a["snaps"],
+                                   a["snap_interval"], a["snap_capacity"], a["ws"], a["ws_bytes"],
                                    a["stream"])
 
 
@@ -84,6 +86,18 @@ def prefill(lib, **kw):
     (dict(ws=0x9000000, ws_bytes=1024), KDA_ERR_INVALID_ARGUMENT, "needed"),
     (dict(ws=0x9000008, ws_bytes=1 << 30), KDA_ERR_INVALID_ARGUMENT, "misaligned workspace"),
     (dict(ws=A - 4096, ws_bytes=1 << 30), KDA_ERR_INVALID_ARGUMENT, "workspace overlaps"),
+    (dict(snaps=Hp, snap_interval=48, snap_capacity=1), KDA_ERR_INVALID_ARGUMENT,
+     "positive multiple of chunk"),
+    (dict(snaps=Hp, snap_interval=0, snap_capacity=1), KDA_ERR_INVALID_ARGUMENT,
+     "positive multiple of chunk"),
+    (dict(snaps=Hp, snap_interval=64, snap_capacity=-1), KDA_ERR_INVALID_ARGUMENT,
+     "snap_capacity"),
+    (dict(snaps=Hp + 8, snap_interval=64, snap_capacity=1), KDA_ERR_INVALID_ARGUMENT,
+     "misaligned snapshots"),
+    (dict(snaps=Gp - 65536, snap_interval=64, snap_capacity=1), KDA_ERR_INVALID_ARGUMENT,
+     "snapshots overlap"),
+    (dict(snaps=Hp, snap_interval=64, snap_capacity=2, s0=Hp + 2 * 65536),
+     KDA_ERR_INVALID_ARGUMENT, "snapshots overlap"),
 ])
 def test_prefill_rejects(lib, kw, status, needle):
     assert prefill(lib, **kw) == status
