@@ -37,7 +37,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc")
 SOURCES = {
     PREFILL_KERNEL: [os.path.join(_CSRC, "kda_prefill_split.hip"),
-                     os.path.join(_CSRC, "kda_chunk_ops.h")],
+                     os.path.join(_CSRC, "kda_chunk_ops.h"),
+                     os.path.join(_CSRC, "kda_state_pass.h")],
     DECODE_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
     DECODE_TOKENS_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
 }

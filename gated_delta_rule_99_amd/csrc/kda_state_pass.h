@@ -1,0 +1,276 @@
+// Operand tiles and the pieces of the state pass of the two-kernel prefill
+// (kda_prefill_split.hip): the tile layout, the exports that write a tile from
+// the operand stages' LDS, and the chain and output waves' per-chunk steps.
+//
+// A tile holds everything the state pass needs of one (sequence, head, chunk)
+// that does not depend on the state, in the exact lane order of the state
+// pass's MFMA operands, so that each lane reads one contiguous 16-byte
+// fragment.  Byte offsets:
+//   0      Kt fragments   [row block c 0..3][kk 0..3][lane 64][16 B]
+//   16384  Qt fragments   same
+//   32768  Kb^T fragments [c 0..3][a 0..1][kk 0..1][lane][16 B]   (rows 32c+16a)
+//   49152  T fragments    [c 0..3][kk 0..1][lane][16 B]
+//   57344  P fragments    same
+//   65536  beta[64] fp32, 65792 Gam[128] fp32
+//
+// State pass of one (sequence, head, 32-column slice of the state), 8 waves
+// (recurrence from page "Ling-3.1-flash: a 560B hybrid-attention MoE, counted
+// from its safetensors headers", section "How KDA and MLA split the work"):
+// waves 0-3 carry the chain that the next chunk depends on,
+//   Y = Kt G,  R = diag(beta)(V - Y),  U = T R,  S <- G + Kb^T U,  G' = Gam' S;
+// waves 4-7 produce the output off that chain, Z = Qt G and O = Z + P U.
+// Wave c of either group owns rows [16c, 16c+16) of the chunk (Y, R, U, Z, O)
+// and chain wave c owns state rows [32c, 32c+32) of the slice.  Per chunk the
+// two groups meet at three barriers: R complete, U complete, next G complete.
+// V and O move with one 16-byte access per lane (16 rows x 32 columns per wave)
+// and are turned into the accumulator layout (lane (r, q4) holds rows 4q4 + e
+// of column r) through a staging tile that only the wave itself touches.
+#pragma once
+
+#include "kda_chunk_ops.h"
+
+namespace kda {
+namespace co {
+
+constexpr int DVS = 32, NS = D / DVS;  // state columns per workgroup, slices per head
+constexpr int TILE = 66304;
+constexpr int OFF_KT = 0, OFF_QT = 16384, OFF_KBT = 32768, OFF_T = 49152, OFF_P = 57344,
+              OFF_BETA = 65536, OFF_GAM = 65792;
+constexpr int LDX = 40;  // row stride (bf16) of the V and O staging tiles
+
+// ---------------------------------------------------------------- tile export
+// The decay stage's sinks: Gam and the Kb^T fragments go straight to the tile.
+struct TileSinks {
+    __amdgpu_buffer_rsrc_t rt;
+    __device__ __forceinline__ void operator()(int ch0, const float (&gam)[4]) const {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(gam[0]), __float_as_uint(gam[1]), __float_as_uint(gam[2]),
+                  __float_as_uint(gam[3])},
+            rt, OFF_GAM + 4 * ch0, 0, 0);
+    }
+    __device__ __forceinline__ void operator()(int i, int tg, u32x4 piece) const {
+        // Kb^T fragment (row block i / 16, k block tg / 4), lane (i % 16, tg % 4)
+        const int blk = (i >> 5) * 4 + ((i >> 4) & 1) * 2 + (tg >> 2);
+        const int ln = (i & 15) + 16 * (tg & 3);
+        __builtin_amdgcn_raw_buffer_store_b128(piece, rt, OFF_KBT + (blk * 64 + ln) * 16, 0, 0);
+    }
+};
+
+// beta of the chunk (wave 0 holds one token per lane).
+__device__ __forceinline__ void tile_beta(__amdgpu_buffer_rsrc_t rt, const ChunkIn& in, int p,
+                                          int lane) {
+    if (p == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(in.beta), rt, OFF_BETA + 4 * lane, 0,
+                                              0);
+}
+
+// Kt and Qt fragments out of LDS (wave p exports row block p); after the decay
+// stage is visible.
+__device__ __forceinline__ void tile_export_kq(const ChunkLds& sm, __amdgpu_buffer_rsrc_t rt,
+                                               int p, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = ld8(sm.Kt + (16 * p + r) * LDK + 32 * kk + 8 * q4);
+        const bf16x8 b = ld8(sm.Qt + (16 * p + r) * LDK + 32 * kk + 8 * q4);
+        __builtin_amdgcn_raw_buffer_store_b128(as_u4(a), rt, OFF_KT + ((p * 4 + kk) * 64 + lane) * 16,
+                                               0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(as_u4(b), rt, OFF_QT + ((p * 4 + kk) * 64 + lane) * 16,
+                                               0, 0);
+    }
+}
+
+// T and P fragments out of LDS (wave p exports row block p); after the merge
+// stage is visible.
+__device__ __forceinline__ void tile_export_tp(const ChunkLds& sm, __amdgpu_buffer_rsrc_t rt,
+                                               int p, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = ld8(sm.T + (16 * p + r) * LDT + 32 * kk + 8 * q4);
+        const bf16x8 b = ld8(sm.P + (16 * p + r) * LDT + 32 * kk + 8 * q4);
+        __builtin_amdgcn_raw_buffer_store_b128(as_u4(a), rt, OFF_T + ((p * 2 + kk) * 64 + lane) * 16,
+                                               0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(as_u4(b), rt, OFF_P + ((p * 2 + kk) * 64 + lane) * 16,
+                                               0, 0);
+    }
+}
+
+// ---------------------------------------------------------------- state pass
+struct StateLds {
+    uint16_t Gt[DVS * LDK];  // bf16 (Gam * S)^T [j][i]
+    uint16_t Rt[DVS * LDT];  // R^T [j][t]
+    uint16_t Ut[DVS * LDT];  // U^T [j][t]
+    uint16_t V[C * LDX];     // V slice [t][j]: each chain wave stages its own 16 rows
+    uint16_t O[C * LDX];     // O slice [t][j]: each output wave stages its own 16 rows
+};
+
+struct ChainFrags {
+    bf16x8 K[4], Kb[2][2], T[2];
+    float4 bet, gam[2];
+    uint4 v;  // V[16c + (lane >> 2)][8 (lane & 3) + 0..7]
+};
+struct OutFrags {
+    bf16x8 Q[4], P[2];
+};
+
+__device__ __forceinline__ bf16x8 ld_frag(__amdgpu_buffer_rsrc_t rt, int off) {
+    return as_bf8(__builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+}
+__device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t rt, int off) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0);
+    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                       __uint_as_float(x[3]));
+}
+
+// Chain fragments, first half: Kt, beta, Gam, and this lane's piece of V
+// (rv: the chunk's V rows of the slice; xoff: the piece's byte offset).
+__device__ __forceinline__ void chain_load_a(ChainFrags& f, __amdgpu_buffer_rsrc_t rt,
+                                             __amdgpu_buffer_rsrc_t rv, int xoff, int cw,
+                                             int lane) {
+    const int q4 = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) f.K[kk] = ld_frag(rt, OFF_KT + ((cw * 4 + kk) * 64 + lane) * 16);
+    f.bet = ld_f4(rt, OFF_BETA + (16 * cw + 4 * q4) * 4);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) f.gam[a] = ld_f4(rt, OFF_GAM + (32 * cw + 16 * a + 4 * q4) * 4);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, xoff, 0, 0);
+    f.v = make_uint4(x[0], x[1], x[2], x[3]);
+}
+// Chain fragments, second half: Kb^T and T.
+__device__ __forceinline__ void chain_load_b(ChainFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
+                                             int lane) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            f.Kb[a][kk] = ld_frag(rt, OFF_KBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) f.T[kk] = ld_frag(rt, OFF_T + ((cw * 2 + kk) * 64 + lane) * 16);
+}
+__device__ __forceinline__ void out_load_a(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
+                                           int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) f.Q[kk] = ld_frag(rt, OFF_QT + ((cw * 4 + kk) * 64 + lane) * 16);
+}
+__device__ __forceinline__ void out_load_b(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
+                                           int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) f.P[kk] = ld_frag(rt, OFF_P + ((cw * 2 + kk) * 64 + lane) * 16);
+}
+
+// S[a][jb] holds S[32cw + 16a + 4q4 + e][16jb + r] of the slice.
+typedef f32x4 StateFrag[2][2];
+
+// S *= Gam (per row) and the bf16 copy of G = Gam * S into Gt.
+__device__ __forceinline__ void chain_scale_store(StateLds& sm, StateFrag& S, const float4 (&gam)[2],
+                                                  int cw, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            S[a][jb][0] *= gam[a].x; S[a][jb][1] *= gam[a].y;
+            S[a][jb][2] *= gam[a].z; S[a][jb][3] *= gam[a].w;
+            st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, S[a][jb]);
+        }
+}
+
+// Stage this wave's V rows (read back by the same wave only).
+__device__ __forceinline__ void chain_stage_v(StateLds& sm, const uint4& v, int xrow, int xcol) {
+    *reinterpret_cast<uint4*>(sm.V + xrow * LDX + xcol) = v;
+    __builtin_amdgcn_wave_barrier();
+}
+
+// [A] Y = Kt G; R = diag(beta)(V - Y) into Rt.
+__device__ __forceinline__ void chain_yr(StateLds& sm, const ChainFrags& cur, int cw, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+    f32x4 Y[2] = {Z4, Z4};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        Y[0] = mma32(cur.K[kk], ld8(sm.Gt + r * LDK + 32 * kk + 8 * q4), Y[0]);
+        Y[1] = mma32(cur.K[kk], ld8(sm.Gt + (16 + r) * LDK + 32 * kk + 8 * q4), Y[1]);
+    }
+    const float bb[4] = {cur.bet.x, cur.bet.y, cur.bet.z, cur.bet.w};
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        f32x4 rv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            rv[e] = bb[e] * (bf16_bits_to_f32(sm.V[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r]) -
+                             Y[jb][e]);
+        st4(sm.Rt + (16 * jb + r) * LDT + 16 * cw + 4 * q4, rv);
+    }
+}
+
+// [B] U = T R into Ut.
+__device__ __forceinline__ void chain_u(StateLds& sm, const ChainFrags& cur, int cw, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        f32x4 u = mma32(cur.T[0], ld8(sm.Rt + (16 * jb + r) * LDT + 8 * q4), Z4);
+        if (cw >= 2) u = mma32(cur.T[1], ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4), u);
+        st4(sm.Ut + (16 * jb + r) * LDT + 16 * cw + 4 * q4, u);
+    }
+}
+
+// [C] S <- G + Kb^T U; the raw S to snp (a snapshot) when snp is set; with
+// more, the next G = Gam' S into Gt.
+__device__ __forceinline__ void chain_s(StateLds& sm, const ChainFrags& cur,
+                                        const float4 (&gam_next)[2], bool more, StateFrag& S,
+                                        float* snp, int j0, int cw, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        const bf16x8 u0 = ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4);
+        const bf16x8 u1 = ld8(sm.Ut + (16 * jb + r) * LDT + 32 + 8 * q4);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            f32x4 s = mma32(cur.Kb[a][1], u1, mma32(cur.Kb[a][0], u0, S[a][jb]));
+            if (snp) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    snp[(size_t)(32 * cw + 16 * a + 4 * q4 + e) * D + j0 + 16 * jb + r] = s[e];
+            }
+            if (more) {
+                s[0] *= gam_next[a].x; s[1] *= gam_next[a].y;
+                s[2] *= gam_next[a].z; s[3] *= gam_next[a].w;
+                st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, s);
+            }
+            S[a][jb] = s;
+        }
+    }
+}
+
+// [A] Z = Qt G.
+__device__ __forceinline__ void out_z(StateLds& sm, const OutFrags& cur, f32x4 (&Zc)[2], int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+    Zc[0] = Z4;
+    Zc[1] = Z4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        Zc[0] = mma32(cur.Q[kk], ld8(sm.Gt + r * LDK + 32 * kk + 8 * q4), Zc[0]);
+        Zc[1] = mma32(cur.Q[kk], ld8(sm.Gt + (16 + r) * LDK + 32 * kk + 8 * q4), Zc[1]);
+    }
+}
+
+// [C] O = Z + P U, staged through this wave's rows; returns this lane's
+// 16-byte piece (row xrow, columns xcol ..) for one store.
+__device__ __forceinline__ u32x4 out_o(StateLds& sm, const OutFrags& cur, const f32x4 (&Zc)[2],
+                                       int cw, int lane, int xrow, int xcol) {
+    const int r = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        f32x4 acc = mma32(cur.P[0], ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
+        if (cw >= 2) acc = mma32(cur.P[1], ld8(sm.Ut + (16 * jb + r) * LDT + 32 + 8 * q4), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint4 x = *reinterpret_cast<const uint4*>(sm.O + xrow * LDX + xcol);
+    return u32x4{x.x, x.y, x.z, x.w};
+}
+
+}  // namespace co
+}  // namespace kda
