@@ -103,10 +103,61 @@ def cpu_baseline_run(inp):
     oracle.recurrence(q, k, v, g, beta, cu_seqlens=inp.cu_seqlens.numpy(), precision="f32",
                       n_threads=cores)
     dt = time.perf_counter() - t0
+    # one thread, on a sample of the heads, scaled to the whole layer
+    hs = 4
+    sl = lambda x: np.ascontiguousarray(x[:, :hs])
+    t0 = time.perf_counter()
+    oracle.recurrence(sl(q), sl(k), sl(v), sl(g), sl(beta), cu_seqlens=inp.cu_seqlens.numpy(),
+                      precision="f32", n_threads=1)
+    dt1 = (time.perf_counter() - t0) * inp.H / hs
     return {"value": inp.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"whole prefill workload (T={inp.T}, H={inp.H}, d={inp.d}), fp32 "
                       f"sequential recurrence, OpenMP over heads; {dt:.2f} s wall",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3),
+            "single_thread": {"value": inp.T / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{hs} of the {inp.H} heads, time scaled by "
+                                        f"{inp.H // hs}"}}
+
+
+def cpu_decode_single_thread(inp, n_sample=32):
+    """The oracle on one thread for a decode step of the batched decode workload
+    (each sequence one token from its initial state), on a sample of sequences,
+    scaled to the whole batch."""
+    import numpy as np
+    import oracle
+
+    rows = slice(0, n_sample)
+    f = lambda x: np.ascontiguousarray(x[rows].float().numpy())
+    t0 = time.perf_counter()
+    oracle.recurrence(f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta),
+                      cu_seqlens=np.arange(n_sample + 1, dtype=np.int32), S0=f(inp.S0),
+                      precision="f32", n_threads=1)
+    dt = (time.perf_counter() - t0) * inp.n_seqs / n_sample
+    return {"value": inp.n_seqs / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_sample} of the {inp.n_seqs} sequences, time scaled by "
+                      f"{inp.n_seqs // n_sample}"}
+
+
+def copy_bandwidth(dev, reps=10):
+    """A plain device copy of 1 GiB (torch's copy kernel), read plus written
+    bytes over the time: the bandwidth a streaming kernel reaches on this machine."""
+    import torch
+
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -239,6 +290,12 @@ def main():
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                             "traffic": measured_traffic(DECODE_KERNEL),
                             "algorithmic_bytes": alg}}
+        copy_gbs = copy_bandwidth(dev)
+        dec["copy_kernel"] = {"achieved": copy_gbs, "unit": "GB/s",
+                              "what": "device copy of 1 GiB, read + written bytes per second"}
+        dec["frac_of_copy"] = gbs / copy_gbs
+        if not args.no_cpu_baseline and args.only is None:
+            dec["cpu_single_thread"] = cpu_decode_single_thread(inp)
         if args.only == "decode":
             result.update({"value": B / (step_ms * 1e-3), "unit": "tokens/s",
                            "ms_per_step": step_ms})

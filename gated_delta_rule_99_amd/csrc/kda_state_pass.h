@@ -81,12 +81,13 @@ __device__ __forceinline__ void tile_export_kq(const ChunkLds& sm, __amdgpu_buff
 }
 
 // T and P fragments out of LDS (wave p exports row block p); after the merge
-// stage is visible.
+// stage is visible.  Both are lower triangular: the fragments of columns
+// 32..63 in row blocks 0 and 1 are zero and are neither stored nor read.
 __device__ __forceinline__ void tile_export_tp(const ChunkLds& sm, __amdgpu_buffer_rsrc_t rt,
                                                int p, int lane) {
     const int r = lane & 15, q4 = lane >> 4;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < (p >= 2 ? 2 : 1); ++kk) {
         const bf16x8 a = ld8(sm.T + (16 * p + r) * LDT + 32 * kk + 8 * q4);
         const bf16x8 b = ld8(sm.P + (16 * p + r) * LDT + 32 * kk + 8 * q4);
         __builtin_amdgcn_raw_buffer_store_b128(as_u4(a), rt, OFF_T + ((p * 2 + kk) * 64 + lane) * 16,
@@ -145,8 +146,8 @@ __device__ __forceinline__ void chain_load_b(ChainFrags& f, __amdgpu_buffer_rsrc
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
             f.Kb[a][kk] = ld_frag(rt, OFF_KBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) f.T[kk] = ld_frag(rt, OFF_T + ((cw * 2 + kk) * 64 + lane) * 16);
+    f.T[0] = ld_frag(rt, OFF_T + (cw * 2 * 64 + lane) * 16);
+    if (cw >= 2) f.T[1] = ld_frag(rt, OFF_T + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
 }
 __device__ __forceinline__ void out_load_a(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
                                            int lane) {
@@ -155,8 +156,8 @@ __device__ __forceinline__ void out_load_a(OutFrags& f, __amdgpu_buffer_rsrc_t r
 }
 __device__ __forceinline__ void out_load_b(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
                                            int lane) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) f.P[kk] = ld_frag(rt, OFF_P + ((cw * 2 + kk) * 64 + lane) * 16);
+    f.P[0] = ld_frag(rt, OFF_P + (cw * 2 * 64 + lane) * 16);
+    if (cw >= 2) f.P[1] = ld_frag(rt, OFF_P + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
 }
 
 // S[a][jb] holds S[32cw + 16a + 4q4 + e][16jb + r] of the slice.
