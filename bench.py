@@ -33,6 +33,7 @@ PREFILL_KERNEL = "prefill"
 PREFILL_KERNELS = "prep_kernel + state_kernel (kda_prefill_split.hip), all windows of one call"
 DECODE_KERNEL = "decode_kernel"
 DECODE_TOKENS_KERNEL = "decode_kernel_4tok"  # traffic record of the 4-token decode
+DECODE_BF16_KERNEL = "decode_kernel_bf16state"  # traffic record of the bf16-state decode
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc")
 SOURCES = {
@@ -41,6 +42,7 @@ SOURCES = {
                      os.path.join(_CSRC, "kda_state_pass.h")],
     DECODE_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
     DECODE_TOKENS_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
+    DECODE_BF16_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
 }
 
 
@@ -81,10 +83,10 @@ def prefill_algorithmic(T, H, d, chunk, with_s0, with_sfinal):
     return bytes_, flops
 
 
-def decode_algorithmic(B, H, d, n_tok=1):
-    """Per (sequence, head): state read + write once (2 * 4 d^2) and, per token,
-    q, k, v, g, beta, o."""
-    return B * H * (2 * 4 * d * d + n_tok * (3 * 2 * d + 4 * d + 4 + 2 * d))
+def decode_algorithmic(B, H, d, n_tok=1, state_bytes=4):
+    """Per (sequence, head): state read + write once (2 * state_bytes * d^2) and,
+    per token, q, k, v, g, beta, o."""
+    return B * H * (2 * state_bytes * d * d + n_tok * (3 * 2 * d + 4 * d + 4 + 2 * d))
 
 
 def cpu_baseline_run(inp):
@@ -168,7 +170,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_tokens", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_tokens", "decode_bf16_state",
+                                       "copy"],
                     default=None, help="run just one kernel (for profiler runs)")
     args = ap.parse_args()
 
@@ -300,6 +303,37 @@ def main():
             result.update({"value": B / (step_ms * 1e-3), "unit": "tokens/s",
                            "ms_per_step": step_ms})
         result["decode"] = dec
+        del q, k, v, g, beta, state, o, inp
+
+    if args.only == "decode_bf16_state" or (args.only is None and not args.no_decode):
+        # the same step on states stored in bf16 (half the state bytes)
+        inp = workloads.decode_batch()
+        q, k, v, g, beta = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+        state = inp.S0.to(dev).to(torch.bfloat16)
+        o = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.warmup):
+            kda.kda_decode_step(q, k, v, g, beta, state, o=o)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(nsteps):
+            kda.kda_decode_step(q, k, v, g, beta, state, o=o)
+        e1.record()
+        torch.cuda.synchronize()
+        b16_ms = e0.elapsed_time(e1) / nsteps
+        alg = decode_algorithmic(B, H, d, state_bytes=2)
+        gbs = alg / (b16_ms * 1e-3) / 1e9
+        result["decode_bf16_state"] = {
+            "workload": "batched decode step as above with the states stored in bf16 (fp32 "
+                        "arithmetic, rounded once per step when written)",
+            "ms_per_step": b16_ms, "tokens_per_s": B / (b16_ms * 1e-3),
+            "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (bf16 state)",
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(DECODE_BF16_KERNEL),
+                         "algorithmic_bytes": alg}}
+        if args.only == "decode_bf16_state":
+            result.update({"value": B / (b16_ms * 1e-3), "unit": "tokens/s",
+                           "ms_per_step": b16_ms})
         del q, k, v, g, beta, state, o, inp
 
     if args.only == "decode_tokens" or (args.only is None and not args.no_decode):

@@ -84,24 +84,33 @@ const char* kda_status_string(kda_status s) {
 
 const char* kda_last_error_detail(void) { return g_detail; }
 
-size_t kda_state_bytes(int H, int dk, int dv) {
+size_t kda_state_bytes(int H, int dk, int dv, kda_dtype state_dtype) {
     if (H <= 0 || dk <= 0 || dv <= 0) return 0;
-    return (size_t)4 * (size_t)H * (size_t)dk * (size_t)dv;
+    if (state_dtype != KDA_F32 && state_dtype != KDA_BF16) return 0;
+    return elem_size(state_dtype) * (size_t)H * (size_t)dk * (size_t)dv;
 }
 
-kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
-                          const float* src, hipStream_t stream) {
+kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, int H, int dk,
+                          int dv, const void* src, kda_dtype src_dtype, hipStream_t stream) {
+    const char* fn = "kda_state_init";
     g_detail[0] = 0;
-    if (kda_status s = check_heads("kda_state_init", H, dk, dv)) return s;
-    if (n_slots < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_state_init: n_slots < 0");
+    if (state_dtype != KDA_F32 && state_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown state dtype %d", fn, (int)state_dtype);
+    if (src && src_dtype != KDA_F32 && src_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown src dtype %d", fn, (int)src_dtype);
+    if (kda_status s = check_heads(fn, H, dk, dv)) return s;
+    if (n_slots < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots < 0", fn);
     if (n_slots == 0) return KDA_OK;
     if (!state || !aligned16(state) || (src && !aligned16(src)))
         return fail(KDA_ERR_INVALID_ARGUMENT,
-                    "kda_state_init: state/src must be non-NULL and 16-byte aligned");
-    const size_t bytes = (size_t)n_slots * kda_state_bytes(H, dk, dv);
-    if (src && overlaps(state, bytes, src, bytes))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_state_init: src overlaps state");
-    return hip_status(kda::launch_state_init(state, (int64_t)(bytes / 4), src, stream),
+                    "%s: state/src must be non-NULL and 16-byte aligned", fn);
+    const size_t bytes = (size_t)n_slots * kda_state_bytes(H, dk, dv, state_dtype);
+    const size_t src_bytes = src ? (size_t)n_slots * kda_state_bytes(H, dk, dv, src_dtype) : 0;
+    if (src && overlaps(state, bytes, src, src_bytes))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: src overlaps state", fn);
+    return hip_status(kda::launch_state_init(state, state_dtype,
+                                             (int64_t)n_slots * H * dk * dv, src, src_dtype,
+                                             stream),
                       "kda_state_init launch");
 }
 
@@ -133,7 +142,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     const size_t es = elem_size(dtype);
     const size_t n_qk = (size_t)T * H * d, n_bt = (size_t)T * H;
     const size_t n_g = gate == KDA_GATE_HEAD ? n_bt : n_qk;  // g elements
-    const size_t sbytes = (size_t)n_seqs * kda_state_bytes(H, dk, dv);
+    const size_t sbytes = (size_t)n_seqs * kda_state_bytes(H, dk, dv, KDA_F32);
     if (T > 0) {
         if (!q || !k || !v || !g || !beta || !o)
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: q, k, v, g, beta and o are required", fn);
@@ -168,7 +177,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: snap_capacity < 0", fn);
         if (!aligned16(snapshots))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned snapshots", fn);
-        const size_t snb = (size_t)n_seqs * snap_capacity * kda_state_bytes(H, dk, dv);
+        const size_t snb = (size_t)n_seqs * snap_capacity * kda_state_bytes(H, dk, dv, KDA_F32);
         if (overlaps(snapshots, snb, q, n_qk * es) || overlaps(snapshots, snb, k, n_qk * es) ||
             overlaps(snapshots, snb, v, n_qk * es) || overlaps(snapshots, snb, g, n_g * 4) ||
             overlaps(snapshots, snb, beta, n_bt * 4) || overlaps(snapshots, snb, o, n_qk * es) ||
@@ -225,13 +234,14 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
 // Shared by kda_decode_step (n_tok = 1, no snapshots) and kda_decode_tokens.
 static kda_status decode_common(const char* fn, const void* q, const void* k, const void* v,
                                 const float* g, const float* beta, kda_dtype dtype, kda_gate gate,
-                                float* state,
-                                int64_t n_slots, const int32_t* slot_idx, int B, int n_tok,
-                                int H, int dk, int dv, void* o, float* token_states,
-                                hipStream_t stream) {
+                                void* state, kda_dtype state_dtype, int64_t n_slots,
+                                const int32_t* slot_idx, int B, int n_tok, int H, int dk, int dv,
+                                void* o, void* token_states, hipStream_t stream) {
     g_detail[0] = 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+    if (state_dtype != KDA_F32 && state_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown state dtype %d", fn, (int)state_dtype);
     if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate layout %d", fn, (int)gate);
     if (kda_status s = check_heads(fn, H, dk, dv)) return s;
@@ -255,8 +265,8 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
     const size_t nv = (size_t)B * n_tok * H * dk, nb = (size_t)B * n_tok * H * 4;
     const size_t ng = gate == KDA_GATE_HEAD ? (size_t)B * n_tok * H : nv;  // g elements
-    const size_t sbytes = (size_t)n_slots * kda_state_bytes(H, dk, dv);
-    const size_t tbytes = (size_t)B * n_tok * kda_state_bytes(H, dk, dv);
+    const size_t sbytes = (size_t)n_slots * kda_state_bytes(H, dk, dv, state_dtype);
+    const size_t tbytes = (size_t)B * n_tok * kda_state_bytes(H, dk, dv, state_dtype);
     if (overlaps(o, nv * es, q, nv * es) || overlaps(o, nv * es, k, nv * es) ||
         overlaps(o, nv * es, v, nv * es) || overlaps(o, nv * es, g, ng * 4) ||
         overlaps(o, nv * es, state, sbytes) || overlaps(state, sbytes, q, nv * es) ||
@@ -270,25 +280,26 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
          overlaps(token_states, tbytes, beta, nb)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: token_states overlaps another argument", fn);
     return hip_status(kda::launch_decode(q, k, v, g, beta, dtype, gate == KDA_GATE_HEAD, state,
-                                         n_slots, slot_idx, B, n_tok, H, dk, token_states, o,
-                                         stream),
+                                         state_dtype, n_slots, slot_idx, B, n_tok, H, dk,
+                                         token_states, o, stream),
                       "decode launch");
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, kda_dtype dtype, kda_gate gate, float* state,
-                           int64_t n_slots, const int32_t* slot_idx, int B, int H, int dk, int dv,
-                           void* o, hipStream_t stream) {
-    return decode_common("kda_decode_step", q, k, v, g, beta, dtype, gate, state, n_slots,
-                         slot_idx, B, 1, H, dk, dv, o, nullptr, stream);
+                           const float* beta, kda_dtype dtype, kda_gate gate, void* state,
+                           kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
+                           int B, int H, int dk, int dv, void* o, hipStream_t stream) {
+    return decode_common("kda_decode_step", q, k, v, g, beta, dtype, gate, state, state_dtype,
+                         n_slots, slot_idx, B, 1, H, dk, dv, o, nullptr, stream);
 }
 
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, kda_dtype dtype, kda_gate gate, float* state,
-                             int64_t n_slots, const int32_t* slot_idx, int B, int n_tok, int H,
-                             int dk, int dv, void* o, float* token_states, hipStream_t stream) {
-    return decode_common("kda_decode_tokens", q, k, v, g, beta, dtype, gate, state, n_slots,
-                         slot_idx, B, n_tok, H, dk, dv, o, token_states, stream);
+                             const float* beta, kda_dtype dtype, kda_gate gate, void* state,
+                             kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
+                             int B, int n_tok, int H, int dk, int dv, void* o,
+                             void* token_states, hipStream_t stream) {
+    return decode_common("kda_decode_tokens", q, k, v, g, beta, dtype, gate, state, state_dtype,
+                         n_slots, slot_idx, B, n_tok, H, dk, dv, o, token_states, stream);
 }
 
 static kda_status check_conv_common(const char* fn, const float* w, kda_dtype dtype,

@@ -23,65 +23,162 @@
 // run, and streamed out once with 128-bit stores.  Both carry the non-temporal
 // hint: a state is touched once per step, and keeping it out of the caches was
 // measured at 5.68 TB/s against 5.10 TB/s without the hint (B=256, H=64).
+// A state may also be stored in bf16 (half the bytes; the page warns that
+// linear-attention state is sensitive to precision, page "Ling-3.1-flash and
+// the 7:1 hybrid: how much KV cache does a 560B model need at 1M tokens?",
+// section "How fast did the community react?"): it is widened to fp32 on load,
+// stepped in fp32 and rounded to nearest even once per call when stored.
 #include "kda_internal.h"
 
 namespace kda {
 
-// 128-bit state access with the non-temporal (streaming) hint.
-__device__ __forceinline__ float4 load_stream(const float* p) {
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ void store_stream(float* p, float4 r) {
-    const f32x4 v = {r.x, r.y, r.z, r.w};
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
-}
+// State access: VEC consecutive state elements of one row (4 or 8), with the
+// non-temporal (streaming) hint, widened to / narrowed from fp32.  fp32 states
+// move 4 elements in 16 bytes; bf16 states 4 elements in 8 bytes or 8 in 16,
+// rounded to nearest even when stored.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <typename TS>
+struct StateIO;
+template <>
+struct StateIO<float> {
+    template <int VEC>
+    static __device__ __forceinline__ void load(const float* p, float (&x)[VEC]) {
+        static_assert(VEC == 4, "fp32 states move 4 elements per access");
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+    }
+    template <int VEC>
+    static __device__ __forceinline__ void store(float* p, const float (&x)[VEC]) {
+        static_assert(VEC == 4, "fp32 states move 4 elements per access");
+        const f32x4 v = {x[0], x[1], x[2], x[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    }
+};
+template <>
+struct StateIO<bf16_t> {
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+    }
+    template <int VEC>
+    static __device__ __forceinline__ void load(const bf16_t* p, float (&x)[VEC]) {
+        if constexpr (VEC == 4) {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                x[2 * e] = bf16_bits_to_f32(v[e] & 0xffffu);
+                x[2 * e + 1] = bf16_bits_to_f32(v[e] >> 16);
+            }
+        } else {
+            static_assert(VEC == 8, "bf16 states move 4 or 8 elements per access");
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16_bits_to_f32(v[e] & 0xffffu);
+                x[2 * e + 1] = bf16_bits_to_f32(v[e] >> 16);
+            }
+        }
+    }
+    template <int VEC>
+    static __device__ __forceinline__ void store(bf16_t* p, const float (&x)[VEC]) {
+        if constexpr (VEC == 4) {
+            const u32x2 v = {pack(x[0], x[1]), pack(x[2], x[3])};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+        } else {
+            static_assert(VEC == 8, "bf16 states move 4 or 8 elements per access");
+            const u32x4 v = {pack(x[0], x[1]), pack(x[2], x[3]), pack(x[4], x[5]),
+                             pack(x[6], x[7])};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+        }
+    }
+};
 
 // ---------------------------------------------------------------- state init
 
-__global__ void __launch_bounds__(256) state_fill_kernel(float4* __restrict__ dst,
-                                                         const float4* __restrict__ src,
+// dst[i] = src[i] (converted between fp32 and bf16 as the types say) or zero.
+template <typename TD, typename TSRC>
+__global__ void __launch_bounds__(256) state_fill_kernel(TD* __restrict__ dst,
+                                                         const TSRC* __restrict__ src,
                                                          int64_t n4) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
-        dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (src) StateIO<TSRC>::load(src + 4 * i, x);
+        StateIO<TD>::store(dst + 4 * i, x);
+    }
 }
 
-hipError_t launch_state_init(float* state, int64_t n_floats, const float* src,
-                             hipStream_t stream) {
-    if (n_floats == 0) return hipSuccess;
-    const int64_t n4 = n_floats / 4;  // n_floats is a multiple of 16 (d >= 16)
+template <typename TD, typename TSRC>
+static hipError_t launch_fill_t(void* dst, const void* src, int64_t n4, hipStream_t stream) {
     int64_t blocks = (n4 + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(state_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<float4*>(state), reinterpret_cast<const float4*>(src),
-                       n4);
+    hipLaunchKernelGGL((state_fill_kernel<TD, TSRC>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<TD*>(dst), reinterpret_cast<const TSRC*>(src), n4);
     return hipGetLastError();
+}
+
+hipError_t launch_state_init(void* state, kda_dtype state_dtype, int64_t n_elems, const void* src,
+                             kda_dtype src_dtype, hipStream_t stream) {
+    if (n_elems == 0) return hipSuccess;
+    const int64_t n4 = n_elems / 4;  // n_elems is a multiple of 16 (d >= 16)
+    const bool db = state_dtype == KDA_BF16, sb = src_dtype == KDA_BF16;
+    if (db) return sb ? launch_fill_t<bf16_t, bf16_t>(state, src, n4, stream)
+                      : launch_fill_t<bf16_t, float>(state, src, n4, stream);
+    return sb ? launch_fill_t<float, bf16_t>(state, src, n4, stream)
+              : launch_fill_t<float, float>(state, src, n4, stream);
 }
 
 // ---------------------------------------------------------------- decode
 
-// Thread layout for one (sequence, head) state of D x D floats:
-//   CG = D/4 column groups (4 consecutive value columns, one float4 each),
+// Thread layout for one (sequence, head) state of D x D elements:
+//   CG = D/VEC column groups (VEC consecutive value columns per thread and row,
+//   one 16-byte access: VEC = 4 for fp32 states, 8 for bf16 states of D >= 64),
 //   RG row groups; thread (rg, cg) owns rows rg, rg+RG, rg+2RG, ... (RPT rows).
-// For D = 128: 256 threads, 16 rows each; the 64 lanes of a wave cover two
-// adjacent 512-byte rows per load instruction (1 KiB contiguous).
-template <int D>
+// For D = 128: 256 threads holding 64 state elements each; the 64 lanes of a
+// wave read 1 KiB of consecutive rows per load instruction.
+template <int D, int VEC>
 struct DecodeShape {
-    static constexpr int CG = D / 4;
-    static constexpr int RG = (D / 4) < 8 ? (D / 4) : 8;
+    static constexpr int CG = D / VEC;
+    static constexpr int RG = VEC == 4 ? (CG < 8 ? CG : 8) : (2 * CG < 16 ? 2 * CG : 16);
     static constexpr int NT = CG * RG;
     static constexpr int RPT = D / RG;
 };
+template <int D, typename TS>
+constexpr int decode_vec() { return sizeof(TS) == 2 && D >= 64 ? 8 : 4; }
 
-template <int D, typename Tin>
-__global__ void __launch_bounds__(DecodeShape<D>::NT)
+// VEC consecutive input elements (v) or outputs (o).
+template <typename Tin, int VEC>
+__device__ __forceinline__ void in_load(const Tin* p, float (&x)[VEC]) {
+#pragma unroll
+    for (int h = 0; h < VEC / 4; ++h) {
+        float y[4];
+        In<Tin>::load4(p + 4 * h, y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * h + e] = y[e];
+    }
+}
+template <typename Tin, int VEC>
+__device__ __forceinline__ void in_store(Tin* p, const float (&x)[VEC]) {
+#pragma unroll
+    for (int h = 0; h < VEC / 4; ++h) {
+        const float y[4] = {x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]};
+        In<Tin>::store4(p + 4 * h, y);
+    }
+}
+
+// TS: the stored state's type (fp32, or bf16 widened to fp32 while it is in
+// registers and rounded once when it is written back).  MULTI: n_tok may
+// exceed 1 (the token loop then also holds the partial-sum reads to fewer
+// registers, which was measured faster for several tokens and slower for one).
+template <int D, typename Tin, typename TS, bool MULTI>
+__global__ void __launch_bounds__((DecodeShape<D, decode_vec<D, TS>()>::NT))
 decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
-              int g_head, float* __restrict__ state, int64_t n_slots,
+              int g_head, TS* __restrict__ state, int64_t n_slots,
               const int32_t* __restrict__ slot_idx, int H, int n_tok,
-              float* __restrict__ token_states, Tin* __restrict__ o) {
-    using S = DecodeShape<D>;
+              TS* __restrict__ token_states, Tin* __restrict__ o) {
+    constexpr int VEC = decode_vec<D, TS>();
+    using S = DecodeShape<D, VEC>;
     constexpr int NT = S::NT, CG = S::CG, RG = S::RG, RPT = S::RPT;
     constexpr int NWAVE = (NT + 63) / 64;
 
@@ -91,7 +188,7 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
     __shared__ float s_k[D];    // k
     __shared__ float s_qk[NWAVE];
     __shared__ float s_qkp[D];  // q_i * k_i (only summed directly when NT < 64)
-    __shared__ float4 s_part[2][RG][CG];  // per-row-group partial column sums
+    __shared__ __attribute__((aligned(16))) float s_part[2][RG][D];  // per-row-group partial sums
 
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;           // b * H + h
@@ -108,16 +205,17 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
         return;
     }
 
-    float* st = state + ((size_t)slot * H + h) * (size_t)(D * D);
-    const int cg = tid % CG, rg = tid / CG;
+    TS* st = state + ((size_t)slot * H + h) * (size_t)(D * D);
+    const int cg = tid % CG, rg = tid / CG, c0 = VEC * cg;
 
-    // 1. stream the state in: RPT independent 128-bit loads per thread
-    float4 s[RPT];
+    // 1. stream the state in: RPT independent 16-byte loads per thread
+    float s[RPT][VEC];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) s[m] = load_stream(st + (size_t)(rg + RG * m) * D + 4 * cg);
+    for (int m = 0; m < RPT; ++m) StateIO<TS>::load(st + (size_t)(rg + RG * m) * D + c0, s[m]);
 
     // 2-5 once per token, the state staying in registers
-    for (int j = 0; j < n_tok; ++j) {
+    const int nt = MULTI ? n_tok : 1;
+    for (int j = 0; j < nt; ++j) {
         const int64_t row = token_row(j), vec = row * D;
         if (j > 0) __syncthreads();  // the previous token's reads of the LDS vectors are done
 
@@ -140,31 +238,50 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
             if ((tid & 63) == 0) s_qk[tid >> 6] = qk_part;
         }
         const float bt = beta[row];
-        float vj[4];
-        In<Tin>::load4(v + vec + 4 * cg, vj);
+        float vj[VEC];
+        in_load<Tin, VEC>(v + vec + c0, vj);
         __syncthreads();
 
         // 3. partial column sums over this thread's rows
-        float yk[4] = {0.f, 0.f, 0.f, 0.f}, yq[4] = {0.f, 0.f, 0.f, 0.f};
+        float yk[VEC], yq[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) yk[e] = yq[e] = 0.f;
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg + RG * m;
             const float ak = s_ak[i], aq = s_aq[i];
-            yk[0] += s[m].x * ak; yk[1] += s[m].y * ak; yk[2] += s[m].z * ak; yk[3] += s[m].w * ak;
-            yq[0] += s[m].x * aq; yq[1] += s[m].y * aq; yq[2] += s[m].z * aq; yq[3] += s[m].w * aq;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                yk[e] += s[m][e] * ak;
+                yq[e] += s[m][e] * aq;
+            }
         }
-        s_part[0][rg][cg] = make_float4(yk[0], yk[1], yk[2], yk[3]);
-        s_part[1][rg][cg] = make_float4(yq[0], yq[1], yq[2], yq[3]);
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            *reinterpret_cast<float4*>(&s_part[0][rg][c0 + e]) =
+                make_float4(yk[e], yk[e + 1], yk[e + 2], yk[e + 3]);
+            *reinterpret_cast<float4*>(&s_part[1][rg][c0 + e]) =
+                make_float4(yq[e], yq[e + 1], yq[e + 2], yq[e + 3]);
+        }
         __syncthreads();
 
         // 4. full column sums, write value and output
-        float4 Yk = s_part[0][0][cg], Yq = s_part[1][0][cg];
+        float Yk[VEC], Yq[VEC];
 #pragma unroll
-        for (int r = 1; r < RG; ++r) {
-            const float4 a = s_part[0][r][cg], c = s_part[1][r][cg];
-            Yk.x += a.x; Yk.y += a.y; Yk.z += a.z; Yk.w += a.w;
-            Yq.x += c.x; Yq.y += c.y; Yq.z += c.z; Yq.w += c.w;
+        for (int e = 0; e < VEC; ++e) {
+            Yk[e] = s_part[0][0][c0 + e];
+            Yq[e] = s_part[1][0][c0 + e];
         }
+        // the partial sums of the other row groups; a bounded unroll keeps the
+        // LDS reads in flight (registers) in check for 16 row groups
+        constexpr int RU = (VEC == 4 && !MULTI) ? RG : 4;
+#pragma unroll RU
+        for (int r = 1; r < RG; ++r)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                Yk[e] += s_part[0][r][c0 + e];
+                Yq[e] += s_part[1][r][c0 + e];
+            }
         float qk = 0.f;
         if constexpr (NT % 64 == 0) {
 #pragma unroll
@@ -173,61 +290,74 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
 #pragma unroll
             for (int i = 0; i < D; ++i) qk += s_qkp[i];
         }
-        float u[4];
-        u[0] = bt * (vj[0] - Yk.x);
-        u[1] = bt * (vj[1] - Yk.y);
-        u[2] = bt * (vj[2] - Yk.z);
-        u[3] = bt * (vj[3] - Yk.w);
+        float u[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) u[e] = bt * (vj[e] - Yk[e]);
         if (rg == 0) {
-            float ov[4] = {Yq.x + qk * u[0], Yq.y + qk * u[1], Yq.z + qk * u[2], Yq.w + qk * u[3]};
-            In<Tin>::store4(o + vec + 4 * cg, ov);
+            float ov[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) ov[e] = Yq[e] + qk * u[e];
+            in_store<Tin, VEC>(o + vec + c0, ov);
         }
 
         // 5. decay + rank-1 write, in registers; optionally a copy per token
-        float* snap = token_states ? token_states + (size_t)row * (D * D) : nullptr;
+        TS* snap = token_states ? token_states + (size_t)row * (D * D) : nullptr;
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg + RG * m;
             const float a = s_a[i], kk = s_k[i];
-            s[m].x = a * s[m].x + kk * u[0];
-            s[m].y = a * s[m].y + kk * u[1];
-            s[m].z = a * s[m].z + kk * u[2];
-            s[m].w = a * s[m].w + kk * u[3];
-            if (snap) store_stream(snap + (size_t)i * D + 4 * cg, s[m]);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s[m][e] = a * s[m][e] + kk * u[e];
+            if (snap) StateIO<TS>::store(snap + (size_t)i * D + c0, s[m]);
         }
     }
 
     // 6. stream the state out
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) store_stream(st + (size_t)(rg + RG * m) * D + 4 * cg, s[m]);
+    for (int m = 0; m < RPT; ++m) StateIO<TS>::store(st + (size_t)(rg + RG * m) * D + c0, s[m]);
 }
 
-template <int D, typename Tin>
+template <int D, typename Tin, typename TS>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, bool g_head, float* state, int64_t n_slots,
+                                  const float* beta, bool g_head, void* state, int64_t n_slots,
                                   const int32_t* slot_idx, int B, int n_tok, int H,
-                                  float* token_states, void* o, hipStream_t stream) {
+                                  void* token_states, void* o, hipStream_t stream) {
     const int64_t blocks = (int64_t)B * H;
     if (blocks == 0 || n_tok == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<D, Tin>), dim3((unsigned)blocks),
-                       dim3(DecodeShape<D>::NT), 0, stream, (const Tin*)q, (const Tin*)k,
-                       (const Tin*)v, g, beta, (int)g_head, state, n_slots, slot_idx, H, n_tok,
-                       token_states, (Tin*)o);
+    auto kern = n_tok > 1 ? decode_kernel<D, Tin, TS, true> : decode_kernel<D, Tin, TS, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(DecodeShape<D, decode_vec<D, TS>()>::NT),
+                       0, stream, (const Tin*)q, (const Tin*)k, (const Tin*)v, g, beta,
+                       (int)g_head, (TS*)state, n_slots, slot_idx, H, n_tok, (TS*)token_states,
+                       (Tin*)o);
     return hipGetLastError();
 }
 
+template <int D, typename Tin>
+static hipError_t launch_decode_s(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, bool g_head, void* state,
+                                  kda_dtype state_dtype, int64_t n_slots,
+                                  const int32_t* slot_idx, int B, int n_tok, int H,
+                                  void* token_states, void* o, hipStream_t stream) {
+    if (state_dtype == KDA_BF16)
+        return launch_decode_t<D, Tin, bf16_t>(q, k, v, g, beta, g_head, state, n_slots, slot_idx,
+                                               B, n_tok, H, token_states, o, stream);
+    return launch_decode_t<D, Tin, float>(q, k, v, g, beta, g_head, state, n_slots, slot_idx, B,
+                                          n_tok, H, token_states, o, stream);
+}
+
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, kda_dtype dtype, bool g_head, float* state,
-                         int64_t n_slots,
-                         const int32_t* slot_idx, int B, int n_tok, int H, int d,
-                         float* token_states, void* o, hipStream_t stream) {
-#define KDA_DEC(D)                                                                          \
-    if (d == D) {                                                                           \
-        if (dtype == KDA_BF16)                                                              \
-            return launch_decode_t<D, bf16_t>(q, k, v, g, beta, g_head, state, n_slots, slot_idx, \
-                                              B, n_tok, H, token_states, o, stream);        \
-        return launch_decode_t<D, float>(q, k, v, g, beta, g_head, state, n_slots, slot_idx, B, \
-                                         n_tok, H, token_states, o, stream);                 \
+                         const float* beta, kda_dtype dtype, bool g_head, void* state,
+                         kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx, int B,
+                         int n_tok, int H, int d, void* token_states, void* o,
+                         hipStream_t stream) {
+#define KDA_DEC(D)                                                                           \
+    if (d == D) {                                                                            \
+        if (dtype == KDA_BF16)                                                               \
+            return launch_decode_s<D, bf16_t>(q, k, v, g, beta, g_head, state, state_dtype,  \
+                                              n_slots, slot_idx, B, n_tok, H, token_states, o, \
+                                              stream);                                       \
+        return launch_decode_s<D, float>(q, k, v, g, beta, g_head, state, state_dtype, n_slots, \
+                                         slot_idx, B, n_tok, H, token_states, o, stream);    \
     }
     KDA_DEC(16)
     KDA_DEC(32)

@@ -102,16 +102,18 @@ __device__ __forceinline__ float* snapshot_at(const Snapshots& sn, int n, int h,
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already checked.
-hipError_t launch_state_init(float* state, int64_t n_floats, const float* src,
-                             hipStream_t stream);
+// n_elems elements of state_dtype: zeros (src NULL) or src converted.
+hipError_t launch_state_init(void* state, kda_dtype state_dtype, int64_t n_elems, const void* src,
+                             kda_dtype src_dtype, hipStream_t stream);
 
-// n_tok consecutive tokens per sequence; token_states may be NULL.
+// n_tok consecutive tokens per sequence; token_states may be NULL; state and
+// token_states hold state_dtype elements.
 // g_head: g holds one value per (token, head) instead of one per key channel.
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, kda_dtype dtype, bool g_head, float* state,
-                         int64_t n_slots,
-                         const int32_t* slot_idx, int B, int n_tok, int H, int d,
-                         float* token_states, void* o, hipStream_t stream);
+                         const float* beta, kda_dtype dtype, bool g_head, void* state,
+                         kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx, int B,
+                         int n_tok, int H, int d, void* token_states, void* o,
+                         hipStream_t stream);
 
 hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, kda_dtype dtype, bool g_head, const int32_t* cu,

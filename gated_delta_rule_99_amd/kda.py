@@ -36,16 +36,16 @@ _i32, _i64, _f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
 _SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [_i32]),
     "kda_last_error_detail": (ctypes.c_char_p, []),
-    "kda_state_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
-    "kda_state_init": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp]),
+    "kda_state_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
+    "kda_state_init": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _i32, _vp]),
     "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
                                    _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                                    ctypes.c_size_t, _vp]),
     "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i64, _vp, _i32, _i32,
-                               _i32, _i32, _vp, _vp]),
-    "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i64, _vp, _i32, _i32,
-                                 _i32, _i32, _i32, _vp, _vp, _vp]),
+    "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _i64, _vp, _i32,
+                               _i32, _i32, _i32, _vp, _vp]),
+    "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _i64, _vp, _i32,
+                                 _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "kda_short_conv_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp, _vp]),
     "kda_short_conv_decode": (_i32, [_vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _f32,
@@ -123,14 +123,26 @@ def _cu_pair(cu_seqlens, cu_seqlens_host, T, device):
     return host.to(device), host
 
 
-def kda_state_bytes(H: int, dk: int, dv: int) -> int:
-    return int(load().kda_state_bytes(H, dk, dv))
+def kda_state_bytes(H: int, dk: int, dv: int, state_dtype=torch.float32) -> int:
+    return int(load().kda_state_bytes(H, dk, dv, _STATE_DTYPES[state_dtype]))
+
+
+_STATE_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+def _state_code(t: torch.Tensor) -> int:
+    if t.dtype not in _STATE_DTYPES:
+        raise TypeError(f"state dtype {t.dtype}: expected float32 or bfloat16")
+    return _STATE_DTYPES[t.dtype]
 
 
 def kda_state_init(state: torch.Tensor, src: torch.Tensor | None = None, stream=None):
-    """Zero-fill (src None) or copy into state [n_slots, H, dk, dv] fp32."""
+    """Zero-fill (src None) or copy src into state [n_slots, H, dk, dv], each
+    fp32 or bf16 (converted; fp32 -> bf16 rounds to nearest even)."""
     n_slots, H, dk, dv = state.shape
-    _check(load().kda_state_init(_ptr(state), n_slots, H, dk, dv, _ptr(src), _stream(stream)))
+    _check(load().kda_state_init(_ptr(state), _state_code(state), n_slots, H, dk, dv, _ptr(src),
+                                 _state_code(src) if src is not None else KDA_F32,
+                                 _stream(stream)))
     return state
 
 
@@ -204,15 +216,15 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
 def kda_decode_step(q, k, v, g, beta, state, slot_idx=None, o=None, stream=None):
     """One token per sequence.  q, k: [B, H, dk]; g: [B, H, dk] or [B, H];
     v: [B, H, dv]; beta: [B, H];
-    state [n_slots, H, dk, dv] fp32 updated in place.  Returns o [B, H, dv]."""
+    state [n_slots, H, dk, dv] fp32 or bf16, updated in place.  Returns o [B, H, dv]."""
     B, H, dk = q.shape
     dv = v.shape[2]
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     _check(load().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
-        _ptr(state),
-        state.shape[0], _ptr(slot_idx), B, H, dk, dv, _ptr(o), _stream(stream)))
+        _ptr(state), _state_code(state), state.shape[0], _ptr(slot_idx), B, H, dk, dv, _ptr(o),
+        _stream(stream)))
     return o
 
 
@@ -220,19 +232,19 @@ def kda_decode_tokens(q, k, v, g, beta, state, slot_idx=None, o=None, token_stat
                       stream=None):
     """n_tok consecutive tokens per sequence.  q, k: [B, n_tok, H, dk]; g: the same
     shape or [B, n_tok, H]; v: [B, n_tok, H, dv]; beta: [B, n_tok, H]; state
-    [n_slots, H, dk, dv] fp32 updated in place.  token_states: None, True (allocate [B, n_tok, H, dk, dv])
-    or a tensor of that shape.  Returns (o [B, n_tok, H, dv], token_states)."""
+    [n_slots, H, dk, dv] fp32 or bf16, updated in place.  token_states: None,
+    True (allocate [B, n_tok, H, dk, dv] of the state's dtype) or such a tensor.
+    Returns (o [B, n_tok, H, dv], token_states)."""
     B, n_tok, H, dk = q.shape
     dv = v.shape[3]
     if o is None:
         o = torch.empty((B, n_tok, H, dv), dtype=q.dtype, device=q.device)
     if token_states is True:
-        token_states = torch.empty((B, n_tok, H, dk, dv), dtype=torch.float32, device=q.device)
+        token_states = torch.empty((B, n_tok, H, dk, dv), dtype=state.dtype, device=q.device)
     _check(load().kda_decode_tokens(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
-        _ptr(state),
-        state.shape[0], _ptr(slot_idx), B, n_tok, H, dk, dv, _ptr(o),
-        _ptr(token_states) if token_states is not None else None, _stream(stream)))
+        _ptr(state), _state_code(state), state.shape[0], _ptr(slot_idx), B, n_tok, H, dk, dv,
+        _ptr(o), _ptr(token_states) if token_states is not None else None, _stream(stream)))
     return o, token_states
 
 

@@ -79,19 +79,23 @@ const char* kda_status_string(kda_status s);
  * Valid until the next call into the library from that thread. */
 const char* kda_last_error_detail(void);
 
-/* Bytes of one sequence's state for one layer: 4 * H * d_k * d_v.
- * 4 194 304 for H = 64, d_k = d_v = 128; 0 for non-positive sizes. */
-size_t kda_state_bytes(int H, int dk, int dv);
+/* Bytes of one sequence's state for one layer: H * d_k * d_v elements of
+ * state_dtype (4 bytes for KDA_F32, 2 for KDA_BF16).  4 194 304 for H = 64,
+ * d_k = d_v = 128 in fp32; 0 for non-positive sizes or an unknown dtype. */
+size_t kda_state_bytes(int H, int dk, int dv, kda_dtype state_dtype);
 
 /*
  * kda_state_init -- set n_slots sequence states to zero (src == NULL) or to a
- * copy of src.  This is the state the recurrence starts from (S_0).
- *   state : [n_slots, H, dk, dv] fp32, written.
- *   src   : [n_slots, H, dk, dv] fp32 or NULL; must not overlap state.
- * Uses a fill/copy kernel (no memset node), so it may be captured in a graph.
+ * copy of src, converted to state_dtype.  This is the state the recurrence
+ * starts from (S_0); it also converts a prefill's fp32 final states into the
+ * bf16 states of the bf16-state decode, and back.
+ *   state     : [n_slots, H, dk, dv] state_dtype, written.
+ *   src       : [n_slots, H, dk, dv] src_dtype or NULL; must not overlap state.
+ * fp32 -> bf16 rounds to nearest even; bf16 -> fp32 is exact.  Uses a
+ * fill/copy kernel (no memset node), so it may be captured in a graph.
  */
-kda_status kda_state_init(float* state, int64_t n_slots, int H, int dk, int dv,
-                          const float* src, hipStream_t stream);
+kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, int H, int dk,
+                          int dv, const void* src, kda_dtype src_dtype, hipStream_t stream);
 
 /*
  * kda_prefill_chunked -- run the recurrence over n_seqs packed sequences,
@@ -175,7 +179,15 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
  *
  *   q, k     : [B, H, dk] dtype        v, o : [B, H, dv] dtype
  *   g        : [B, H, dk] fp32 ([B, H] with KDA_GATE_HEAD)    beta : [B, H] fp32
- *   state    : [n_slots, H, dk, dv] fp32, read and written in place.
+ *   state    : [n_slots, H, dk, dv] state_dtype, read and written in place.
+ *   state_dtype : KDA_F32, or KDA_BF16 for half the state bytes: the state is
+ *              widened to fp32 when read, stepped in fp32, and rounded to the
+ *              nearest bf16 (ties to even) once per call when written.  Page
+ *              "Ling-3.1-flash and the 7:1 hybrid: how much KV cache does a
+ *              560B model need at 1M tokens?" (section "How fast did the
+ *              community react?") warns that linear-attention state is
+ *              sensitive to precision; the rounding error accumulates over
+ *              steps.
  *   slot_idx : [B] int32 on the device giving each sequence's state slot, or
  *              NULL for slot b = b (then n_slots >= B).  Slots must be
  *              distinct.  A slot outside [0, n_slots) is not touched and that
@@ -184,10 +196,9 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
  * written once (fused form of one recurrence step).
  */
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, kda_dtype dtype, kda_gate gate, float* state,
-                           int64_t n_slots,
-                           const int32_t* slot_idx, int B, int H, int dk, int dv, void* o,
-                           hipStream_t stream);
+                           const float* beta, kda_dtype dtype, kda_gate gate, void* state,
+                           kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
+                           int B, int H, int dk, int dv, void* o, hipStream_t stream);
 
 /*
  * kda_decode_tokens -- advance B sequences by n_tok consecutive tokens each, in
@@ -205,10 +216,12 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
  *   q, k         : [B, n_tok, H, dk] dtype    v, o : [B, n_tok, H, dv] dtype
  *   g            : [B, n_tok, H, dk] fp32 ([B, n_tok, H] with KDA_GATE_HEAD)
  *   beta         : [B, n_tok, H] fp32
- *   state        : [n_slots, H, dk, dv] fp32, read and written in place; on
- *                  return it holds the state after the last token.
+ *   state        : [n_slots, H, dk, dv] state_dtype, read and written in
+ *                  place; on return it holds the state after the last token.
+ *   state_dtype  : as in kda_decode_step (a bf16 state is rounded once, after
+ *                  the last token).
  *   slot_idx     : as in kda_decode_step.
- *   token_states : [B, n_tok, H, dk, dv] fp32, or NULL.  When given, entry
+ *   token_states : [B, n_tok, H, dk, dv] state_dtype, or NULL.  When given, entry
  *                  [b, j] receives sequence b's state after token j, so that
  *                  a caller that accepts only the first m drafts can restore
  *                  the state after token m - 1 (kda_state_init copies it).
@@ -218,10 +231,10 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
  * that sequence to NaN.
  */
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, kda_dtype dtype, kda_gate gate, float* state,
-                             int64_t n_slots,
-                             const int32_t* slot_idx, int B, int n_tok, int H, int dk, int dv,
-                             void* o, float* token_states, hipStream_t stream);
+                             const float* beta, kda_dtype dtype, kda_gate gate, void* state,
+                             kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
+                             int B, int n_tok, int H, int dk, int dv, void* o,
+                             void* token_states, hipStream_t stream);
 
 /*
  * kda_short_conv_prefill -- width-4 causal depthwise convolution over packed

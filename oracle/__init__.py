@@ -14,6 +14,8 @@ Contents
 * ``brute_force``   -- a second, independent formulation in numpy fp64: the
   dense transition matrices M_t = (I - beta_t k_t k_t^T) Diag(alpha_t) multiplied
   out, for tiny inputs only.
+* ``round_bf16``    -- rounding to the nearest bfloat16 value (ties to even), the
+  storage rounding of a state kept in bf16 (numpy, integer arithmetic).
 
 Where each step comes from is stated in ``kda_oracle.c``'s header: page
 "Ling-3.1-flash: a 560B hybrid-attention MoE, counted from its safetensors
@@ -214,3 +216,23 @@ def brute_force(q, k, v, g, beta, S0=None):
             if t == T - 1:
                 S_T[h] = St
     return o, S_T
+
+
+def round_bf16(x):
+    """Round finite values in the normal binary32 range to the nearest bfloat16
+    value, ties to even; returns float64 (exact).
+
+    bfloat16 keeps a binary32 number's sign, its 8 exponent bits and the top 7 of
+    its 23 fraction bits, so a value keeps 8 significant bits.  In binary64 that
+    is the sign, the exponent and the top 7 of the 52 fraction bits: the low 45
+    bits are rounded away.  Adding 2^44 - 1 plus the lowest kept bit and then
+    clearing the 45 bits rounds to nearest with ties to even; a carry out of the
+    fraction moves into the exponent, which is the correct result there too.
+    """
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    bits = a.view(np.uint64)
+    drop = np.uint64(45)
+    keep_lsb = (bits >> drop) & np.uint64(1)
+    bias = (np.uint64(1) << np.uint64(44)) - np.uint64(1) + keep_lsb
+    out = ((bits + bias) >> drop) << drop
+    return out.view(np.float64).reshape(a.shape)

@@ -43,8 +43,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_state_bytes(lib):
-    assert lib.kda_state_bytes(64, 128, 128) == 4194304
-    assert lib.kda_state_bytes(0, 128, 128) == 0
+    assert lib.kda_state_bytes(64, 128, 128, KDA_F32) == 4194304
+    assert lib.kda_state_bytes(64, 128, 128, KDA_BF16) == 2097152
+    assert lib.kda_state_bytes(0, 128, 128, KDA_F32) == 0
+    assert lib.kda_state_bytes(64, 128, 128, 7) == 0
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
 
@@ -127,12 +129,12 @@ def test_prefill_nothing_to_do(lib):
 
 
 def decode(lib, **kw):
-    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_F32, gate=0, state=Fp, n_slots=4,
-             slot=None, B=4, H=2, dk=64, dv=64, o=Gp, stream=None)
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_F32, gate=0, state=Fp, sdt=KDA_F32,
+             n_slots=4, slot=None, B=4, H=2, dk=64, dv=64, o=Gp, stream=None)
     a.update(kw)
     return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"], a["gate"],
-                               a["state"], a["n_slots"], a["slot"], a["B"], a["H"], a["dk"],
-                               a["dv"], a["o"], a["stream"])
+                               a["state"], a["sdt"], a["n_slots"], a["slot"], a["B"], a["H"],
+                               a["dk"], a["dv"], a["o"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -145,6 +147,9 @@ def decode(lib, **kw):
     (dict(slot=Gp + 2, n_slots=8), KDA_ERR_INVALID_ARGUMENT, "misaligned"),
     (dict(o=A), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(state=Dp), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(sdt=3), KDA_ERR_INVALID_ARGUMENT, "state dtype"),
+    # a bf16 state is half the bytes: this one ends just below o, an fp32 one would not
+    (dict(state=Gp - 4 * 2 * 64 * 64 * 2, sdt=KDA_F32), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
 ])
 def test_decode_rejects(lib, kw, status, needle):
     assert decode(lib, **kw) == status
@@ -152,11 +157,12 @@ def test_decode_rejects(lib, kw, status, needle):
 
 
 def decode_tokens(lib, **kw):
-    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=1, state=Fp, n_slots=4,
-             slot=None, B=4, n_tok=3, H=2, dk=128, dv=128, o=Gp, snaps=None, stream=None)
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=1, state=Fp, sdt=KDA_BF16,
+             n_slots=4, slot=None, B=4, n_tok=3, H=2, dk=128, dv=128, o=Gp, snaps=None,
+             stream=None)
     a.update(kw)
     return lib.kda_decode_tokens(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
-                                 a["gate"], a["state"], a["n_slots"], a["slot"], a["B"],
+                                 a["gate"], a["state"], a["sdt"], a["n_slots"], a["slot"], a["B"],
                                  a["n_tok"], a["H"], a["dk"], a["dv"], a["o"], a["snaps"],
                                  a["stream"])
 
@@ -175,11 +181,16 @@ def test_decode_tokens_rejects(lib, kw, status, needle):
 
 
 def test_state_init_rejects(lib):
-    assert lib.kda_state_init(None, 2, 2, 64, 64, None, None) == KDA_ERR_INVALID_ARGUMENT
-    assert lib.kda_state_init(A, 2, 2, 64, 32, None, None) == KDA_ERR_UNSUPPORTED
-    assert lib.kda_state_init(A, -1, 2, 64, 64, None, None) == KDA_ERR_INVALID_ARGUMENT
-    assert lib.kda_state_init(A, 2, 2, 64, 64, A + 16, None) == KDA_ERR_INVALID_ARGUMENT
-    assert lib.kda_state_init(A, 0, 2, 64, 64, None, None) == 0
+    f = lib.kda_state_init
+    assert f(None, KDA_F32, 2, 2, 64, 64, None, KDA_F32, None) == KDA_ERR_INVALID_ARGUMENT
+    assert f(A, KDA_F32, 2, 2, 64, 32, None, KDA_F32, None) == KDA_ERR_UNSUPPORTED
+    assert f(A, KDA_F32, -1, 2, 64, 64, None, KDA_F32, None) == KDA_ERR_INVALID_ARGUMENT
+    assert f(A, KDA_F32, 2, 2, 64, 64, A + 16, KDA_F32, None) == KDA_ERR_INVALID_ARGUMENT
+    assert f(A, 5, 2, 2, 64, 64, None, KDA_F32, None) == KDA_ERR_INVALID_ARGUMENT
+    assert f(A, KDA_BF16, 2, 2, 64, 64, Bp, 5, None) == KDA_ERR_INVALID_ARGUMENT
+    # 2 fp32 states of 2 x 64 x 64 end 64 KiB after A; a bf16 source there overlaps
+    assert f(A, KDA_F32, 2, 2, 64, 64, A + 65536 - 16, KDA_BF16, None) == KDA_ERR_INVALID_ARGUMENT
+    assert f(A, KDA_F32, 0, 2, 64, 64, None, KDA_F32, None) == 0
 
 
 def conv(lib, **kw):

@@ -38,3 +38,33 @@ def test_state_size_matches_pages(orc):
     assert round(total / 1e6, 1) == gold["state_MB_printed"]
     assert total / 2 ** 20 == gold["state_MiB_printed"]
     assert H * d == gold["qkv_width"]
+
+
+# ---- bfloat16 storage rounding (the bf16-state decode's write-back)
+# (value, its nearest bfloat16 with ties to even): bfloat16 keeps 8 significant
+# bits, so just above 1 its spacing is 2^-7 and in [128, 256) it is 1.
+BF16_CASES = [
+    (1.0 + 2.0 ** -8, 1.0),                        # tie: down to the even neighbour
+    (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),        # tie: up to the even neighbour
+    (1.0 + 2.0 ** -8 + 2.0 ** -30, 1.0 + 2.0 ** -7),  # just above a tie: up
+    (1.0 + 2.0 ** -8 - 2.0 ** -30, 1.0),           # just below a tie: down
+    (-(1.0 + 3 * 2.0 ** -8), -(1.0 + 2.0 ** -6)),  # sign kept
+    (255.5, 256.0),                                # tie carried into the exponent
+    (0.15625, 0.15625),                            # representable: unchanged
+    (0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("x,want", BF16_CASES)
+def test_round_bf16_cases(x, want):
+    assert oracle.round_bf16(np.array([x]))[0] == want
+
+
+def test_round_bf16_matches_torch_on_binary32():
+    """On binary32 inputs the rounding equals torch's float32 -> bfloat16
+    conversion, an independent implementation, bit for bit."""
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(7).standard_normal(200_000).astype(np.float32)
+    x[::3] *= 1e-3
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)

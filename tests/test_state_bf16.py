@@ -1,0 +1,155 @@
+"""GPU tests of states stored in bfloat16 (half the bytes of the fp32 state; page
+"Ling-3.1-flash and the 7:1 hybrid: how much KV cache does a 560B model need at
+1M tokens?", section "How fast did the community react?", warns that linear-
+attention state is sensitive to precision) through the C ABI.
+
+A bf16 state is widened to fp32 when read, stepped in fp32, and rounded to the
+nearest bfloat16 (ties to even) when written back.  The oracle for one call is
+therefore the fp64 recurrence from the stored bf16 values followed by
+oracle.round_bf16 of the final state."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from kda_testutil import TOL_BF16, dev, gpu_or_skip, np64, oracle_on, per_seq_errors, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+
+def kda():
+    gpu_or_skip()
+    import gated_delta_rule_99_amd as m
+    m.load()
+    return m
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 values at |x| (8 significant bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 1e-30)))
+    return 2.0 ** (e - 7)
+
+
+# Where the update nearly cancels (a state of 0.3 stepping to 1e-5), the fp32
+# step's own rounding, about 2^-24 of the terms, exceeds one bf16 spacing of the
+# result: each element may differ by one bf16 spacing plus this.
+FP32_SLACK = 1e-6
+
+
+def within_rounding(got, want):
+    return np.all(np.abs(got - want) <= bf16_ulp(want) * (1 + 1e-9) + FP32_SLACK)
+
+
+def test_state_init_converts():
+    """fp32 -> bf16 rounds to nearest even (equal to the oracle's rounding, bit
+    for bit); bf16 -> fp32 is exact; zero fill of a bf16 state."""
+    m = kda()
+    src = torch.randn((3, 2, 64, 64), generator=torch.Generator().manual_seed(3)) * 0.3
+    half = torch.empty((3, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    m.kda_state_init(half, dev(src))
+    back = torch.empty((3, 2, 64, 64), dtype=torch.float32, device="cuda")
+    m.kda_state_init(back, half)
+    torch.cuda.synchronize()
+    want = oracle.round_bf16(src.double().numpy())
+    assert np.array_equal(half.float().cpu().double().numpy(), want)
+    assert np.array_equal(back.cpu().double().numpy(), want)
+    m.kda_state_init(half)
+    torch.cuda.synchronize()
+    assert not half.float().abs().sum().item()
+
+
+@pytest.mark.parametrize("n_tok", [1, 4])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_bf16_state_matches_rounded_oracle(d, n_tok):
+    """One call of n_tok tokens on bf16 states, through a slot permutation: the
+    outputs match the oracle run from the stored values, and every written
+    state element is the oracle's final state rounded to bf16 (all within one
+    bf16 spacing, nearly all equal: fp32 and fp64 round apart only next to a
+    tie, or where the step nearly cancels); other slots are untouched."""
+    m = kda()
+    B, H, n_slots = 5, 3, 8
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", s0_std=0.3,
+                                      seed=400 + d + n_tok)
+    S0 = torch.from_numpy(oracle.round_bf16(inp.S0.double().numpy())).float()
+    pool = torch.zeros((n_slots, H, d, d))
+    slots = torch.tensor([6, 1, 3, 0, 7], dtype=torch.int32)
+    pool[slots.long()] = S0
+    state = dev(pool.to(torch.bfloat16))
+    t = lambda x: dev(x.reshape((B, n_tok) + tuple(x.shape[1:])))
+    o, _ = m.kda_decode_tokens(t(inp.q), t(inp.k), t(inp.v), t(inp.g), t(inp.beta), state,
+                               slot_idx=dev(slots))
+    torch.cuda.synchronize()
+    ref = workloads.RecurrenceInputs(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, S0,
+                                     "bf16", inp.chunk)
+    o_ref, S_ref = oracle_on(ref)
+    S_gpu = state.float().cpu().double().numpy()[slots.long().numpy()]
+    S_want = oracle.round_bf16(S_ref)
+    eo, _ = per_seq_errors(np64(o).reshape(B * n_tok, H, d), o_ref, None, None, inp.cu_seqlens)
+    diff = np.abs(S_gpu - S_want)
+    exact = float(np.mean(diff == 0))
+    print(f"bf16 state d={d} n_tok={n_tok}: o {eo:.2e}, state elements equal {exact:.5f}")
+    assert eo <= TOL_BF16
+    assert within_rounding(S_gpu, S_want)
+    assert exact >= 0.999
+    untouched = [s for s in range(n_slots) if s not in slots.tolist()]
+    assert not state[untouched].float().abs().sum().item()
+
+
+def test_bf16_state_error_over_many_steps():
+    """The precision cost, measured: 64 single-token steps on a bf16 state and on
+    an fp32 state, both against the fp64 recurrence over the same 64 tokens.
+    The fp32 state tracks it to ~1e-6; the bf16 state's per-step rounding
+    accumulates to ~1e-3 relative, still inside the bf16 budget at the configs'
+    decay rates (alpha ~ 0.88 forgets old rounding errors)."""
+    m = kda()
+    B, H, d, n = 16, 4, 128, 64
+    inp = workloads.recurrence_inputs([n] * B, H=H, d=d, dtype="bf16", g_mu=2.0, g_sigma=0.5,
+                                      s0_std=0.02, seed=411)
+    S0 = torch.from_numpy(oracle.round_bf16(inp.S0.double().numpy())).float()
+    o_ref, S_ref = oracle_on(workloads.RecurrenceInputs(inp.q, inp.k, inp.v, inp.g, inp.beta,
+                                                        inp.cu_seqlens, S0, "bf16", inp.chunk))
+    res = {}
+    for name, dt in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
+        state = dev(S0.to(dt))
+        outs = []
+        for j in range(n):
+            rows = torch.arange(B) * n + j
+            outs.append(m.kda_decode_step(dev(inp.q[rows]), dev(inp.k[rows]), dev(inp.v[rows]),
+                                          dev(inp.g[rows]), dev(inp.beta[rows]), state))
+        torch.cuda.synchronize()
+        o = torch.stack(outs, dim=1).reshape(B * n, H, d)
+        eo, es = per_seq_errors(np64(o), o_ref, state.float().cpu().double().numpy(), S_ref,
+                                inp.cu_seqlens)
+        res[name] = (eo, es)
+        print(f"{name} state, {n} steps: o {eo:.2e}  final state {es:.2e}")
+    assert res["fp32"][1] <= 1e-4
+    assert res["bf16"][1] <= TOL_BF16 and res["bf16"][0] <= TOL_BF16
+    assert res["bf16"][1] > 10 * res["fp32"][1]
+
+
+def test_decode_bf16_token_states():
+    """token_states of a bf16-state call are bf16: entry [b, j] is the state
+    after token j rounded once, and the last entry equals the written state."""
+    m = kda()
+    B, n_tok, H, d = 3, 4, 2, 128
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", s0_std=0.3, seed=412)
+    S0 = torch.from_numpy(oracle.round_bf16(inp.S0.double().numpy())).float()
+    state = dev(S0.to(torch.bfloat16))
+    t = lambda x: dev(x.reshape((B, n_tok) + tuple(x.shape[1:])))
+    _, snaps = m.kda_decode_tokens(t(inp.q), t(inp.k), t(inp.v), t(inp.g), t(inp.beta), state,
+                                   token_states=True)
+    torch.cuda.synchronize()
+    assert snaps.dtype == torch.bfloat16
+    assert torch.equal(snaps[:, -1], state)
+    for j in range(n_tok):
+        rows = torch.tensor([b * n_tok + i for b in range(B) for i in range(j + 1)])
+        pre = workloads.RecurrenceInputs(inp.q[rows], inp.k[rows], inp.v[rows], inp.g[rows],
+                                         inp.beta[rows],
+                                         torch.arange(0, B * (j + 1) + 1, j + 1,
+                                                      dtype=torch.int32), S0, "bf16", inp.chunk)
+        _, S_ref = oracle_on(pre)
+        want = oracle.round_bf16(S_ref)
+        got = snaps[:, j].float().cpu().double().numpy()
+        assert within_rounding(got, want)
+        assert max(rel_fro(got[b], S_ref[b]) for b in range(B)) <= TOL_BF16
