@@ -68,3 +68,15 @@ def test_round_bf16_matches_torch_on_binary32():
     x[::3] *= 1e-3
     ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
     assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_conv_tail_size_matches_pages():
+    """A conv tail as the library keeps it, [3, channels] bf16 per sequence and
+    layer for the q, k, v streams (3 x 8192 channels), over 63 KDA layers, is
+    the pages' ~9 MB per sequence."""
+    gold = json.load(open(os.path.join(HERE, "golden", "state_sizes.json")))
+    assert gold["conv_channels"] == 3 * gold["qkv_width"]
+    per_layer = gold["conv_history_tokens"] * gold["conv_channels"] * \
+        gold["conv_tail_bytes_per_element"]
+    total = per_layer * gold["kda_layers"]
+    assert round(total / 1e6) == gold["conv_tail_MB_printed"]
