@@ -14,7 +14,8 @@
 //   waves 4-7  chain: Y = Kt G, R, U = T R, S <- G + Kb^T U, next G, and
 //   waves 8-11 output: Z = Qt G, O = Z + P U
 // run chunk c from register copies of its fragments, taken from LDS at the end
-// of the previous step.
+// of the previous step.  The chain and output steps are the state pass's own
+// (kda_state_pass.h); only where their fragments come from differs.
 //
 //   step s:  [A] producer decay(s+1) | chain Y, R      | output Z
 //            B1
@@ -24,25 +25,18 @@
 //            B3
 //            [D]                     | chain copy-in(s+1) | output copy-in(s+1)
 //            B0
-#include "kda_chunk_ops.h"
+#include "kda_state_pass.h"
 
 namespace kda {
 namespace fu {
 
 using namespace co;
 
-constexpr int DVS = 32, NS = D / DVS;
-constexpr int LDX = 40;  // row stride (bf16) of the V and O staging tiles
-
 struct FusedLds {
     ChunkLds ck;              // operand stages of the next chunk
     uint16_t KbT[D * LDT];    // Kb^T [i][t] of the next chunk
     float gam[D];             // Gam of the next chunk
-    uint16_t Gt[DVS * LDK];   // bf16 (Gam * S)^T [j][i]
-    uint16_t Rt[DVS * LDT];   // R^T [j][t]
-    uint16_t Ut[DVS * LDT];   // U^T [j][t]
-    uint16_t V[C * LDX];      // V slice [t][j]: each chain wave stages its own 16 rows
-    uint16_t O[C * LDX];      // O slice [t][j]: each output wave stages its own 16 rows
+    StateLds st;              // state pass (kda_state_pass.h)
 };
 
 }  // namespace fu
@@ -139,7 +133,7 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     } else if (wave < 8) {
         // ============================================================ chain
         const int cw = w4;
-        f32x4 S[2][2];  // S[32cw + 16a + 4q4 + e][16jb + r]
+        StateFrag S;
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -153,30 +147,31 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vo_rsrc(v, c), xoff, 0, 0);
             return make_uint4(x[0], x[1], x[2], x[3]);
         };
-        uint4 vcur = load_v(0), vnext = load_v(1);
-        bf16x8 K[4], Kb[2][2], Tf[2];
-        float4 bet;
+        uint4 vnext = load_v(1);
+        ChainFrags cur;  // chunk s's fragments, copied from the producer's LDS
+        cur.v = load_v(0);
+        auto gam_lds = [&](float4 (&gm)[2]) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+                gm[a] = *reinterpret_cast<const float4*>(sm.gam + 32 * cw + 16 * a + 4 * q4);
+        };
         auto copy_in = [&]() {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) K[kk] = ld8(sm.ck.Kt + (16 * cw + r) * LDK + 32 * kk + 8 * q4);
+            for (int kk = 0; kk < 4; ++kk) cur.K[kk] = ld8(sm.ck.Kt + (16 * cw + r) * LDK + 32 * kk + 8 * q4);
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    Kb[a][kk] = ld8(sm.KbT + (32 * cw + 16 * a + r) * LDT + 32 * kk + 8 * q4);
+                    cur.Kb[a][kk] = ld8(sm.KbT + (32 * cw + 16 * a + r) * LDT + 32 * kk + 8 * q4);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) Tf[kk] = ld8(sm.ck.T + (16 * cw + r) * LDT + 32 * kk + 8 * q4);
-            bet = *reinterpret_cast<const float4*>(sm.ck.beta + 16 * cw + 4 * q4);
+            for (int kk = 0; kk < 2; ++kk) cur.T[kk] = ld8(sm.ck.T + (16 * cw + r) * LDT + 32 * kk + 8 * q4);
+            cur.bet = *reinterpret_cast<const float4*>(sm.ck.beta + 16 * cw + 4 * q4);
         };
         __syncthreads();  // P1: Gam of chunk 0 is in LDS
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            const float4 gm = *reinterpret_cast<const float4*>(sm.gam + 32 * cw + 16 * a + 4 * q4);
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                S[a][jb][0] *= gm.x; S[a][jb][1] *= gm.y; S[a][jb][2] *= gm.z; S[a][jb][3] *= gm.w;
-                st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, S[a][jb]);
-            }
+        {
+            float4 gm[2];
+            gam_lds(gm);
+            chain_scale_store(sm.st, S, gm, cw, lane);
         }
         __syncthreads();  // P2
         __syncthreads();  // P3
@@ -185,59 +180,20 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int s = 0; s < nc; ++s) {
             const bool next = s + 1 < nc;
             // ---- [A] Y = Kt G; R = diag(beta)(V - Y)
-            *reinterpret_cast<uint4*>(sm.V + xrow * LDX + xcol) = vcur;
-            __builtin_amdgcn_wave_barrier();
-            f32x4 Y[2] = {Z4, Z4};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                Y[0] = mma32(K[kk], ld8(sm.Gt + r * LDK + 32 * kk + 8 * q4), Y[0]);
-                Y[1] = mma32(K[kk], ld8(sm.Gt + (16 + r) * LDK + 32 * kk + 8 * q4), Y[1]);
-            }
-            const float bb[4] = {bet.x, bet.y, bet.z, bet.w};
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                f32x4 rv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    rv[e] = bb[e] * (bf16_bits_to_f32(sm.V[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r]) -
-                                     Y[jb][e]);
-                st4(sm.Rt + (16 * jb + r) * LDT + 16 * cw + 4 * q4, rv);
-            }
-            vcur = vnext;
+            chain_stage_v(sm.st, cur.v, xrow, xcol);
+            chain_yr(sm.st, cur, cw, lane);
+            cur.v = vnext;
             vnext = load_v(s + 2);
             __syncthreads();  // B1
             // ---- [B] U = T R
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                f32x4 u = mma32(Tf[0], ld8(sm.Rt + (16 * jb + r) * LDT + 8 * q4), Z4);
-                if (cw >= 2) u = mma32(Tf[1], ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4), u);
-                st4(sm.Ut + (16 * jb + r) * LDT + 16 * cw + 4 * q4, u);
-            }
+            chain_u(sm.st, cur, cw, lane);
             __syncthreads();  // B2
             // ---- [C] S <- G + Kb^T U (a snapshot when one falls here); next G = Gam(s+1) * S
-            float* snp = snapshot_at(snap, n, h, H, D, (int64_t)(s + 1) * C, te - tb);
-            float4 gm[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-                gm[a] = *reinterpret_cast<const float4*>(sm.gam + 32 * cw + 16 * a + 4 * q4);
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                const bf16x8 u0 = ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4);
-                const bf16x8 u1 = ld8(sm.Ut + (16 * jb + r) * LDT + 32 + 8 * q4);
-#pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    f32x4 st = mma32(Kb[a][1], u1, mma32(Kb[a][0], u0, S[a][jb]));
-                    if (snp) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            snp[(size_t)(32 * cw + 16 * a + 4 * q4 + e) * D + j0 + 16 * jb + r] = st[e];
-                    }
-                    if (next) {
-                        st[0] *= gm[a].x; st[1] *= gm[a].y; st[2] *= gm[a].z; st[3] *= gm[a].w;
-                        st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, st);
-                    }
-                    S[a][jb] = st;
-                }
+            {
+                float4 gm[2];
+                gam_lds(gm);
+                chain_s(sm.st, cur, gm, next, S,
+                        snapshot_at(snap, n, h, H, D, (int64_t)(s + 1) * C, te - tb), j0, cw, lane);
             }
             __syncthreads();  // B3
             // ---- [D] fragments of chunk s + 1
@@ -258,12 +214,12 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     } else {
         // ============================================================ output
         const int cw = w4;
-        bf16x8 Qf[4], Pf[2];
+        OutFrags cur;  // chunk s's fragments, copied from the producer's LDS
         auto copy_in = [&]() {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) Qf[kk] = ld8(sm.ck.Qt + (16 * cw + r) * LDK + 32 * kk + 8 * q4);
+            for (int kk = 0; kk < 4; ++kk) cur.Q[kk] = ld8(sm.ck.Qt + (16 * cw + r) * LDK + 32 * kk + 8 * q4);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) Pf[kk] = ld8(sm.ck.P + (16 * cw + r) * LDT + 32 * kk + 8 * q4);
+            for (int kk = 0; kk < 2; ++kk) cur.P[kk] = ld8(sm.ck.P + (16 * cw + r) * LDT + 32 * kk + 8 * q4);
         };
         __syncthreads();  // P1
         __syncthreads();  // P2
@@ -273,26 +229,13 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int s = 0; s < nc; ++s) {
             const bool next = s + 1 < nc;
             // ---- [A] Z = Qt G
-            f32x4 Zc[2] = {Z4, Z4};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                Zc[0] = mma32(Qf[kk], ld8(sm.Gt + r * LDK + 32 * kk + 8 * q4), Zc[0]);
-                Zc[1] = mma32(Qf[kk], ld8(sm.Gt + (16 + r) * LDK + 32 * kk + 8 * q4), Zc[1]);
-            }
+            f32x4 Zc[2];
+            out_z(sm.st, cur, Zc, lane);
             __syncthreads();  // B1
             __syncthreads();  // B2
             // ---- [C] O = Z + P U, staged through this wave's rows, one 16-byte store
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                f32x4 acc = mma32(Pf[0], ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
-                if (cw >= 2) acc = mma32(Pf[1], ld8(sm.Ut + (16 * jb + r) * LDT + 32 + 8 * q4), acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[e]);
-            }
-            __builtin_amdgcn_wave_barrier();
-            const uint4 x = *reinterpret_cast<const uint4*>(sm.O + xrow * LDX + xcol);
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, vo_rsrc(o, s), xoff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(out_o(sm.st, cur, Zc, cw, lane, xrow, xcol),
+                                                   vo_rsrc(o, s), xoff, 0, 0);
             __syncthreads();  // B3
             // ---- [D] fragments of chunk s + 1
             if (next) copy_in();

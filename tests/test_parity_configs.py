@@ -60,6 +60,30 @@ def test_config_decode_batch():
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
+def test_config_decode_batch_bf16_state():
+    """The same step on states stored in bf16: outputs against the oracle run from
+    the stored values, every written state against the oracle's final state
+    rounded to bf16 (one bf16 spacing, plus fp32 slack where a step cancels)."""
+    m = kda()
+    inp = workloads.decode_batch()
+    S0 = torch.from_numpy(oracle.round_bf16(inp.S0.double().numpy())).float()
+    state = dev(S0.to(torch.bfloat16))
+    o = m.kda_decode_step(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), state)
+    torch.cuda.synchronize()
+    ref = workloads.RecurrenceInputs(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, S0,
+                                     "bf16", inp.chunk)
+    o_ref, S_ref = oracle_on(ref)
+    want = oracle.round_bf16(S_ref)
+    got = state.float().cpu().double().numpy()
+    spacing = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
+    eo, es = per_seq_errors(np64(o), o_ref, got, S_ref, inp.cu_seqlens)
+    exact = float(np.mean(got == want))
+    print(f"decode batch, bf16 state: o {eo:.2e} S {es:.2e}, state elements equal {exact:.5f}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert np.all(np.abs(got - want) <= spacing * (1 + 1e-9) + 1e-6)
+    assert exact >= 0.999
+
+
 PACKED_HEADS = (0, 21, 42, 63)
 
 
