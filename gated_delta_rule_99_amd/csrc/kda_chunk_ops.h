@@ -144,33 +144,23 @@ __device__ __forceinline__ void load_chunk(ChunkIn& in, const bf16_t* q, const b
 // Kt, Qt, Kb (rows into LDS) and beta into LDS.  Hands Gam[ch0 + e] (lanes with
 // tg == 0) to gam_sink(ch0, gam4) and, for every lane, the Kb^T piece of channel
 // ch0 + e, tokens [8tg, 8tg + 8) as 8 packed bf16 to kbt_sink(i, tg, u32x4).
-// It runs as pieces, decay_scan, decay_rows_kq (together decay_kq) and
-// decay_kb, which a caller may place in different segments of its schedule
-// (the carry holds what the later pieces need).
-struct DecayCarry {
-    float al[8][4];  // alpha of this lane's 8 tokens and 4 channels
-    float dsc[4];    // running product of alpha up to the token being scaled, / Gam
-    float fsc[4];    // running product of alpha over the later token groups
-};
-
-// First half, part 1: alpha, the products across the token groups, beta, Gam.
-template <typename GamSink>
-__device__ __forceinline__ void decay_scan(ChunkLds& sm, const ChunkIn& in, int p, int lane,
-                                           GamSink gam_sink, DecayCarry& dc) {
+template <typename GamSink, typename KbtSink>
+__device__ __forceinline__ void decay_stage(ChunkLds& sm, const ChunkIn& in, int p, int lane,
+                                            GamSink gam_sink, KbtSink kbt_sink) {
     const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
     if (p == 0) sm.beta[lane] = in.beta;
-    float tot[4] = {1.f, 1.f, 1.f, 1.f};
+    float al[8][4], tot[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
-        dc.al[rr][0] = __builtin_amdgcn_exp2f(in.g[rr].x * LOG2E);
-        dc.al[rr][1] = __builtin_amdgcn_exp2f(in.g[rr].y * LOG2E);
-        dc.al[rr][2] = __builtin_amdgcn_exp2f(in.g[rr].z * LOG2E);
-        dc.al[rr][3] = __builtin_amdgcn_exp2f(in.g[rr].w * LOG2E);
+        al[rr][0] = __builtin_amdgcn_exp2f(in.g[rr].x * LOG2E);
+        al[rr][1] = __builtin_amdgcn_exp2f(in.g[rr].y * LOG2E);
+        al[rr][2] = __builtin_amdgcn_exp2f(in.g[rr].z * LOG2E);
+        al[rr][3] = __builtin_amdgcn_exp2f(in.g[rr].w * LOG2E);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tot[e] *= dc.al[rr][e];
+        for (int e = 0; e < 4; ++e) tot[e] *= al[rr][e];
     }
     // products across the 8 token groups of a channel group (lanes 8 apart)
-    float gam[4];
+    float dsc[4], fsc[4], gam[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         float xp = tot[e], xs = tot[e];
@@ -184,17 +174,10 @@ __device__ __forceinline__ void decay_scan(ChunkLds& sm, const ChunkIn& in, int 
         const float epre = __shfl_up(xp, 8);
         const float esuf = __shfl_down(xs, 8);
         gam[e] = __shfl(xp, 56 + cg);
-        dc.dsc[e] = (tg > 0 ? epre : 1.f) * __builtin_amdgcn_rcpf(gam[e]);
-        dc.fsc[e] = tg < 7 ? esuf : 1.f;
+        dsc[e] = (tg > 0 ? epre : 1.f) * __builtin_amdgcn_rcpf(gam[e]);
+        fsc[e] = tg < 7 ? esuf : 1.f;
     }
     if (tg == 0) gam_sink(ch0, gam);
-}
-
-// First half, part 2: Kt and Qt rows.
-__device__ __forceinline__ void decay_rows_kq(ChunkLds& sm, const ChunkIn& in, int p, int lane,
-                                              const DecayCarry& dc) {
-    const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
-    float dsc[4] = {dc.dsc[0], dc.dsc[1], dc.dsc[2], dc.dsc[3]};
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
         const float kx[4] = {bf_lo(in.k[rr].x), bf_hi(in.k[rr].x), bf_lo(in.k[rr].y),
@@ -204,7 +187,7 @@ __device__ __forceinline__ void decay_rows_kq(ChunkLds& sm, const ChunkIn& in, i
         float kt[4], qt[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            dsc[e] *= dc.al[rr][e];
+            dsc[e] *= al[rr][e];
             kt[e] = kx[e] * dsc[e];
             qt[e] = qx[e] * dsc[e];
         }
@@ -214,22 +197,6 @@ __device__ __forceinline__ void decay_rows_kq(ChunkLds& sm, const ChunkIn& in, i
         *reinterpret_cast<uint2*>(sm.Qt + t * LDK + ch0) =
             make_uint2(pack2(qt[0], qt[1]), pack2(qt[2], qt[3]));
     }
-}
-
-// First half: both parts.
-template <typename GamSink>
-__device__ __forceinline__ void decay_kq(ChunkLds& sm, const ChunkIn& in, int p, int lane,
-                                         GamSink gam_sink, DecayCarry& dc) {
-    decay_scan(sm, in, p, lane, gam_sink, dc);
-    decay_rows_kq(sm, in, p, lane, dc);
-}
-
-// Second half: Kb rows and the Kb^T pieces.
-template <typename KbtSink>
-__device__ __forceinline__ void decay_kb(ChunkLds& sm, const ChunkIn& in, int p, int lane,
-                                         const DecayCarry& dc, KbtSink kbt_sink) {
-    const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
-    float fsc[4] = {dc.fsc[0], dc.fsc[1], dc.fsc[2], dc.fsc[3]};
     u32x4 kbt[4];     // Kb^T pieces: channel ch0 + e, token pairs (2j, 2j + 1) packed
     float kb_odd[4];  // Kb of the odd token of the pair being formed
 #pragma unroll
@@ -242,21 +209,13 @@ __device__ __forceinline__ void decay_kb(ChunkLds& sm, const ChunkIn& in, int p,
             kb[e] = kx[e] * fsc[e];
             if (rr & 1) kb_odd[e] = kb[e];
             else kbt[e][rr >> 1] = pack2(kb[e], kb_odd[e]);
-            fsc[e] *= dc.al[rr][e];
+            fsc[e] *= al[rr][e];
         }
         *reinterpret_cast<uint2*>(sm.Kb + (8 * tg + rr) * LDK + ch0) =
             make_uint2(pack2(kb[0], kb[1]), pack2(kb[2], kb[3]));
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) kbt_sink(ch0 + e, tg, kbt[e]);
-}
-
-template <typename GamSink, typename KbtSink>
-__device__ __forceinline__ void decay_stage(ChunkLds& sm, const ChunkIn& in, int p, int lane,
-                                            GamSink gam_sink, KbtSink kbt_sink) {
-    DecayCarry dc;
-    decay_kq(sm, in, p, lane, gam_sink, dc);
-    decay_kb(sm, in, p, lane, dc, kbt_sink);
 }
 
 // N stage (after the decay stage is visible): wave p forms diagonal block p of

@@ -26,7 +26,9 @@
  *   beta [tokens, H];  state [slots, H, d_k, d_v] (d_v contiguous: row i of a
  *   head's state belongs to key channel i).
  * - q, k, v and o share one dtype (KDA_F32 or KDA_BF16).  g (the log of the
- *   decay, alpha = exp(g)), beta and the state are always fp32.  g is per key
+ *   decay, alpha = exp(g)) and beta are always fp32; the state is fp32, except
+ *   that decode and state init also take states stored in bf16 (their
+ *   state_dtype argument; arithmetic stays fp32).  g is per key
  *   channel ([..., H, d_k], KDA_GATE_CHANNEL) or per head ([..., H],
  *   KDA_GATE_HEAD, alpha broadcast over the channels).  No query scale is
  *   applied: a caller that wants one scales q.
