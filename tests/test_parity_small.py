@@ -192,13 +192,16 @@ def test_decode_out_of_range_slot():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("l2", [0, 128])
-def test_short_conv_prefill(l2, dtype):
+@pytest.mark.parametrize("C,l2", [(512, 0), (512, 128), (2560, 128), (384, 96)])
+def test_short_conv_prefill(C, l2, dtype):
     """Conv (+ per-head L2) over packed ragged sequences with incoming tails;
-    outgoing tails are copies of inputs, so they must match bit for bit."""
+    outgoing tails are copies of inputs, so they must match bit for bit.  Heads
+    of 128 channels run the 16-byte-per-lane kernel (2560 channels: a partly
+    filled last workgroup); heads of 96, not a power of two in lanes, the
+    general one."""
     m = kda()
     lens = [1, 40, 0, 2, 33]
-    T, C = sum(lens), 512
+    T = sum(lens)
     cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     x = workloads.normal((T, C), 11, 0).to(tdt)
@@ -214,9 +217,51 @@ def test_short_conv_prefill(l2, dtype):
     if l2:
         y_ref = oracle.l2norm_heads(y_ref, l2, eps=1e-6)
     err = rel_fro(np64(y), y_ref)
-    print(f"conv prefill l2={l2} {dtype}: {err:.2e}")
+    print(f"conv prefill C={C} l2={l2} {dtype}: {err:.2e}")
     assert err <= (1e-6 if dtype == "f32" else 1e-2)
     assert np.array_equal(np64(tail_out), tail_ref)
+
+
+def test_short_conv_prefill_long_runs():
+    """131072 tokens x 2048 bf16 channels: enough tokens that each workgroup of
+    the 16-byte kernel walks 128 of them, over ragged sequences (empty ones
+    included) that start and end inside those runs.  Checked on sampled tokens
+    (every sequence's first four, the ends, and random ones); output token t
+    needs only inputs t-3..t of its sequence, or the incoming tail."""
+    m = kda()
+    C, l2 = 2048, 128
+    rng = np.random.default_rng(14)
+    lens = rng.integers(1, 700, size=400)
+    lens[::37] = 0
+    lens[-1] += 131072 - int(lens.sum())
+    assert lens[-1] > 0
+    T = int(lens.sum())
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    x = workloads.normal((T, C), 14, 0).to(torch.bfloat16)
+    w = workloads.normal((C, 4), 14, 1, 0.0, 0.5)
+    tail = workloads.normal((len(lens), 3, C), 14, 2).to(torch.bfloat16)
+    y = m.kda_short_conv_prefill(dev(x), dev(w), cu_seqlens=dev(cu), cu_seqlens_host=cu,
+                                 l2_head_dim=l2, conv_tail_in=dev(tail))
+    torch.cuda.synchronize()
+    y = y.cpu()
+    cuv = cu.numpy().astype(np.int64)
+    picks = set(rng.integers(0, T, size=200).tolist())
+    for n in range(len(lens)):
+        for t in range(cuv[n], min(cuv[n] + 4, cuv[n + 1])):
+            picks.add(t)
+        if cuv[n + 1] > cuv[n]:
+            picks.add(int(cuv[n + 1] - 1))
+    w64 = np64(w)
+    worst = 0.0
+    for t in sorted(picks):
+        n = int(np.searchsorted(cuv, t, side="right") - 1)
+        lo = max(int(cuv[n]), t - 3)
+        y_ref, _ = oracle.short_conv(np64(x[lo:t + 1]), w64,
+                                     tail=np64(tail[n:n + 1]) if lo == cuv[n] else None)
+        y_ref = oracle.l2norm_heads(y_ref[-1:], l2, eps=1e-6)
+        worst = max(worst, rel_fro(np64(y[t:t + 1]), y_ref))
+    print(f"conv prefill {T} x {C}, {len(picks)} sampled tokens: worst {worst:.2e}")
+    assert worst <= 1e-2
 
 
 def test_short_conv_prefill_in_place_tail():
