@@ -34,6 +34,7 @@ PREFILL_KERNELS = "prep_kernel + state_kernel (kda_prefill_split.hip), all windo
 DECODE_KERNEL = "decode_kernel"
 DECODE_TOKENS_KERNEL = "decode_kernel_4tok"  # traffic record of the 4-token decode
 DECODE_BF16_KERNEL = "decode_kernel_bf16state"  # traffic record of the bf16-state decode
+CONV_KERNEL = "conv_prefill"  # traffic record of the mixer front end (3 conv launches)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc")
 SOURCES = {
@@ -43,6 +44,7 @@ SOURCES = {
     DECODE_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
     DECODE_TOKENS_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
     DECODE_BF16_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
+    CONV_KERNEL: [os.path.join(_CSRC, "kda_conv.hip")],
 }
 
 
@@ -171,7 +173,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_tokens", "decode_bf16_state",
-                                       "copy"],
+                                       "conv", "copy"],
                     default=None, help="run just one kernel (for profiler runs)")
     args = ap.parse_args()
 
@@ -368,6 +370,47 @@ def main():
         if args.only == "decode_tokens":
             result.update({"value": B * n_tok / (mtp_ms * 1e-3), "unit": "tokens/s",
                            "ms_per_step": mtp_ms})
+    if args.only == "conv" or (args.only is None and not args.no_decode):
+        # the mixer's front end: width-4 causal conv of the q, k, v streams
+        # (32768 x 8192 bf16 each), per-head L2 norm (128 channels) of q and k
+        xs, ws = workloads.mixer_conv_streams()
+        T, Cc = xs[0].shape
+        xs = [x.to(dev) for x in xs]
+        ws = [w.to(dev) for w in ws]
+        ys = [torch.empty_like(x) for x in xs]
+        cu_h = torch.tensor([0, T], dtype=torch.int32)
+        cu_d = cu_h.to(dev)
+
+        def front():
+            for x, w, y, l2 in zip(xs, ws, ys, (128, 128, 0)):
+                kda.kda_short_conv_prefill(x, w, cu_seqlens=cu_d, cu_seqlens_host=cu_h,
+                                           l2_head_dim=l2, y=y)
+
+        for _ in range(args.warmup):
+            front()
+        torch.cuda.synchronize()
+        csteps = max(1, min(nsteps, 20))
+        e0.record()
+        for _ in range(csteps):
+            front()
+        e1.record()
+        torch.cuda.synchronize()
+        conv_ms = e0.elapsed_time(e1) / csteps
+        alg = 3 * (2 * T * Cc * 2 + Cc * 4 * 4)  # x read, y written, w read; per stream
+        gbs = alg / (conv_ms * 1e-3) / 1e9
+        result["conv_prefill"] = {
+            "workload": f"mixer front end: width-4 causal conv of 3 streams [{T}, {Cc}] bf16, "
+                        "per-head L2 norm (128 channels) of the q and k streams, one call each",
+            "ms_per_step": conv_ms, "tokens_per_s": T / (conv_ms * 1e-3),
+            "roofline": {"bound": "hbm", "kernel": "conv_prefill_wide_kernel (3 launches)",
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(CONV_KERNEL),
+                         "algorithmic_bytes": alg}}
+        if args.only == "conv":
+            result.update({"value": T / (conv_ms * 1e-3), "unit": "tokens/s",
+                           "ms_per_step": conv_ms})
+        del xs, ws, ys
     print(json.dumps(result), flush=True)
 
 

@@ -203,6 +203,16 @@ def packed_long(lengths=PACKED_LENGTHS):
                              g_sigma=0.5, s0_std=0.02, seed=1004)
 
 
+def mixer_conv_streams(t_prefill=32768, seed=1005):
+    """The pre-conv q, k, v streams [t_prefill, 8192] bf16 and conv weights
+    [8192, 4] of the mixer workload: the same draws as mixer() for its first
+    t_prefill tokens, without the recurrence inputs."""
+    C = 64 * 128
+    w = normal((3 * C, 4), seed, TID["conv_w"], 0.0, 0.5)
+    xs = [normal((t_prefill, C), seed, TID[n]).to(torch.bfloat16) for n in ("x_q", "x_k", "x_v")]
+    return xs, [w[i * C:(i + 1) * C].contiguous() for i in range(3)]
+
+
 def mixer(t_prefill=32768, n_decode=512):
     """Full mixer with state handoff: width-4 causal conv over 8192-channel q, k, v
     streams, per-head L2 norm of q and k, prefill of 32768 tokens then 512 decode
