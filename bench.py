@@ -72,13 +72,14 @@ def measured_traffic(kernel):
             rec["write_kib"] * 1024 * rec["write_scale"])
 
 
-def prefill_algorithmic(T, H, d, chunk, with_s0, with_sfinal):
+def prefill_algorithmic(T, H, d, chunk, with_s0, with_sfinal, g_bytes=4):
     """Algorithmic HBM bytes and flops of one prefill launch (bf16 q/k/v/o, fp32
-    g/beta/state).  Bytes per token-head: q, k, v 3*2d, g 4d, beta 4, o 2d.
+    g/beta/state).  Bytes per token-head: q, k, v 3*2d, g 4d (2d for the bf16
+    decay projection of the fused gate prologue), beta 4, o 2d.
     Flops per token-head: 6 d^2 (W S, Qt S, Kb^T U) + 5 C d (the C x C products
     and the two C-wide applications) + C^2 / 3 (triangular inverse)."""
     th = T * H
-    bytes_ = th * (3 * 2 * d + 4 * d + 4 + 2 * d)
+    bytes_ = th * (3 * 2 * d + g_bytes * d + 4 + 2 * d)
     state = H * d * d * 4
     bytes_ += state * (int(with_s0) + int(with_sfinal))
     flops = th * (6 * d * d + 5 * chunk * d + chunk * chunk / 3.0)
@@ -172,8 +173,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_tokens", "decode_bf16_state",
-                                       "conv", "copy"],
+    ap.add_argument("--only", choices=["prefill", "prefill_gate_proj", "decode", "decode_tokens",
+                                       "decode_bf16_state", "conv", "copy"],
                     default=None, help="run just one kernel (for profiler runs)")
     args = ap.parse_args()
 
@@ -266,6 +267,53 @@ def main():
         if not args.no_cpu_baseline and args.only is None:
             result["cpu_baseline"] = cpu_baseline_run(inp)
         del inp
+        torch.cuda.empty_cache()
+
+    if args.only == "prefill_gate_proj" or (args.only is None and not args.no_decode):
+        # the same layer with the gate prologue fused: bf16 decay projection f,
+        # a_log = 0 and f = -N(3, 1), so that the decay has the layer's own
+        # distribution; beta from fp32 logits
+        inp = workloads.ling_prefill()
+        T, H, d, C = inp.T, inp.H, inp.d, inp.chunk
+        pr = workloads.gate_projections(T, H, d, dtype="bf16", g_mu=3.0, g_sigma=1.0,
+                                        seed=1002)
+        q, k, v, f, b, a_log = (x.to(dev) for x in (inp.q, inp.k, inp.v, pr.f, pr.b, pr.a_log))
+        cu = inp.cu_seqlens.to(dev)
+        state = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+        o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+
+        def gstep(e0=None, e1=None):
+            kda.kda_state_init(state)
+            if e0 is not None:
+                e0.record()
+            kda.kda_prefill_chunked(q, k, v, f, b, cu_seqlens=cu, cu_seqlens_host=inp.cu_seqlens,
+                                    chunk=C, initial_state=state, final_state=state, o=o,
+                                    a_log=a_log)
+            if e1 is not None:
+                e1.record()
+
+        for _ in range(args.warmup):
+            gstep()
+        torch.cuda.synchronize()
+        gsteps = args.steps
+        pairs = [(ev(), ev()) for _ in range(gsteps)]
+        for e0_, e1_ in pairs:
+            gstep(e0_, e1_)
+        torch.cuda.synchronize()
+        g_ms = sum(a.elapsed_time(b_) for a, b_ in pairs) / len(pairs)
+        alg_bytes, _ = prefill_algorithmic(T, H, d, C, True, True, g_bytes=2)
+        gbs = alg_bytes / (g_ms * 1e-3) / 1e9
+        result["prefill_gate_proj"] = {
+            "workload": "the Ling-shaped layer prefill with the gate prologue fused: bf16 decay "
+                        "projection f [8192, 64, 128], a_log [64] = 0, fp32 beta logits",
+            "ms_per_call": g_ms, "tokens_per_s": T / (g_ms * 1e-3),
+            "roofline": {"bound": "hbm", "kernel": PREFILL_KERNELS, "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes": alg_bytes}}
+        if args.only == "prefill_gate_proj":
+            result.update({"value": T / (g_ms * 1e-3), "unit": "tokens/s",
+                           "ms_per_step": g_ms})
+        del q, k, v, f, b, a_log, o, state, inp, pr
         torch.cuda.empty_cache()
 
     B, H, d = 256, 64, 128  # the batched decode workload's shape

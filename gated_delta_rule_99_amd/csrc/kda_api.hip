@@ -41,6 +41,32 @@ bool mfma_shape(kda_dtype dtype, int dk, int dv, int chunk) {
 
 size_t elem_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
 
+// Gate layout and a_log checks shared by the recurrence entry points.
+kda_status check_gate(const char* fn, kda_gate gate, const float* a_log) {
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_PROJ)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate layout %d", fn, (int)gate);
+    if (gate == KDA_GATE_PROJ && (!a_log || ((uintptr_t)a_log & 3u)))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "%s: KDA_GATE_PROJ needs a_log, non-NULL and 4-byte aligned", fn);
+    if (gate != KDA_GATE_PROJ && a_log)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: a_log is only taken with KDA_GATE_PROJ", fn);
+    return KDA_OK;
+}
+
+// Bytes of g for `tokens` tokens: fp32 per channel or per head, or the
+// projection in the q/k/v dtype.
+size_t gate_bytes(kda_gate gate, size_t tokens, int H, int dk, kda_dtype dtype) {
+    if (gate == KDA_GATE_HEAD) return tokens * H * 4;
+    return tokens * H * dk * (gate == KDA_GATE_PROJ ? elem_size(dtype) : 4);
+}
+
+kda::Gate make_gate(const void* g, const float* a_log, kda_gate gate) {
+    return kda::Gate{g, a_log,
+                     gate == KDA_GATE_HEAD   ? kda::GATE_HEAD
+                     : gate == KDA_GATE_PROJ ? kda::GATE_PROJ
+                                             : kda::GATE_CH};
+}
+
 // Common head-shape checks.  Returns KDA_OK or an error with detail set.
 kda_status check_heads(const char* fn, int H, int dk, int dv) {
     if (H <= 0 || dk <= 0 || dv <= 0)
@@ -114,9 +140,9 @@ kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, i
                       "kda_state_init launch");
 }
 
-kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const float* g,
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const void* g,
                                const float* beta, kda_dtype dtype, kda_gate gate,
-                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               const float* a_log, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
                                const float* initial_state, float* final_state, void* o,
                                float* snapshots, int snap_interval, int snap_capacity,
@@ -125,8 +151,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     g_detail[0] = 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
-    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate layout %d", fn, (int)gate);
+    if (kda_status s = check_gate(fn, gate, a_log)) return s;
     if (kda_status s = check_heads(fn, H, dk, dv)) return s;
     if (chunk != 16 && chunk != 32 && chunk != 64)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: chunk %d not in {16, 32, 64}", fn, chunk);
@@ -141,7 +166,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                     (long long)blocks);
     const size_t es = elem_size(dtype);
     const size_t n_qk = (size_t)T * H * d, n_bt = (size_t)T * H;
-    const size_t n_g = gate == KDA_GATE_HEAD ? n_bt : n_qk;  // g elements
+    const size_t gb = gate_bytes(gate, (size_t)T, H, d, dtype);
+    const size_t ab = a_log ? (size_t)H * 4 : 0;
     const size_t sbytes = (size_t)n_seqs * kda_state_bytes(H, dk, dv, KDA_F32);
     if (T > 0) {
         if (!q || !k || !v || !g || !beta || !o)
@@ -150,8 +176,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
             ((uintptr_t)beta & 3u))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
         if (overlaps(o, n_qk * es, q, n_qk * es) || overlaps(o, n_qk * es, k, n_qk * es) ||
-            overlaps(o, n_qk * es, v, n_qk * es) || overlaps(o, n_qk * es, g, n_g * 4) ||
-            overlaps(o, n_qk * es, beta, n_bt * 4) ||
+            overlaps(o, n_qk * es, v, n_qk * es) || overlaps(o, n_qk * es, g, gb) ||
+            overlaps(o, n_qk * es, beta, n_bt * 4) || overlaps(o, n_qk * es, a_log, ab) ||
             overlaps(o, n_qk * es, final_state, sbytes) ||
             overlaps(o, n_qk * es, initial_state, sbytes))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o overlaps another argument", fn);
@@ -164,7 +190,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                     "%s: initial_state and final_state overlap without being equal", fn);
     if (final_state && T > 0 &&
         (overlaps(final_state, sbytes, q, n_qk * es) || overlaps(final_state, sbytes, k, n_qk * es) ||
-         overlaps(final_state, sbytes, v, n_qk * es) || overlaps(final_state, sbytes, g, n_g * 4)))
+         overlaps(final_state, sbytes, v, n_qk * es) || overlaps(final_state, sbytes, g, gb) ||
+         overlaps(final_state, sbytes, a_log, ab)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state overlaps an input", fn);
 
     // snapshots: [n_seqs, snap_capacity, H, dk, dv] fp32
@@ -179,7 +206,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned snapshots", fn);
         const size_t snb = (size_t)n_seqs * snap_capacity * kda_state_bytes(H, dk, dv, KDA_F32);
         if (overlaps(snapshots, snb, q, n_qk * es) || overlaps(snapshots, snb, k, n_qk * es) ||
-            overlaps(snapshots, snb, v, n_qk * es) || overlaps(snapshots, snb, g, n_g * 4) ||
+            overlaps(snapshots, snb, v, n_qk * es) || overlaps(snapshots, snb, g, gb) ||
+            overlaps(snapshots, snb, a_log, ab) ||
             overlaps(snapshots, snb, beta, n_bt * 4) || overlaps(snapshots, snb, o, n_qk * es) ||
             overlaps(snapshots, snb, initial_state, sbytes) ||
             overlaps(snapshots, snb, final_state, sbytes) ||
@@ -198,13 +226,15 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
         if (!aligned16(workspace))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned workspace", fn);
         if (overlaps(workspace, ws_need, q, n_qk * es) || overlaps(workspace, ws_need, k, n_qk * es) ||
-            overlaps(workspace, ws_need, v, n_qk * es) || overlaps(workspace, ws_need, g, n_g * 4) ||
+            overlaps(workspace, ws_need, v, n_qk * es) || overlaps(workspace, ws_need, g, gb) ||
+            overlaps(workspace, ws_need, a_log, ab) ||
             overlaps(workspace, ws_need, beta, n_bt * 4) || overlaps(workspace, ws_need, o, n_qk * es) ||
             overlaps(workspace, ws_need, initial_state, sbytes) ||
             overlaps(workspace, ws_need, final_state, sbytes))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps another argument", fn);
     }
 
+    const kda::Gate gt = make_gate(g, a_log, gate);
     hipError_t err;
     if (mfma && workspace) {
         int max_chunks = 0;
@@ -212,15 +242,14 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
             const int nc = (int)(((int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n] + 63) / 64);
             max_chunks = nc > max_chunks ? nc : max_chunks;
         }
-        err = kda::launch_prefill_split(q, k, v, g, beta, gate == KDA_GATE_HEAD, cu_seqlens_dev,
+        err = kda::launch_prefill_split(q, k, v, gt, beta, cu_seqlens_dev,
                                         n_seqs, T, H, max_chunks, initial_state, final_state, o,
                                         snap, workspace, stream);
     } else if (mfma)
-        err = kda::launch_prefill_fused(q, k, v, g, beta, gate == KDA_GATE_HEAD, cu_seqlens_dev,
+        err = kda::launch_prefill_fused(q, k, v, gt, beta, cu_seqlens_dev,
                                         n_seqs, T, H, initial_state, final_state, o, snap, stream);
     else
-        err = kda::launch_prefill_vector(q, k, v, g, beta, dtype, gate == KDA_GATE_HEAD,
-                                         cu_seqlens_dev, n_seqs, T, H, d, chunk, initial_state,
+        err = kda::launch_prefill_vector(q, k, v, gt, beta, dtype, cu_seqlens_dev, n_seqs, T, H, d, chunk, initial_state,
                                          final_state, o, snap, stream);
     return hip_status(err, "kda_prefill_chunked launch");
 }
@@ -233,8 +262,9 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
 
 // Shared by kda_decode_step (n_tok = 1, no snapshots) and kda_decode_tokens.
 static kda_status decode_common(const char* fn, const void* q, const void* k, const void* v,
-                                const float* g, const float* beta, kda_dtype dtype, kda_gate gate,
-                                void* state, kda_dtype state_dtype, int64_t n_slots,
+                                const void* g, const float* beta, kda_dtype dtype, kda_gate gate,
+                                const float* a_log, void* state, kda_dtype state_dtype,
+                                int64_t n_slots,
                                 const int32_t* slot_idx, int B, int n_tok, int H, int dk, int dv,
                                 void* o, void* token_states, hipStream_t stream) {
     g_detail[0] = 0;
@@ -242,8 +272,7 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
     if (state_dtype != KDA_F32 && state_dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown state dtype %d", fn, (int)state_dtype);
-    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate layout %d", fn, (int)gate);
+    if (kda_status s = check_gate(fn, gate, a_log)) return s;
     if (kda_status s = check_heads(fn, H, dk, dv)) return s;
     if (B < 0 || n_slots < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B and n_slots must be >= 0", fn);
@@ -264,41 +293,48 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
         !aligned16(token_states))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
     const size_t nv = (size_t)B * n_tok * H * dk, nb = (size_t)B * n_tok * H * 4;
-    const size_t ng = gate == KDA_GATE_HEAD ? (size_t)B * n_tok * H : nv;  // g elements
+    const size_t gb = gate_bytes(gate, (size_t)B * n_tok, H, dk, dtype);
+    const size_t ab = a_log ? (size_t)H * 4 : 0;
     const size_t sbytes = (size_t)n_slots * kda_state_bytes(H, dk, dv, state_dtype);
     const size_t tbytes = (size_t)B * n_tok * kda_state_bytes(H, dk, dv, state_dtype);
     if (overlaps(o, nv * es, q, nv * es) || overlaps(o, nv * es, k, nv * es) ||
-        overlaps(o, nv * es, v, nv * es) || overlaps(o, nv * es, g, ng * 4) ||
+        overlaps(o, nv * es, v, nv * es) || overlaps(o, nv * es, g, gb) ||
+        overlaps(o, nv * es, a_log, ab) ||
         overlaps(o, nv * es, state, sbytes) || overlaps(state, sbytes, q, nv * es) ||
         overlaps(state, sbytes, k, nv * es) || overlaps(state, sbytes, v, nv * es) ||
-        overlaps(state, sbytes, g, ng * 4) || overlaps(state, sbytes, beta, nb))
+        overlaps(state, sbytes, g, gb) || overlaps(state, sbytes, beta, nb) ||
+        overlaps(state, sbytes, a_log, ab))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state or o overlaps another argument", fn);
     if (token_states &&
         (overlaps(token_states, tbytes, state, sbytes) || overlaps(token_states, tbytes, o, nv * es) ||
          overlaps(token_states, tbytes, q, nv * es) || overlaps(token_states, tbytes, k, nv * es) ||
-         overlaps(token_states, tbytes, v, nv * es) || overlaps(token_states, tbytes, g, ng * 4) ||
-         overlaps(token_states, tbytes, beta, nb)))
+         overlaps(token_states, tbytes, v, nv * es) || overlaps(token_states, tbytes, g, gb) ||
+         overlaps(token_states, tbytes, beta, nb) || overlaps(token_states, tbytes, a_log, ab)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: token_states overlaps another argument", fn);
-    return hip_status(kda::launch_decode(q, k, v, g, beta, dtype, gate == KDA_GATE_HEAD, state,
+    return hip_status(kda::launch_decode(q, k, v, make_gate(g, a_log, gate), beta, dtype, state,
                                          state_dtype, n_slots, slot_idx, B, n_tok, H, dk,
                                          token_states, o, stream),
                       "decode launch");
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, kda_dtype dtype, kda_gate gate, void* state,
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g,
+                           const float* beta, kda_dtype dtype, kda_gate gate,
+                           const float* a_log, void* state,
                            kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
                            int B, int H, int dk, int dv, void* o, hipStream_t stream) {
-    return decode_common("kda_decode_step", q, k, v, g, beta, dtype, gate, state, state_dtype,
+    return decode_common("kda_decode_step", q, k, v, g, beta, dtype, gate, a_log, state,
+                         state_dtype,
                          n_slots, slot_idx, B, 1, H, dk, dv, o, nullptr, stream);
 }
 
-kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, kda_dtype dtype, kda_gate gate, void* state,
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const void* g,
+                             const float* beta, kda_dtype dtype, kda_gate gate,
+                             const float* a_log, void* state,
                              kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
                              int B, int n_tok, int H, int dk, int dv, void* o,
                              void* token_states, hipStream_t stream) {
-    return decode_common("kda_decode_tokens", q, k, v, g, beta, dtype, gate, state, state_dtype,
+    return decode_common("kda_decode_tokens", q, k, v, g, beta, dtype, gate, a_log, state,
+                         state_dtype,
                          n_slots, slot_idx, B, n_tok, H, dk, dv, o, token_states, stream);
 }
 

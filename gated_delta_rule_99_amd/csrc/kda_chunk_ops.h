@@ -100,32 +100,47 @@ __device__ __forceinline__ void zero_tp(ChunkLds& sm, int tid, int nthreads) {
 // One lane's inputs of a chunk: channels [32p + 4cg, +4) of tokens [8tg, 8tg+8).
 struct ChunkIn {
     float4 g[8];
+    uint2 f[8];   // GATE_PROJ: the decay projection (bf16 pairs) in place of g
+    float a_log;  // GATE_PROJ: the head's log rate
+    int L;        // GATE_PROJ: rows of the chunk (rows past it keep alpha = 1)
     uint2 k[8], q[8];
-    float beta;  // beta of token `lane` (wave 0 only)
+    float beta;  // beta of token `lane` (wave 0 only); logits with GATE_PROJ
 };
 
 // Issue the loads of chunk rows [c0, c0 + L) of head h; rows past L (and every
-// row when L = 0) read as zero, i.e. alpha = 1 and k = q = 0.  With GH (per-head
-// decay), g holds one value per (token, head), broadcast here to the channels.
-template <bool GH>
+// row when L = 0) read as zero, i.e. alpha = 1 and k = q = 0.  GM (GateMode):
+// GATE_HEAD broadcasts one g per (token, head) to the channels; GATE_PROJ loads
+// the bf16 decay projection, turned into alpha by the decay stage.
+template <int GM>
 __device__ __forceinline__ void load_chunk(ChunkIn& in, const bf16_t* q, const bf16_t* k,
-                                           const float* g, const float* beta, int64_t c0, int L,
+                                           const Gate& gt, const float* beta, int64_t c0, int L,
                                            int H, int h, int p, int lane) {
     const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
     const size_t row = (size_t)H * D;
     const int64_t cc0 = L > 0 ? c0 : 0;  // keep the base address inside the tensors
     const size_t base = (size_t)cc0 * row + (size_t)h * D;
     const int rowb2 = (int)(row * 2), rowb4 = (int)(row * 4);
-    const auto rg = GH ? window(g + (size_t)cc0 * H + h, L * H * 4) : window(g + base, L * rowb4);
+    const float* g = static_cast<const float*>(gt.g);
+    const auto rg = GM == GATE_HEAD ? window(g + (size_t)cc0 * H + h, L * H * 4)
+                    : GM == GATE_PROJ
+                        ? window(static_cast<const bf16_t*>(gt.g) + base, L * rowb2)
+                        : window(g + base, L * rowb4);
     const auto rk = window(k + base, L * rowb2);
     const auto rq = window(q + base, L * rowb2);
     const int vkq = 8 * tg * rowb2 + ch0 * 2, vg = 8 * tg * rowb4 + ch0 * 4;
+    if constexpr (GM == GATE_PROJ) {
+        in.a_log = gt.a_log[h];
+        in.L = L;
+    }
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
-        if constexpr (GH) {
+        if constexpr (GM == GATE_HEAD) {
             const float x = __uint_as_float(
                 __builtin_amdgcn_raw_buffer_load_b32(rg, 8 * tg * H * 4, rr * H * 4, 0));
             in.g[rr] = make_float4(x, x, x, x);
+        } else if constexpr (GM == GATE_PROJ) {
+            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rg, vkq, rr * rowb2, 0);
+            in.f[rr] = make_uint2(x[0], x[1]);
         } else {
             const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rg, vg, rr * rowb4, 0);
             in.g[rr] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]),
@@ -140,22 +155,40 @@ __device__ __forceinline__ void load_chunk(ChunkIn& in, const bf16_t* q, const b
     in.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, lane * H * 4, 0, 0));
 }
 
+// beta of token `lane` of the chunk (wave 0); zero on padding rows.
+template <int GM>
+__device__ __forceinline__ float chunk_beta(const ChunkIn& in, int lane) {
+    if constexpr (GM == GATE_PROJ) return lane < in.L ? sigmoid_f(in.beta) : 0.f;
+    return in.beta;
+}
+
 // Decay stage: alpha = exp(g), in-chunk running products, the scaled operands
 // Kt, Qt, Kb (rows into LDS) and beta into LDS.  Hands Gam[ch0 + e] (lanes with
 // tg == 0) to gam_sink(ch0, gam4) and, for every lane, the Kb^T piece of channel
 // ch0 + e, tokens [8tg, 8tg + 8) as 8 packed bf16 to kbt_sink(i, tg, u32x4).
-template <typename GamSink, typename KbtSink>
+template <int GM, typename GamSink, typename KbtSink>
 __device__ __forceinline__ void decay_stage(ChunkLds& sm, const ChunkIn& in, int p, int lane,
                                             GamSink gam_sink, KbtSink kbt_sink) {
     const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
-    if (p == 0) sm.beta[lane] = in.beta;
+    if (p == 0) sm.beta[lane] = chunk_beta<GM>(in, lane);
     float al[8][4], tot[4] = {1.f, 1.f, 1.f, 1.f};
+    float rate = 0.f;
+    if constexpr (GM == GATE_PROJ) rate = __builtin_amdgcn_exp2f(in.a_log * LOG2E);
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
-        al[rr][0] = __builtin_amdgcn_exp2f(in.g[rr].x * LOG2E);
-        al[rr][1] = __builtin_amdgcn_exp2f(in.g[rr].y * LOG2E);
-        al[rr][2] = __builtin_amdgcn_exp2f(in.g[rr].z * LOG2E);
-        al[rr][3] = __builtin_amdgcn_exp2f(in.g[rr].w * LOG2E);
+        if constexpr (GM == GATE_PROJ) {
+            const float fx[4] = {bf_lo(in.f[rr].x), bf_hi(in.f[rr].x), bf_lo(in.f[rr].y),
+                                 bf_hi(in.f[rr].y)};
+            const bool live = 8 * tg + rr < in.L;  // padding rows keep alpha = 1
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                al[rr][e] = live ? __builtin_amdgcn_exp2f(proj_log2_decay(fx[e], rate)) : 1.f;
+        } else {
+            al[rr][0] = __builtin_amdgcn_exp2f(in.g[rr].x * LOG2E);
+            al[rr][1] = __builtin_amdgcn_exp2f(in.g[rr].y * LOG2E);
+            al[rr][2] = __builtin_amdgcn_exp2f(in.g[rr].z * LOG2E);
+            al[rr][3] = __builtin_amdgcn_exp2f(in.g[rr].w * LOG2E);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) tot[e] *= al[rr][e];
     }

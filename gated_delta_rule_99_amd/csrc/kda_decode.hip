@@ -170,11 +170,14 @@ __device__ __forceinline__ void in_store(Tin* p, const float (&x)[VEC]) {
 // registers and rounded once when it is written back).  MULTI: n_tok may
 // exceed 1 (the token loop then also holds the partial-sum reads to fewer
 // registers, which was measured faster for several tokens and slower for one).
-template <int D, typename Tin, typename TS, bool MULTI>
+// PROJ: g is the decay projection in Tin, with one log rate a_log per head,
+// and beta holds logits (GATE_PROJ); otherwise g is fp32, per key channel or,
+// with g_head, per head.
+template <int D, typename Tin, typename TS, bool MULTI, bool PROJ>
 __global__ void __launch_bounds__((DecodeShape<D, decode_vec<D, TS>()>::NT))
 decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-              const float* __restrict__ g, const float* __restrict__ beta,
-              int g_head, TS* __restrict__ state, int64_t n_slots,
+              const float* __restrict__ g, const float* __restrict__ a_log,
+              const float* __restrict__ beta, int g_head, TS* __restrict__ state, int64_t n_slots,
               const int32_t* __restrict__ slot_idx, int H, int n_tok,
               TS* __restrict__ token_states, Tin* __restrict__ o) {
     constexpr int VEC = decode_vec<D, TS>();
@@ -206,6 +209,8 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
     }
 
     TS* st = state + ((size_t)slot * H + h) * (size_t)(D * D);
+    float rate = 0.f;
+    if constexpr (PROJ) rate = __expf(a_log[h]);
     const int cg = tid % CG, rg = tid / CG, c0 = VEC * cg;
 
     // 1. stream the state in: RPT independent 16-byte loads per thread
@@ -222,7 +227,12 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
         // 2. gate vectors (small, cooperative)
         float qk_part = 0.f;
         for (int i = tid; i < D; i += NT) {
-            const float a = __expf(g_head ? g[row] : g[vec + i]);
+            float a;
+            if constexpr (PROJ)
+                a = __builtin_amdgcn_exp2f(proj_log2_decay(
+                    In<Tin>::load1(reinterpret_cast<const Tin*>(g) + vec + i), rate));
+            else
+                a = __expf(g_head ? g[row] : g[vec + i]);
             const float kv = In<Tin>::load1(k + vec + i);
             const float qv = In<Tin>::load1(q + vec + i);
             s_a[i] = a;
@@ -237,7 +247,8 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
             for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
             if ((tid & 63) == 0) s_qk[tid >> 6] = qk_part;
         }
-        const float bt = beta[row];
+        float bt = beta[row];
+        if constexpr (PROJ) bt = sigmoid_f(bt);
         float vj[VEC];
         in_load<Tin, VEC>(v + vec + c0, vj);
         __syncthreads();
@@ -318,45 +329,50 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
 }
 
 template <int D, typename Tin, typename TS>
-static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, bool g_head, void* state, int64_t n_slots,
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v, Gate g,
+                                  const float* beta, void* state, int64_t n_slots,
                                   const int32_t* slot_idx, int B, int n_tok, int H,
                                   void* token_states, void* o, hipStream_t stream) {
     const int64_t blocks = (int64_t)B * H;
     if (blocks == 0 || n_tok == 0) return hipSuccess;
-    auto kern = n_tok > 1 ? decode_kernel<D, Tin, TS, true> : decode_kernel<D, Tin, TS, false>;
+    const bool proj = g.mode == GATE_PROJ;
+    auto kern = n_tok > 1 ? (proj ? decode_kernel<D, Tin, TS, true, true>
+                                  : decode_kernel<D, Tin, TS, true, false>)
+                          : (proj ? decode_kernel<D, Tin, TS, false, true>
+                                  : decode_kernel<D, Tin, TS, false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(DecodeShape<D, decode_vec<D, TS>()>::NT),
-                       0, stream, (const Tin*)q, (const Tin*)k, (const Tin*)v, g, beta,
-                       (int)g_head, (TS*)state, n_slots, slot_idx, H, n_tok, (TS*)token_states,
+                       0, stream, (const Tin*)q, (const Tin*)k, (const Tin*)v,
+                       static_cast<const float*>(g.g), g.a_log, beta, (int)(g.mode == GATE_HEAD),
+                       (TS*)state, n_slots, slot_idx, H, n_tok, (TS*)token_states,
                        (Tin*)o);
     return hipGetLastError();
 }
 
 template <int D, typename Tin>
-static hipError_t launch_decode_s(const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, bool g_head, void* state,
+static hipError_t launch_decode_s(const void* q, const void* k, const void* v, Gate g,
+                                  const float* beta, void* state,
                                   kda_dtype state_dtype, int64_t n_slots,
                                   const int32_t* slot_idx, int B, int n_tok, int H,
                                   void* token_states, void* o, hipStream_t stream) {
     if (state_dtype == KDA_BF16)
-        return launch_decode_t<D, Tin, bf16_t>(q, k, v, g, beta, g_head, state, n_slots, slot_idx,
+        return launch_decode_t<D, Tin, bf16_t>(q, k, v, g, beta, state, n_slots, slot_idx,
                                                B, n_tok, H, token_states, o, stream);
-    return launch_decode_t<D, Tin, float>(q, k, v, g, beta, g_head, state, n_slots, slot_idx, B,
+    return launch_decode_t<D, Tin, float>(q, k, v, g, beta, state, n_slots, slot_idx, B,
                                           n_tok, H, token_states, o, stream);
 }
 
-hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, kda_dtype dtype, bool g_head, void* state,
+hipError_t launch_decode(const void* q, const void* k, const void* v, Gate g,
+                         const float* beta, kda_dtype dtype, void* state,
                          kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx, int B,
                          int n_tok, int H, int d, void* token_states, void* o,
                          hipStream_t stream) {
 #define KDA_DEC(D)                                                                           \
     if (d == D) {                                                                            \
         if (dtype == KDA_BF16)                                                               \
-            return launch_decode_s<D, bf16_t>(q, k, v, g, beta, g_head, state, state_dtype,  \
+            return launch_decode_s<D, bf16_t>(q, k, v, g, beta, state, state_dtype,  \
                                               n_slots, slot_idx, B, n_tok, H, token_states, o, \
                                               stream);                                       \
-        return launch_decode_s<D, float>(q, k, v, g, beta, g_head, state, state_dtype, n_slots, \
+        return launch_decode_s<D, float>(q, k, v, g, beta, state, state_dtype, n_slots, \
                                          slot_idx, B, n_tok, H, token_states, o, stream);    \
     }
     KDA_DEC(16)

@@ -100,6 +100,32 @@ __device__ __forceinline__ float* snapshot_at(const Snapshots& sn, int n, int h,
     return sn.ptr + (((size_t)n * sn.capacity + j) * H + h) * (size_t)D * D;
 }
 
+// ---------------------------------------------------------------- decay inputs
+// How a call gives the decay alpha = exp(g) and the write strength beta.
+//   GATE_CH   g: [tokens, H, D] fp32 log decay per key channel; beta as given.
+//   GATE_HEAD g: [tokens, H] fp32, one log decay per head; beta as given.
+//   GATE_PROJ g: [tokens, H, D] decay projection f in the q/k/v dtype, with
+//             one log rate a_log[h] per head: g = -exp(a_log[h]) softplus(f);
+//             beta holds logits: beta = sigmoid(beta).
+enum GateMode : int { GATE_CH = 0, GATE_HEAD = 1, GATE_PROJ = 2 };
+struct Gate {
+    const void* g;
+    const float* a_log;  // [H], GATE_PROJ only
+    int mode;
+};
+
+// log2 of the decay from the projection: -A softplus(f) / ln 2, with
+// softplus(f) = max(f, 0) + ln(1 + e^{-|f|}).
+__device__ __forceinline__ float proj_log2_decay(float f, float A) {
+    const float LOG2E_ = 1.4426950408889634f;
+    const float sp2 = fmaxf(f, 0.f) * LOG2E_ +
+                      __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(f) * LOG2E_));
+    return -A * sp2;
+}
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already checked.
 // n_elems elements of state_dtype: zeros (src NULL) or src converted.
@@ -108,22 +134,21 @@ hipError_t launch_state_init(void* state, kda_dtype state_dtype, int64_t n_elems
 
 // n_tok consecutive tokens per sequence; token_states may be NULL; state and
 // token_states hold state_dtype elements.
-// g_head: g holds one value per (token, head) instead of one per key channel.
-hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, kda_dtype dtype, bool g_head, void* state,
+hipError_t launch_decode(const void* q, const void* k, const void* v, Gate gate,
+                         const float* beta, kda_dtype dtype, void* state,
                          kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx, int B,
                          int n_tok, int H, int d, void* token_states, void* o,
                          hipStream_t stream);
 
-hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
-                                 const float* beta, kda_dtype dtype, bool g_head, const int32_t* cu,
+hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, Gate gate,
+                                 const float* beta, kda_dtype dtype, const int32_t* cu,
                                  int n_seqs, int64_t T, int H, int d, int chunk,
                                  const float* s0, float* s_final, void* o, Snapshots snap,
                                  hipStream_t stream);
 
 // bf16, d = 128, chunk = 64, one fused kernel (no workspace).
-hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, Gate gate,
+                                const float* beta, const int32_t* cu, int n_seqs,
                                 int64_t T, int H, const float* s0, float* s_final, void* o,
                                 Snapshots snap, hipStream_t stream);
 
@@ -132,8 +157,8 @@ hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, con
 // sequence's chunk count.
 int prefill_split_window(int n_seqs, int H);
 size_t prefill_split_workspace_bytes(int n_seqs, int H);
-hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gate gate,
+                                const float* beta, const int32_t* cu, int n_seqs,
                                 int64_t T, int H, int max_chunks, const float* s0,
                                 float* s_final, void* o, Snapshots snap, void* workspace,
                                 hipStream_t stream);

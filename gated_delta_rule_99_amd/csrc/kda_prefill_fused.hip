@@ -43,11 +43,11 @@ struct FusedLds {
 
 using namespace fu;
 
-// GH: g holds one log decay per (token, head) instead of one per key channel.
-template <bool GH>
+// GM: the decay inputs' GateMode (per channel, per head, or the projection).
+template <int GM>
 __global__ void __launch_bounds__(768)
 prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                     const bf16_t* __restrict__ v, const float* __restrict__ g,
+                     const bf16_t* __restrict__ v, Gate g,
                      const float* __restrict__ beta, const int32_t* __restrict__ cu,
                      int64_t T, int H, int n_pairs, const float* __restrict__ s0,
                      float* __restrict__ s_final, bf16_t* __restrict__ o, Snapshots snap) {
@@ -109,9 +109,9 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             *reinterpret_cast<u32x4*>(sm.KbT + i * LDT + 8 * tg) = piece;
         };
         ChunkIn in;
-        load_chunk<GH>(in, q, k, g, beta, tb, chunk_len(0), H, h, p, lane);
-        decay_stage(sm.ck, in, p, lane, gam_sink, kbt_sink);
-        load_chunk<GH>(in, q, k, g, beta, tb + C, chunk_len(1), H, h, p, lane);
+        load_chunk<GM>(in, q, k, g, beta, tb, chunk_len(0), H, h, p, lane);
+        decay_stage<GM>(sm.ck, in, p, lane, gam_sink, kbt_sink);
+        load_chunk<GM>(in, q, k, g, beta, tb + C, chunk_len(1), H, h, p, lane);
         __syncthreads();  // P1
         n_stage(sm.ck, p, lane);
         __syncthreads();  // P2
@@ -120,8 +120,8 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         __syncthreads();  // P4: copy-in of chunk 0 done
         for (int s = 0; s < nc; ++s) {
             const bool next = s + 1 < nc;
-            if (next) decay_stage(sm.ck, in, p, lane, gam_sink, kbt_sink);
-            load_chunk<GH>(in, q, k, g, beta, tb + (int64_t)(s + 2) * C, chunk_len(s + 2), H, h, p,
+            if (next) decay_stage<GM>(sm.ck, in, p, lane, gam_sink, kbt_sink);
+            load_chunk<GM>(in, q, k, g, beta, tb + (int64_t)(s + 2) * C, chunk_len(s + 2), H, h, p,
                            lane);
             __syncthreads();  // B1
             if (next) n_stage(sm.ck, p, lane);
@@ -244,13 +244,15 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
 }
 
-hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, Gate g,
+                                const float* beta, const int32_t* cu, int n_seqs,
                                 int64_t T, int H, const float* s0, float* s_final, void* o,
                                 Snapshots snap, hipStream_t stream) {
     const int64_t n_pairs = (int64_t)n_seqs * H;
     if (n_pairs == 0) return hipSuccess;
-    hipLaunchKernelGGL(g_head ? prefill_fused_kernel<true> : prefill_fused_kernel<false>,
+    hipLaunchKernelGGL(g.mode == GATE_HEAD   ? prefill_fused_kernel<GATE_HEAD>
+                       : g.mode == GATE_PROJ ? prefill_fused_kernel<GATE_PROJ>
+                                             : prefill_fused_kernel<GATE_CH>,
                        dim3((unsigned)(n_pairs * NS)), dim3(768), 0, stream, (const bf16_t*)q,
                        (const bf16_t*)k, (const bf16_t*)v, g, beta, cu, T, H, (int)n_pairs, s0,
                        s_final, (bf16_t*)o, snap);

@@ -30,11 +30,11 @@ using namespace sp;
 // ---------------------------------------------------------------- prep
 // grid (n_seqs * H, chunks in the window): one workgroup of 4 waves per
 // (sequence, head, window chunk) runs the operand stages and exports the tile.
-// GH: g holds one log decay per (token, head) instead of one per key channel.
-template <bool GH>
+// GM: the decay inputs' GateMode (per channel, per head, or the projection).
+template <int GM>
 __global__ void __launch_bounds__(256, 2)
-prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-            const float* __restrict__ g, const float* __restrict__ beta,
+prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
+            const float* __restrict__ beta,
             const int32_t* __restrict__ cu, int64_t T, int H, int w0, int win,
             uint8_t* __restrict__ ws_tiles) {
     __shared__ __attribute__((aligned(16))) ChunkLds sm;
@@ -51,9 +51,9 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
     zero_tp(sm, tid, 256);
     ChunkIn in;
-    load_chunk<GH>(in, q, k, g, beta, c0, L, H, h, p, lane);
-    tile_beta(rt, in, p, lane);
-    decay_stage(sm, in, p, lane, TileSinks{rt}, TileSinks{rt});
+    load_chunk<GM>(in, q, k, g, beta, c0, L, H, h, p, lane);
+    tile_beta<GM>(rt, in, p, lane);
+    decay_stage<GM>(sm, in, p, lane, TileSinks{rt}, TileSinks{rt});
     __syncthreads();
     tile_export_kq(sm, rt, p, lane);
     n_stage(sm, p, lane);
@@ -239,8 +239,8 @@ size_t prefill_split_workspace_bytes(int n_seqs, int H) {
 // state pass.  (Running the operand kernel of the next window concurrently on a
 // second stream was measured slower: both kernels then share the HBM bandwidth
 // that the tile round trip already saturates.)
-hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gate g,
+                                const float* beta, const int32_t* cu, int n_seqs,
                                 int64_t T, int H, int max_chunks, const float* s0,
                                 float* s_final, void* o, Snapshots snap, void* workspace,
                                 hipStream_t stream) {
@@ -254,7 +254,9 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, con
         const int w0 = w * win;
         const int rows = max_chunks - w0 < win ? max_chunks - w0 : win;
         if (rows > 0) {
-            hipLaunchKernelGGL(g_head ? prep_kernel<true> : prep_kernel<false>,
+            hipLaunchKernelGGL(g.mode == GATE_HEAD   ? prep_kernel<GATE_HEAD>
+                               : g.mode == GATE_PROJ ? prep_kernel<GATE_PROJ>
+                                                     : prep_kernel<GATE_CH>,
                                dim3((unsigned)n_pairs, (unsigned)rows), dim3(256), 0, stream,
                                (const bf16_t*)q, (const bf16_t*)k, g, beta, cu, T, H, w0, win,
                                tiles);

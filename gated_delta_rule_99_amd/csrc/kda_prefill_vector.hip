@@ -36,8 +36,8 @@ struct VecShape {
 template <int D, int C, typename Tin>
 __global__ void __launch_bounds__(256)
 prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
-                      const Tin* __restrict__ v, const float* __restrict__ g,
-                      const float* __restrict__ beta, int g_head, const int32_t* __restrict__ cu,
+                      const Tin* __restrict__ v, Gate gate,
+                      const float* __restrict__ beta, const int32_t* __restrict__ cu,
                       int64_t T, int H, const float* __restrict__ s0,
                       float* __restrict__ s_final, Tin* __restrict__ o, Snapshots snap) {
     using SH = VecShape<D, C>;
@@ -67,6 +67,8 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     }
 
     const size_t rowk = (size_t)H * D;  // stride between tokens in q/k/g/v/o
+    const float* g = static_cast<const float*>(gate.g);
+    const float rate = gate.mode == GATE_PROJ ? __expf(gate.a_log[h]) : 0.f;
     for (int64_t c0 = tb; c0 < te; c0 += C) {
         const int L = (int)((te - c0) < C ? (te - c0) : C);
         __syncthreads();  // previous chunk done with every buffer
@@ -77,7 +79,12 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
             if (t < L) {
                 const size_t off = (size_t)(c0 + t) * rowk + (size_t)h * D + i;
                 kv = In<Tin>::load1(k + off);
-                gv = g_head ? g[(size_t)(c0 + t) * H + h] : g[off];
+                gv = gate.mode == GATE_HEAD ? g[(size_t)(c0 + t) * H + h]
+                     : gate.mode == GATE_PROJ
+                         ? 0.6931471805599453f *
+                               proj_log2_decay(In<Tin>::load1(static_cast<const Tin*>(gate.g) + off),
+                                               rate)
+                         : g[off];
                 qv = In<Tin>::load1(q + off);
             }
             sKt[t * LD + i] = kv;
@@ -85,7 +92,9 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
             sQt[t * LD + i] = qv;
         }
         for (int t = tid; t < C; t += NT)
-            sBeta[t] = t < L ? beta[(size_t)(c0 + t) * H + h] : 0.f;
+            sBeta[t] = t >= L                    ? 0.f
+                       : gate.mode == GATE_PROJ ? sigmoid_f(beta[(size_t)(c0 + t) * H + h])
+                                                : beta[(size_t)(c0 + t) * H + h];
         __syncthreads();
         // cumulative decay per channel, scaled tiles
         if (tid < D) {
@@ -172,8 +181,8 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
 }
 
 template <int D, int C, typename Tin>
-static hipError_t launch_vec_t(const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, bool g_head, const int32_t* cu, int n_seqs,
+static hipError_t launch_vec_t(const void* q, const void* k, const void* v, Gate g,
+                               const float* beta, const int32_t* cu, int n_seqs,
                                int64_t T, int H, const float* s0, float* s_final, void* o,
                                Snapshots snap, hipStream_t stream) {
     using SH = VecShape<D, C>;
@@ -185,35 +194,35 @@ static hipError_t launch_vec_t(const void* q, const void* k, const void* v, cons
                                          (int)SH::BYTES);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(SH::NT), SH::BYTES, stream,
-                       (const Tin*)q, (const Tin*)k, (const Tin*)v, g, beta, (int)g_head, cu, T, H,
+                       (const Tin*)q, (const Tin*)k, (const Tin*)v, g, beta, cu, T, H,
                        s0, s_final, (Tin*)o, snap);
     return hipGetLastError();
 }
 
 template <int D, typename Tin>
 static hipError_t launch_vec_c(int chunk, const void* q, const void* k, const void* v,
-                               const float* g, const float* beta, bool g_head, const int32_t* cu,
+                               Gate g, const float* beta, const int32_t* cu,
                                int n_seqs, int64_t T, int H, const float* s0, float* s_final,
                                void* o, Snapshots snap, hipStream_t stream) {
     switch (chunk) {
-        case 16: return launch_vec_t<D, 16, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
-        case 32: return launch_vec_t<D, 32, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
-        case 64: return launch_vec_t<D, 64, Tin>(q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
+        case 16: return launch_vec_t<D, 16, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
+        case 32: return launch_vec_t<D, 32, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
+        case 64: return launch_vec_t<D, 64, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, const float* g,
-                                 const float* beta, kda_dtype dtype, bool g_head, const int32_t* cu,
+hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, Gate g,
+                                 const float* beta, kda_dtype dtype, const int32_t* cu,
                                  int n_seqs, int64_t T, int H, int d, int chunk,
                                  const float* s0, float* s_final, void* o, Snapshots snap,
                                  hipStream_t stream) {
 #define KDA_VEC(D)                                                                            \
     if (d == D) {                                                                             \
         if (dtype == KDA_BF16)                                                                \
-            return launch_vec_c<D, bf16_t>(chunk, q, k, v, g, beta, g_head, cu, n_seqs, T, H, \
+            return launch_vec_c<D, bf16_t>(chunk, q, k, v, g, beta, cu, n_seqs, T, H, \
                                            s0, s_final, o, snap, stream);                     \
-        return launch_vec_c<D, float>(chunk, q, k, v, g, beta, g_head, cu, n_seqs, T, H, s0,  \
+        return launch_vec_c<D, float>(chunk, q, k, v, g, beta, cu, n_seqs, T, H, s0,  \
                                       s_final, o, snap, stream);                              \
     }
     KDA_VEC(16)

@@ -57,11 +57,12 @@ struct TileSinks {
 };
 
 // beta of the chunk (wave 0 holds one token per lane).
+template <int GM>
 __device__ __forceinline__ void tile_beta(__amdgpu_buffer_rsrc_t rt, const ChunkIn& in, int p,
                                           int lane) {
     if (p == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(in.beta), rt, OFF_BETA + 4 * lane, 0,
-                                              0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(chunk_beta<GM>(in, lane)), rt,
+                                              OFF_BETA + 4 * lane, 0, 0);
 }
 
 // Kt and Qt fragments out of LDS (wave p exports row block p); after the decay

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
-KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
+KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_PROJ = 0, 1, 2
 
 
 class KdaError(RuntimeError):
@@ -38,14 +38,14 @@ _SIGNATURES = {
     "kda_last_error_detail": (ctypes.c_char_p, []),
     "kda_state_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
     "kda_state_init": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _i32, _vp]),
-    "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
-                                   _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+    "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32,
+                                   _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                                    ctypes.c_size_t, _vp]),
     "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _i64, _vp, _i32,
-                               _i32, _i32, _i32, _vp, _vp]),
-    "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _i64, _vp, _i32,
-                                 _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp,
+                               _i32, _i32, _i32, _i32, _vp, _vp]),
+    "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp,
+                                 _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "kda_short_conv_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp, _vp]),
     "kda_short_conv_decode": (_i32, [_vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _f32,
@@ -87,8 +87,13 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _gate_code(g, q) -> int:
-    """Per-channel log decay has q's shape; per-head decay drops the channel axis."""
+def _gate_code(g, q, a_log=None) -> int:
+    """Per-channel log decay has q's shape; per-head decay drops the channel axis.
+    With a_log, g is the decay projection (q's shape and dtype) and beta logits."""
+    if a_log is not None:
+        if g.shape != q.shape or g.dtype != q.dtype:
+            raise ValueError("with a_log, g is the decay projection: q's shape and dtype")
+        return KDA_GATE_PROJ
     if g.dim() == q.dim():
         return KDA_GATE_CHANNEL
     if g.dim() == q.dim() - 1:
@@ -170,9 +175,11 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
                         initial_state=None, final_state=None, o=None,
                         output_final_state: bool = True, cu_seqlens_host=None,
                         workspace="auto", snapshots=None, snap_interval: int = 0,
-                        stream=None):
+                        a_log=None, stream=None):
     """Chunked prefill over packed sequences.  q, k: [T, H, dk]; v: [T, H, dv];
     g: [T, H, dk] (per-channel decay) or [T, H] (per-head decay); beta: [T, H].
+    With a_log ([H] fp32), g is the decay projection f (q's dtype) and beta the
+    write-strength logits: log alpha = -exp(a_log) softplus(f), beta = sigmoid.
     Returns (o, final_state or None), or (o, final_state, snapshots) when
     snapshots is given.
 
@@ -204,8 +211,8 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
         workspace = _workspace(need, q.device) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kda_prefill_chunked(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
-        _ptr(cu_dev), cu_host.data_ptr(), n_seqs, H, dk, dv, int(chunk), _ptr(initial_state),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q),
+        _gate_code(g, q, a_log), _ptr(a_log), _ptr(cu_dev), cu_host.data_ptr(), n_seqs, H, dk, dv, int(chunk), _ptr(initial_state),
         _ptr(final_state), _ptr(o), _ptr(snapshots), int(snap_interval), snap_cap,
         _ptr(workspace), ws_bytes, _stream(stream)))
     if want_snaps:
@@ -213,23 +220,24 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     return o, final_state
 
 
-def kda_decode_step(q, k, v, g, beta, state, slot_idx=None, o=None, stream=None):
-    """One token per sequence.  q, k: [B, H, dk]; g: [B, H, dk] or [B, H];
-    v: [B, H, dv]; beta: [B, H];
+def kda_decode_step(q, k, v, g, beta, state, slot_idx=None, o=None, a_log=None, stream=None):
+    """One token per sequence.  q, k: [B, H, dk]; g: [B, H, dk] or [B, H] (or the
+    decay projection with a_log, as in kda_prefill_chunked); v: [B, H, dv]; beta: [B, H];
     state [n_slots, H, dk, dv] fp32 or bf16, updated in place.  Returns o [B, H, dv]."""
     B, H, dk = q.shape
     dv = v.shape[2]
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     _check(load().kda_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
-        _ptr(state), _state_code(state), state.shape[0], _ptr(slot_idx), B, H, dk, dv, _ptr(o),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q, a_log),
+        _ptr(a_log), _ptr(state), _state_code(state), state.shape[0], _ptr(slot_idx), B, H, dk,
+        dv, _ptr(o),
         _stream(stream)))
     return o
 
 
 def kda_decode_tokens(q, k, v, g, beta, state, slot_idx=None, o=None, token_states=None,
-                      stream=None):
+                      a_log=None, stream=None):
     """n_tok consecutive tokens per sequence.  q, k: [B, n_tok, H, dk]; g: the same
     shape or [B, n_tok, H]; v: [B, n_tok, H, dv]; beta: [B, n_tok, H]; state
     [n_slots, H, dk, dv] fp32 or bf16, updated in place.  token_states: None,
@@ -242,8 +250,9 @@ def kda_decode_tokens(q, k, v, g, beta, state, slot_idx=None, o=None, token_stat
     if token_states is True:
         token_states = torch.empty((B, n_tok, H, dk, dv), dtype=state.dtype, device=q.device)
     _check(load().kda_decode_tokens(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q),
-        _ptr(state), _state_code(state), state.shape[0], _ptr(slot_idx), B, n_tok, H, dk, dv,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q, a_log),
+        _ptr(a_log), _ptr(state), _state_code(state), state.shape[0], _ptr(slot_idx), B, n_tok,
+        H, dk, dv,
         _ptr(o), _ptr(token_states) if token_states is not None else None, _stream(stream)))
     return o, token_states
 

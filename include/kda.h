@@ -70,9 +70,25 @@ typedef enum kda_dtype {
  * need at 1M tokens?" (section "Why would a model keep only 9 full-attention
  * layers?") names as the layer KDA extends with finer-grained gating. */
 typedef enum kda_gate {
-    KDA_GATE_CHANNEL = 0, /* g [tokens, H, d_k]: alpha_t per key channel (KDA) */
-    KDA_GATE_HEAD = 1     /* g [tokens, H]: one alpha_t per head, all channels */
+    KDA_GATE_CHANNEL = 0, /* g [tokens, H, d_k] fp32: alpha_t per key channel (KDA) */
+    KDA_GATE_HEAD = 1,    /* g [tokens, H] fp32: one alpha_t per head, all channels */
+    KDA_GATE_PROJ = 2     /* gate prologue fused in: see below */
 } kda_gate;
+
+/* KDA_GATE_PROJ takes the decay and write strength before their activations,
+ * as the layer's projections produce them.  Page "Ling-3.1-flash: a 560B
+ * hybrid-attention MoE, counted from its safetensors headers" (section "How KDA
+ * and MLA split the work") names the tensors behind them, f_proj and A_log for
+ * the per-channel decay and b_proj for the per-head write strength, but not the
+ * formula; the library applies
+ *     g_t    = -exp(a_log[h]) * softplus(f_t)     (log alpha_t, per key channel)
+ *     beta_t = sigmoid(b_t)
+ * with softplus(x) = log(1 + exp(x)).  Then:
+ *   g     : f, [tokens, H, d_k] in the q/k/v dtype (half the bytes of an fp32
+ *           g for bf16 inputs);
+ *   a_log : [H] fp32, one log rate per head (a positive rate exp(a_log));
+ *   beta  : the logits b, [tokens, H] fp32.
+ * With the other gate layouts a_log must be NULL. */
 
 /* Text for a status code (static storage). */
 const char* kda_status_string(kda_status s);
@@ -104,9 +120,11 @@ kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, i
  * chunk tokens at a time (the chunked/WY form, exact up to rounding).
  *
  *   q, k            : [T, H, dk] dtype       v, o : [T, H, dv] dtype
- *   g               : [T, H, dk] fp32 (log decay; alpha = exp(g)), or [T, H]
- *                     with gate = KDA_GATE_HEAD
- *   beta            : [T, H] fp32
+ *   g               : [T, H, dk] fp32 (log decay; alpha = exp(g)), [T, H] fp32
+ *                     with gate = KDA_GATE_HEAD, or the decay projection
+ *                     [T, H, dk] in dtype with gate = KDA_GATE_PROJ
+ *   a_log           : [H] fp32 with KDA_GATE_PROJ, else NULL
+ *   beta            : [T, H] fp32 (logits with KDA_GATE_PROJ)
  *   cu_seqlens_dev  : [n_seqs + 1] int32 on the device
  *   cu_seqlens_host : the same values in host memory (validated: cu[0] = 0,
  *                     non-decreasing; T = cu[n_seqs]).  The kernels clamp
@@ -157,7 +175,8 @@ kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, i
  * kda_prefill_workspace_bytes or overlapping another argument.
  */
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
-                               const float* g, const float* beta, kda_dtype dtype, kda_gate gate,
+                               const void* g, const float* beta, kda_dtype dtype, kda_gate gate,
+                               const float* a_log,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
                                const float* initial_state, float* final_state, void* o,
@@ -180,7 +199,10 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
  * kda_decode_step -- advance B sequences by one token each, in place.
  *
  *   q, k     : [B, H, dk] dtype        v, o : [B, H, dv] dtype
- *   g        : [B, H, dk] fp32 ([B, H] with KDA_GATE_HEAD)    beta : [B, H] fp32
+ *   g        : [B, H, dk] fp32 ([B, H] fp32 with KDA_GATE_HEAD; the decay
+ *              projection [B, H, dk] in dtype with KDA_GATE_PROJ)
+ *   a_log    : [H] fp32 with KDA_GATE_PROJ, else NULL
+ *   beta     : [B, H] fp32 (logits with KDA_GATE_PROJ)
  *   state    : [n_slots, H, dk, dv] state_dtype, read and written in place.
  *   state_dtype : KDA_F32, or KDA_BF16 for half the state bytes: the state is
  *              widened to fp32 when read, stepped in fp32, and rounded to the
@@ -197,8 +219,9 @@ size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
  * Supported: dk == dv in {16, 32, 64, 128}.  Each state is read once and
  * written once (fused form of one recurrence step).
  */
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, kda_dtype dtype, kda_gate gate, void* state,
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g,
+                           const float* beta, kda_dtype dtype, kda_gate gate,
+                           const float* a_log, void* state,
                            kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
                            int B, int H, int dk, int dv, void* o, hipStream_t stream);
 
@@ -216,8 +239,11 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
  * sequence by the drafted tokens at once.
  *
  *   q, k         : [B, n_tok, H, dk] dtype    v, o : [B, n_tok, H, dv] dtype
- *   g            : [B, n_tok, H, dk] fp32 ([B, n_tok, H] with KDA_GATE_HEAD)
- *   beta         : [B, n_tok, H] fp32
+ *   g            : [B, n_tok, H, dk] fp32 ([B, n_tok, H] fp32 with
+ *                  KDA_GATE_HEAD; the decay projection [B, n_tok, H, dk] in
+ *                  dtype with KDA_GATE_PROJ)
+ *   a_log        : [H] fp32 with KDA_GATE_PROJ, else NULL
+ *   beta         : [B, n_tok, H] fp32 (logits with KDA_GATE_PROJ)
  *   state        : [n_slots, H, dk, dv] state_dtype, read and written in
  *                  place; on return it holds the state after the last token.
  *   state_dtype  : as in kda_decode_step (a bf16 state is rounded once, after
@@ -232,8 +258,9 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
  * Out-of-range slots leave every state untouched and set all n_tok outputs of
  * that sequence to NaN.
  */
-kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, kda_dtype dtype, kda_gate gate, void* state,
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const void* g,
+                             const float* beta, kda_dtype dtype, kda_gate gate,
+                             const float* a_log, void* state,
                              kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
                              int B, int n_tok, int H, int dk, int dv, void* o,
                              void* token_states, hipStream_t stream);

@@ -16,6 +16,10 @@ Contents
   out, for tiny inputs only.
 * ``round_bf16``    -- rounding to the nearest bfloat16 value (ties to even), the
   storage rounding of a state kept in bf16 (numpy, integer arithmetic).
+* ``gate_prologue`` -- the decay and write strength from the projections' raw
+  outputs (numpy fp64): g = -exp(a_log) softplus(f), beta = sigmoid(b).  The
+  same page names f_proj and A_log behind the per-channel decay and b_proj
+  behind beta but prints no formula; this is the reading the library adopts.
 
 Where each step comes from is stated in ``kda_oracle.c``'s header: page
 "Ling-3.1-flash: a 560B hybrid-attention MoE, counted from its safetensors
@@ -236,3 +240,27 @@ def round_bf16(x):
     bias = (np.uint64(1) << np.uint64(44)) - np.uint64(1) + keep_lsb
     out = ((bits + bias) >> drop) << drop
     return out.view(np.float64).reshape(a.shape)
+
+
+def gate_prologue(f, a_log, b):
+    """Decay and write strength from the projections' outputs, in fp64.
+
+    f: [..., H, d_k] decay projection; a_log: [H] log rate per head; b: [..., H]
+    write-strength logits.  Returns (g, beta) with
+        g    = -exp(a_log[h]) * softplus(f),  softplus(x) = log(1 + e^x),
+        beta = 1 / (1 + e^{-b}),
+    so alpha = exp(g) lies in (0, 1] and beta in (0, 1).  Page "Ling-3.1-flash:
+    a 560B hybrid-attention MoE, counted from its safetensors headers", section
+    "How KDA and MLA split the work", names the tensors (f_proj and A_log for the
+    per-channel decay, b_proj for beta, one per head) without the formula; this
+    is the plainest form in which a per-head log rate scales a per-channel
+    projection into a negative log decay.  softplus uses numpy's logaddexp(0, x),
+    exact for every finite x."""
+    f = np.asarray(f, dtype=np.float64)
+    a_log = np.asarray(a_log, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    rate = np.exp(a_log)[:, None]           # [H, 1], broadcast over d_k
+    g = -rate * np.logaddexp(0.0, f)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    return g, beta
+

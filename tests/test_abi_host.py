@@ -56,12 +56,12 @@ def cu_arr(vals):
 
 
 def prefill(lib, **kw):
-    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=0, cu_dev=Fp,
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=0, a_log=None, cu_dev=Fp,
              cu_host=cu_arr([0, 8]), n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, o=Gp,
              snaps=None, snap_interval=0, snap_capacity=0, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
-                                   a["gate"], a["cu_dev"], a["cu_host"], a["n"], a["H"], a["dk"],
+                                   a["gate"], a["a_log"], a["cu_dev"], a["cu_host"], a["n"], a["H"], a["dk"],
                                    a["dv"],
                                    a["chunk"], a["s0"], a["sf"], a["o"], a["snaps"],
                                    a["snap_interval"], a["snap_capacity"], a["ws"], a["ws_bytes"],
@@ -74,7 +74,11 @@ def prefill(lib, **kw):
     (dict(H=0), KDA_ERR_INVALID_ARGUMENT, "positive"),
     (dict(chunk=48), KDA_ERR_INVALID_ARGUMENT, "chunk"),
     (dict(dtype=7), KDA_ERR_INVALID_ARGUMENT, "dtype"),
-    (dict(gate=2), KDA_ERR_INVALID_ARGUMENT, "gate layout"),
+    (dict(gate=3), KDA_ERR_INVALID_ARGUMENT, "gate layout"),
+    (dict(gate=2), KDA_ERR_INVALID_ARGUMENT, "needs a_log"),
+    (dict(gate=2, a_log=Hp + 2), KDA_ERR_INVALID_ARGUMENT, "needs a_log"),
+    (dict(gate=0, a_log=Hp), KDA_ERR_INVALID_ARGUMENT, "only taken"),
+    (dict(gate=2, a_log=Gp + 64), KDA_ERR_INVALID_ARGUMENT, "o overlaps"),
     (dict(n=-1), KDA_ERR_INVALID_ARGUMENT, "n_seqs"),
     (dict(cu_host=None), KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host"),
     (dict(cu_host=cu_arr([1, 8])), KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0]"),
@@ -129,17 +133,20 @@ def test_prefill_nothing_to_do(lib):
 
 
 def decode(lib, **kw):
-    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_F32, gate=0, state=Fp, sdt=KDA_F32,
-             n_slots=4, slot=None, B=4, H=2, dk=64, dv=64, o=Gp, stream=None)
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_F32, gate=0, a_log=None, state=Fp,
+             sdt=KDA_F32, n_slots=4, slot=None, B=4, H=2, dk=64, dv=64, o=Gp, stream=None)
     a.update(kw)
     return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"], a["gate"],
-                               a["state"], a["sdt"], a["n_slots"], a["slot"], a["B"], a["H"],
+                               a["a_log"], a["state"], a["sdt"], a["n_slots"], a["slot"], a["B"], a["H"],
                                a["dk"], a["dv"], a["o"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(dk=48, dv=48), KDA_ERR_UNSUPPORTED, "head dim"),
     (dict(gate=-1), KDA_ERR_INVALID_ARGUMENT, "gate layout"),
+    (dict(gate=2), KDA_ERR_INVALID_ARGUMENT, "needs a_log"),
+    (dict(gate=1, a_log=Hp), KDA_ERR_INVALID_ARGUMENT, "only taken"),
+    (dict(gate=2, a_log=Fp + 256), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(B=-1), KDA_ERR_INVALID_ARGUMENT, ">= 0"),
     (dict(n_slots=3), KDA_ERR_INVALID_ARGUMENT, "n_slots"),
     (dict(state=None), KDA_ERR_INVALID_ARGUMENT, "required"),
@@ -157,12 +164,12 @@ def test_decode_rejects(lib, kw, status, needle):
 
 
 def decode_tokens(lib, **kw):
-    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=1, state=Fp, sdt=KDA_BF16,
-             n_slots=4, slot=None, B=4, n_tok=3, H=2, dk=128, dv=128, o=Gp, snaps=None,
-             stream=None)
+    a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=1, a_log=None, state=Fp,
+             sdt=KDA_BF16, n_slots=4, slot=None, B=4, n_tok=3, H=2, dk=128, dv=128, o=Gp,
+             snaps=None, stream=None)
     a.update(kw)
     return lib.kda_decode_tokens(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
-                                 a["gate"], a["state"], a["sdt"], a["n_slots"], a["slot"], a["B"],
+                                 a["gate"], a["a_log"], a["state"], a["sdt"], a["n_slots"], a["slot"], a["B"],
                                  a["n_tok"], a["H"], a["dk"], a["dv"], a["o"], a["snaps"],
                                  a["stream"])
 
@@ -174,6 +181,7 @@ def decode_tokens(lib, **kw):
     (dict(snaps=Fp + 4096), KDA_ERR_INVALID_ARGUMENT, "token_states overlaps"),
     (dict(dk=96, dv=96), KDA_ERR_UNSUPPORTED, "head dim"),
     (dict(n_slots=3), KDA_ERR_INVALID_ARGUMENT, "n_slots"),
+    (dict(gate=2, a_log=None), KDA_ERR_INVALID_ARGUMENT, "needs a_log"),
 ])
 def test_decode_tokens_rejects(lib, kw, status, needle):
     assert decode_tokens(lib, **kw) == status

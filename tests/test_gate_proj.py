@@ -1,0 +1,124 @@
+"""GPU parity of the fused gate prologue (gate layout KDA_GATE_PROJ) through the
+C ABI: the library takes the decay projection f (in the q/k/v dtype), one log
+rate a_log per head and the write-strength logits b, and forms
+g = -exp(a_log) softplus(f) and beta = sigmoid(b) inside its kernels.  The
+oracle applies oracle.gate_prologue to the same values (f widened from its
+stored dtype) and runs the recurrence on the result.
+
+Ragged lengths put padding rows in partial chunks: a padding row must keep
+alpha = 1 (not the softplus of a zero projection), which the final states
+check.  Tolerances as for the other parity tests."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, np64, oracle_on,
+                          per_seq_errors)
+
+pytestmark = pytest.mark.gpu
+
+
+def kda():
+    gpu_or_skip()
+    import gated_delta_rule_99_amd as m
+    m.load()
+    return m
+
+
+def case(lens, H, d, dtype, chunk, seed, a_log_std=0.5, s0_std=0.05, g_mu=2.0, g_sigma=0.5):
+    """(inputs with f in place of g and logits in place of beta, oracle inputs)."""
+    inp = workloads.recurrence_inputs(lens, H=H, d=d, dtype=dtype, chunk=chunk, s0_std=s0_std,
+                                      seed=seed)
+    pr = workloads.gate_projections(inp.T, H, d, dtype=dtype, g_mu=g_mu, g_sigma=g_sigma,
+                                    a_log_std=a_log_std, seed=seed)
+    g, beta = oracle.gate_prologue(np64(pr.f), np64(pr.a_log), np64(pr.b))
+    ref = workloads.RecurrenceInputs(inp.q, inp.k, inp.v, torch.from_numpy(g),
+                                     torch.from_numpy(beta), inp.cu_seqlens, inp.S0, dtype,
+                                     chunk)
+    return inp, pr, ref
+
+
+PREFILL_CASES = {
+    # name: (lens, H, d, dtype, chunk, workspace)
+    "split": ([1, 70, 0, 200], 4, 128, "bf16", 64, "auto"),
+    "fused": ([1, 70, 0, 200], 4, 128, "bf16", 64, None),
+    "vector-f32": ([5, 33, 0, 64], 3, 64, "f32", 32, None),
+    "vector-bf16": ([17, 2, 40], 2, 32, "bf16", 16, None),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_CASES))
+def test_prefill_gate_proj(name):
+    m = kda()
+    lens, H, d, dtype, chunk, ws = PREFILL_CASES[name]
+    inp, pr, ref = case(lens, H, d, dtype, chunk, seed=600 + len(name))
+    print(f"gate proj prefill {name}: lens {lens} H {H} d {d} {dtype} chunk {chunk}", flush=True)
+    o, S = m.kda_prefill_chunked(dev(inp.q), dev(inp.k), dev(inp.v), dev(pr.f), dev(pr.b),
+                                 cu_seqlens=dev(inp.cu_seqlens), cu_seqlens_host=inp.cu_seqlens,
+                                 chunk=chunk, initial_state=dev(inp.S0), workspace=ws,
+                                 a_log=dev(pr.a_log))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_on(ref)
+    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    print(f"  o {eo:.2e} S {es:.2e}")
+    assert eo <= tol and es <= tol
+
+
+def test_prefill_gate_proj_ling_layer():
+    """The Ling-shaped layer (B=1, H=64, T=8192, d=128, chunk 64, bf16) with the
+    prologue fused, in the two-kernel launch configuration the benchmark times;
+    with a_log = 0 and f = -N(3, 1) the decay has the layer's own distribution.
+    Every head is checked."""
+    m = kda()
+    inp, pr, ref = case([8192], 64, 128, "bf16", 64, seed=1002, a_log_std=0.0, s0_std=0.0,
+                        g_mu=3.0, g_sigma=1.0)
+    o, S = m.kda_prefill_chunked(dev(inp.q), dev(inp.k), dev(inp.v), dev(pr.f), dev(pr.b),
+                                 cu_seqlens=dev(inp.cu_seqlens), cu_seqlens_host=inp.cu_seqlens,
+                                 chunk=64, a_log=dev(pr.a_log))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_on(ref)
+    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
+    print(f"gate proj ling layer: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("dtype,d,n_tok", [("bf16", 128, 1), ("f32", 64, 4)])
+def test_decode_gate_proj(dtype, d, n_tok):
+    """n_tok tokens per sequence in one call through a slot permutation."""
+    m = kda()
+    B, H, n_slots = 5, 3, 8
+    inp, pr, ref = case([n_tok] * B, H, d, dtype, 64, seed=620 + d + n_tok)
+    pool = torch.zeros((n_slots, H, d, d))
+    slots = torch.tensor([6, 1, 3, 0, 7], dtype=torch.int32)
+    pool[slots.long()] = inp.S0
+    state = dev(pool)
+    t = lambda x: dev(x.reshape((B, n_tok) + tuple(x.shape[1:])))
+    if n_tok == 1:
+        o = m.kda_decode_step(dev(inp.q), dev(inp.k), dev(inp.v), dev(pr.f), dev(pr.b), state,
+                              slot_idx=dev(slots), a_log=dev(pr.a_log))
+        o = o.reshape(B, H, d)
+    else:
+        o, _ = m.kda_decode_tokens(t(inp.q), t(inp.k), t(inp.v), t(pr.f), t(pr.b), state,
+                                   slot_idx=dev(slots), a_log=dev(pr.a_log))
+        o = o.reshape(B * n_tok, H, d)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_on(ref)
+    S_gpu = np64(state)[slots.long().numpy()]
+    eo, es = per_seq_errors(np64(o), o_ref, S_gpu, S_ref, inp.cu_seqlens)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    print(f"gate proj decode {dtype} d={d} n_tok={n_tok}: o {eo:.2e} S {es:.2e}")
+    assert eo <= tol and es <= tol
+    untouched = [s for s in range(n_slots) if s not in slots.tolist()]
+    assert not state[untouched].abs().sum().item()
+
+
+def test_gate_proj_rejects_mismatched_projection():
+    """The binding takes the projection in q's shape and dtype only."""
+    m = kda()
+    q = torch.zeros((4, 2, 64), device="cuda")
+    with pytest.raises(ValueError):
+        m.kda_prefill_chunked(q, q, q, q.to(torch.bfloat16), torch.zeros((4, 2), device="cuda"),
+                              a_log=torch.zeros(2, device="cuda"))

@@ -80,3 +80,41 @@ def test_conv_tail_size_matches_pages():
         gold["conv_tail_bytes_per_element"]
     total = per_layer * gold["kda_layers"]
     assert round(total / 1e6) == gold["conv_tail_MB_printed"]
+
+
+# ---- gate prologue (decay and write strength from the projections' outputs)
+def test_gate_prologue_unit_rate_is_logsigmoid():
+    """With a_log = 0 (rate 1) the decay is alpha = sigmoid(-f), i.e. g equals
+    torch's logsigmoid(-f), an independent implementation; beta equals
+    torch.sigmoid(b)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    f = rng.standard_normal((50, 3, 8)) * 6
+    b = rng.standard_normal((50, 3)) * 6
+    g, beta = oracle.gate_prologue(f, np.zeros(3), b)
+    want_g = torch.nn.functional.logsigmoid(-torch.from_numpy(f)).numpy()
+    assert np.allclose(g, want_g, rtol=1e-13, atol=1e-300)
+    assert np.allclose(beta, torch.sigmoid(torch.from_numpy(b)).numpy(), rtol=1e-14)
+
+
+def test_gate_prologue_closed_forms():
+    """f = 0 gives g = -exp(a_log) ln 2 per head (heads on the second-to-last
+    axis, channels on the last); the decay scales linearly with the rate
+    exp(a_log); far tails follow softplus's asymptotes; alpha lies in (0, 1]."""
+    a_log = np.array([0.0, np.log(3.0), -1.5])
+    g0, beta0 = oracle.gate_prologue(np.zeros((2, 3, 5)), a_log, np.zeros((2, 3)))
+    assert np.allclose(g0, -np.exp(a_log)[None, :, None] * np.log(2.0) * np.ones((2, 3, 5)),
+                       rtol=1e-15)
+    assert np.all(beta0 == 0.5)
+    rng = np.random.default_rng(22)
+    f = rng.standard_normal((4, 3, 5))
+    g_unit, _ = oracle.gate_prologue(f, np.zeros(3), np.zeros((4, 3)))
+    g_rate, _ = oracle.gate_prologue(f, a_log, np.zeros((4, 3)))
+    assert np.allclose(g_rate, g_unit * np.exp(a_log)[None, :, None], rtol=1e-14)
+    lo, _ = oracle.gate_prologue(np.full((1, 1, 1), -40.0), np.zeros(1), np.zeros((1, 1)))
+    hi, _ = oracle.gate_prologue(np.full((1, 1, 1), 40.0), np.zeros(1), np.zeros((1, 1)))
+    assert abs(lo[0, 0, 0] / -np.exp(-40.0) - 1) < 1e-12
+    assert abs(hi[0, 0, 0] / -40.0 - 1) < 1e-15
+    alpha = np.exp(oracle.gate_prologue(rng.standard_normal((9, 3, 5)) * 20, a_log,
+                                        np.zeros((9, 3)))[0])
+    assert np.all((alpha > 0) & (alpha <= 1))

@@ -37,7 +37,7 @@ _BLOCK = 1 << 22
 
 # tensor ids: the order in which a workload's tensors are drawn
 TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "S0": 5, "conv_w": 6,
-       "x_q": 7, "x_k": 8, "x_v": 9}
+       "x_q": 7, "x_k": 8, "x_v": 9, "f": 10, "a_log": 11, "b": 12}
 
 
 def _threads() -> int:
@@ -201,6 +201,26 @@ def packed_long(lengths=PACKED_LENGTHS):
     seeded nonzero initial states N(0, 0.02)."""
     return recurrence_inputs(list(lengths), H=64, d=128, dtype="bf16", chunk=64, g_mu=2.0,
                              g_sigma=0.5, s0_std=0.02, seed=1004)
+
+
+@dataclasses.dataclass
+class GateProjections:
+    """Raw inputs of the fused gate prologue (CPU tensors)."""
+    f: torch.Tensor       # [T, H, dk] dtype: decay projection
+    a_log: torch.Tensor   # [H] fp32: log rate per head
+    b: torch.Tensor       # [T, H] fp32: write-strength logits
+
+
+def gate_projections(T, H, d, dtype="bf16", g_mu=2.0, g_sigma=0.5, a_log_std=0.0,
+                     seed=0) -> GateProjections:
+    """f = -N(g_mu, g_sigma) rounded to dtype, b = N(0, 1), a_log = N(0, a_log_std)
+    per head (zeros for a_log_std = 0).  With a_log = 0 the decay sigmoid(-f) and
+    the strength sigmoid(b) follow the per-channel recipe of recurrence_inputs."""
+    f = to_dtype(-normal((T, H, d), seed, TID["f"], g_mu, g_sigma), dtype)
+    a_log = (normal((H,), seed, TID["a_log"], 0.0, a_log_std) if a_log_std > 0
+             else torch.zeros(H))
+    b = normal((T, H), seed, TID["b"])
+    return GateProjections(f, a_log, b)
 
 
 def mixer_conv_streams(t_prefill=32768, seed=1005):
