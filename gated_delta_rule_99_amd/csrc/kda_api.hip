@@ -237,14 +237,9 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     const kda::Gate gt = make_gate(g, a_log, gate);
     hipError_t err;
     if (mfma && workspace) {
-        int max_chunks = 0;
-        for (int n = 0; n < n_seqs; ++n) {
-            const int nc = (int)(((int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n] + 63) / 64);
-            max_chunks = nc > max_chunks ? nc : max_chunks;
-        }
-        err = kda::launch_prefill_split(q, k, v, gt, beta, cu_seqlens_dev,
-                                        n_seqs, T, H, max_chunks, initial_state, final_state, o,
-                                        snap, workspace, stream);
+        err = kda::launch_prefill_split(q, k, v, gt, beta, cu_seqlens_dev, cu_seqlens_host,
+                                        n_seqs, T, H, initial_state, final_state, o, snap,
+                                        workspace, stream);
     } else if (mfma)
         err = kda::launch_prefill_fused(q, k, v, gt, beta, cu_seqlens_dev,
                                         n_seqs, T, H, initial_state, final_state, o, snap, stream);

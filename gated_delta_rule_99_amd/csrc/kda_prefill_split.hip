@@ -10,9 +10,15 @@
 // head, chunk) by prep_kernel, chunk-parallel, and stored in a workspace as
 // operand tiles (layout in kda_state_pass.h).  state_kernel then runs the
 // serial chain per (sequence, head, 32-column slice), streaming those
-// fragments.  The sequence is processed in windows of up to 32 chunks (prep
+// fragments.  The sequences are processed in windows of up to 32 chunks (prep
 // for the window, then the state pass over it), which bounds the workspace;
-// the fp32 state is carried between windows in the workspace.
+// the fp32 state is carried between windows in the workspace.  Only the
+// sequences still running in a window take part in it: they are ranked by
+// length, longest first, so that those of window w are the first A_w ranks,
+// and the window's length is what the tile budget allows for A_w of them.
+#include <algorithm>
+#include <vector>
+
 #include "kda_state_pass.h"
 
 namespace kda {
@@ -22,23 +28,26 @@ using namespace co;
 
 constexpr int MAX_WIN = 32;                 // chunks per window, at most
 constexpr size_t TILE_BUDGET = 192u << 20;  // bytes of one window's tiles, at most
+constexpr int RANK_MAX = 4096;              // sequences ranked by length, at most
 
 }  // namespace sp
 
 using namespace sp;
 
 // ---------------------------------------------------------------- prep
-// grid (n_seqs * H, chunks in the window): one workgroup of 4 waves per
-// (sequence, head, window chunk) runs the operand stages and exports the tile.
+// grid (active sequences * H, chunks in the window): one workgroup of 4 waves
+// per (sequence rank, head, window chunk) runs the operand stages and exports
+// the tile.  order[rank] is the sequence.
 // GM: the decay inputs' GateMode (per channel, per head, or the projection).
 template <int GM>
 __global__ void __launch_bounds__(256, 2)
 prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
             const float* __restrict__ beta,
-            const int32_t* __restrict__ cu, int64_t T, int H, int w0, int win,
-            uint8_t* __restrict__ ws_tiles) {
+            const int32_t* __restrict__ cu, const int32_t* __restrict__ order, int64_t T, int H,
+            int w0, int win, uint8_t* __restrict__ ws_tiles) {
     __shared__ __attribute__((aligned(16))) ChunkLds sm;
-    const int pair = blockIdx.x, cl = blockIdx.y, n = pair / H, h = pair - n * H;
+    const int slot = blockIdx.x / H, h = blockIdx.x - slot * H, cl = blockIdx.y;
+    const int n = order[slot];
     int64_t tb, te;
     int nc;
     seq_chunks(cu, n, T, tb, te, nc);
@@ -47,7 +56,7 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
     const int tid = threadIdx.x, p = tid >> 6, lane = tid & 63;
     const int64_t c0 = tb + (int64_t)c * C;
     const int L = (te - c0) < C ? (int)(te - c0) : C;
-    const auto rt = window(ws_tiles + ((size_t)(n * win + cl) * H + h) * TILE, TILE);
+    const auto rt = window(ws_tiles + ((size_t)(slot * win + cl) * H + h) * TILE, TILE);
 
     zero_tp(sm, tid, 256);
     ChunkIn in;
@@ -64,29 +73,32 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
 }
 
 // ---------------------------------------------------------------- state pass
-// grid n_seqs * H * NS (the slices of one head placed on one XCD); 8 waves, the
-// roles and barriers of the state pass pieces in kda_state_pass.h.  Fragments
-// come straight from the tiles into registers, two chunks ahead (three register
-// sets in rotation), spread over the step's segments.
+// grid n_pairs * NS, n_pairs = (ranked sequences in the window) * H, the slices
+// of one head placed on one XCD; 8 waves, the roles and barriers of the state
+// pass pieces in kda_state_pass.h.  Fragments come straight from the tiles into
+// registers, two chunks ahead (three register sets in rotation), spread over
+// the step's segments.
 __global__ void __launch_bounds__(512)
-state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64_t T, int H,
+state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
+             const int32_t* __restrict__ order, int64_t T, int H,
              int n_pairs, int w0, int win, const uint8_t* __restrict__ ws_tiles,
              float* __restrict__ ws_state, const float* __restrict__ s0,
              float* __restrict__ s_final, bf16_t* __restrict__ o, Snapshots snap) {
     __shared__ __attribute__((aligned(16))) StateLds sm;
-    int pair, slice;
+    int rp, slice;  // (rank, head) pair and slice
     {
         const int b = blockIdx.x;
         if ((n_pairs & 7) == 0) {
             const int xcd = b & 7, kx = b >> 3;
-            pair = (kx / NS) * 8 + xcd;
+            rp = (kx / NS) * 8 + xcd;
             slice = kx % NS;
         } else {
-            pair = b / NS;
+            rp = b / NS;
             slice = b % NS;
         }
     }
-    const int n = pair / H, h = pair - n * H;
+    const int slot = rp / H, h = rp - slot * H;
+    const int n = order[slot], pair = n * H + h;
     const int j0 = slice * DVS;
     int64_t tb, te;
     int nc;
@@ -124,7 +136,7 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
     };
     auto tile_rsrc = [&](int c) {
         const int cc = c < c_end ? c : c_beg;  // keep the address inside the workspace
-        return window(ws_tiles + ((size_t)(n * win + (cc - w0)) * H + h) * TILE,
+        return window(ws_tiles + ((size_t)(slot * win + (cc - w0)) * H + h) * TILE,
                       c < c_end ? TILE : 0);
     };
     // this lane's (row, column) of the chunk in the accumulator layout, as a
@@ -223,16 +235,40 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu, int64
     }
 }
 
-int prefill_split_window(int n_seqs, int H) {
-    const size_t per_chunk = (size_t)n_seqs * H * TILE;
-    const size_t w = TILE_BUDGET / per_chunk;
-    return w < 1 ? 1 : (w > (size_t)MAX_WIN ? MAX_WIN : (int)w);
+// Rank of every sequence by chunk count, longest first (ties by index):
+// order[rank] = sequence.  One thread per sequence; with rank_them false (too
+// many sequences to rank by comparison) the order is the identity.
+__global__ void __launch_bounds__(256)
+seq_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int64_t T, int rank_them,
+                 int32_t* __restrict__ order) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= n_seqs) return;
+    if (!rank_them) {
+        order[n] = n;
+        return;
+    }
+    int64_t b, e;
+    int nc;
+    seq_chunks(cu, n, T, b, e, nc);
+    int rank = 0;
+    for (int m = 0; m < n_seqs; ++m) {
+        int mc;
+        seq_chunks(cu, m, T, b, e, mc);
+        rank += (mc > nc) || (mc == nc && m < n);
+    }
+    order[rank] = n;
 }
 
-// State carry, then the tiles of one window.
+// Workspace: the fp32 state carry, the rank table, then the tiles of one
+// window (at most TILE_BUDGET bytes, at least one chunk of every sequence).
+static size_t order_bytes(int n_seqs) { return ((size_t)n_seqs * 4 + 255) & ~(size_t)255; }
+static size_t tile_bytes(int n_seqs, int H) {
+    const size_t one = (size_t)n_seqs * H * TILE;
+    const size_t most = one * MAX_WIN < TILE_BUDGET ? one * MAX_WIN : TILE_BUDGET;
+    return most > one ? most : one;
+}
 size_t prefill_split_workspace_bytes(int n_seqs, int H) {
-    return (size_t)n_seqs * H * D * D * 4 +
-           (size_t)n_seqs * prefill_split_window(n_seqs, H) * H * TILE;
+    return (size_t)n_seqs * H * D * D * 4 + order_bytes(n_seqs) + tile_bytes(n_seqs, H);
 }
 
 // Windows run one after the other on the caller's stream: operand kernel, then
@@ -240,35 +276,53 @@ size_t prefill_split_workspace_bytes(int n_seqs, int H) {
 // second stream was measured slower: both kernels then share the HBM bandwidth
 // that the tile round trip already saturates.)
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gate g,
-                                const float* beta, const int32_t* cu, int n_seqs,
-                                int64_t T, int H, int max_chunks, const float* s0,
-                                float* s_final, void* o, Snapshots snap, void* workspace,
-                                hipStream_t stream) {
-    const int64_t n_pairs = (int64_t)n_seqs * H;
-    if (n_pairs == 0) return hipSuccess;
-    const int win = prefill_split_window(n_seqs, H);
+                                const float* beta, const int32_t* cu, const int32_t* cu_host,
+                                int n_seqs, int64_t T, int H, const float* s0, float* s_final,
+                                void* o, Snapshots snap, void* workspace, hipStream_t stream) {
+    if ((int64_t)n_seqs * H == 0) return hipSuccess;
+    // chunk counts, longest first: the ranks' lengths
+    std::vector<int> len(n_seqs);
+    for (int n = 0; n < n_seqs; ++n) len[n] = (int)(((int64_t)cu_host[n + 1] - cu_host[n] + C - 1) / C);
+    std::sort(len.begin(), len.end(), [](int a, int b) { return a > b; });
+    const int max_chunks = len[0];
     float* ws_state = reinterpret_cast<float*>(workspace);
-    uint8_t* tiles = reinterpret_cast<uint8_t*>(workspace) + (size_t)n_pairs * D * D * 4;
-    const int n_win = max_chunks > 0 ? (max_chunks + win - 1) / win : 1;
-    for (int w = 0; w < n_win; ++w) {
-        const int w0 = w * win;
+    int32_t* order = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) +
+                                                (size_t)n_seqs * H * D * D * 4);
+    uint8_t* tiles = reinterpret_cast<uint8_t*>(order) + order_bytes(n_seqs);
+    const size_t tbytes = tile_bytes(n_seqs, H);
+    const bool ranked = n_seqs <= RANK_MAX;
+    hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((n_seqs + 255) / 256)), dim3(256), 0,
+                       stream, cu, n_seqs, T, (int)ranked, order);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    auto prep = g.mode == GATE_HEAD   ? prep_kernel<GATE_HEAD>
+                : g.mode == GATE_PROJ ? prep_kernel<GATE_PROJ>
+                                      : prep_kernel<GATE_CH>;
+    int w0 = 0;
+    do {
+        // ranks still running at chunk w0; the first window also visits the
+        // empty sequences, whose final states are their initial ones
+        int active = 0;
+        while (active < n_seqs && len[active] > w0) ++active;
+        if (!ranked) active = n_seqs;  // identity order: every sequence takes part
+        const int visit = w0 == 0 ? n_seqs : active;
+        size_t w = active ? tbytes / ((size_t)active * H * TILE) : 1;
+        const int win = w < 1 ? 1 : (w > (size_t)MAX_WIN ? MAX_WIN : (int)w);
         const int rows = max_chunks - w0 < win ? max_chunks - w0 : win;
-        if (rows > 0) {
-            hipLaunchKernelGGL(g.mode == GATE_HEAD   ? prep_kernel<GATE_HEAD>
-                               : g.mode == GATE_PROJ ? prep_kernel<GATE_PROJ>
-                                                     : prep_kernel<GATE_CH>,
-                               dim3((unsigned)n_pairs, (unsigned)rows), dim3(256), 0, stream,
-                               (const bf16_t*)q, (const bf16_t*)k, g, beta, cu, T, H, w0, win,
-                               tiles);
-            hipError_t err = hipGetLastError();
+        if (rows > 0 && active > 0) {
+            hipLaunchKernelGGL(prep, dim3((unsigned)(active * H), (unsigned)rows), dim3(256), 0,
+                               stream, (const bf16_t*)q, (const bf16_t*)k, g, beta, cu, order, T,
+                               H, w0, win, tiles);
+            err = hipGetLastError();
             if (err != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(state_kernel, dim3((unsigned)(n_pairs * NS)), dim3(512), 0, stream,
-                           (const bf16_t*)v, cu, T, H, (int)n_pairs, w0, win, tiles, ws_state, s0,
-                           s_final, (bf16_t*)o, snap);
-        hipError_t err = hipGetLastError();
+        hipLaunchKernelGGL(state_kernel, dim3((unsigned)((int64_t)visit * H * NS)), dim3(512), 0,
+                           stream, (const bf16_t*)v, cu, order, T, H, visit * H, w0, win, tiles,
+                           ws_state, s0, s_final, (bf16_t*)o, snap);
+        err = hipGetLastError();
         if (err != hipSuccess) return err;
-    }
+        w0 += win;
+    } while (w0 < max_chunks);
     return hipSuccess;
 }
 

@@ -187,10 +187,13 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
  * kda_prefill_workspace_bytes -- size of the workspace that lets
  * kda_prefill_chunked use its two-kernel matrix-core path for this shape; 0 when
  * the shape runs a path that needs none.  Depends only on n_seqs and H for the
- * matrix-core shapes: a state carry (64 KiB per sequence and head) plus the
- * per-chunk operand tiles (66 304 bytes per chunk and head) of a window of at
- * most 32 chunks per sequence, sized to about 192 MiB where the batch allows
- * (at least one chunk per sequence and head).
+ * matrix-core shapes: a state carry (64 KiB per sequence and head), a table of
+ * the sequences ranked by length (4 bytes per sequence, rounded up to 256),
+ * and the per-chunk operand tiles (66 304 bytes per chunk and head) of one
+ * window: 192 MiB, or 32 chunks of every sequence if that is less, and at least
+ * one chunk of every sequence.  The sequences still running at a window's
+ * start share its tiles, so windows grow as shorter sequences end (up to 32
+ * chunks).
  */
 size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,
                                    kda_dtype dtype);

@@ -111,15 +111,16 @@ def test_prefill_rejects(lib, kw, status, needle):
 
 
 def test_prefill_workspace_bytes(lib):
-    """State carry (64 KiB per sequence and head) plus a window of 66 304-byte
-    chunk tiles; 0 for shapes that run without a workspace."""
+    """State carry (64 KiB per sequence and head), the rank table (4 bytes per
+    sequence, rounded up to 256) and a window of 66 304-byte chunk tiles; 0 for
+    shapes that run without a workspace."""
     f = lib.kda_prefill_workspace_bytes
-    # one sequence, 64 heads: a full 32-chunk window fits the 192 MiB budget
-    assert f(1, 64, 128, 128, 64, KDA_BF16) == 64 * 65536 + 32 * 64 * 66304
-    # four sequences, 64 heads: 11 chunks per window
-    assert f(4, 64, 128, 128, 64, KDA_BF16) == 4 * 64 * 65536 + 4 * 11 * 64 * 66304
+    # one sequence, 64 heads: a full 32-chunk window is below the 192 MiB budget
+    assert f(1, 64, 128, 128, 64, KDA_BF16) == 64 * 65536 + 256 + 32 * 64 * 66304
+    # four sequences, 64 heads: the 192 MiB budget
+    assert f(4, 64, 128, 128, 64, KDA_BF16) == 4 * 64 * 65536 + 256 + (192 << 20)
     # large batches keep one chunk per sequence and head
-    assert f(256, 64, 128, 128, 64, KDA_BF16) == 256 * 64 * (65536 + 66304)
+    assert f(256, 64, 128, 128, 64, KDA_BF16) == 256 * 64 * (65536 + 66304) + 1024
     assert f(1, 64, 128, 128, 64, KDA_F32) == 0
     assert f(1, 64, 64, 64, 64, KDA_BF16) == 0
     assert f(1, 64, 128, 128, 32, KDA_BF16) == 0

@@ -105,6 +105,27 @@ def test_config_packed_long():
     assert eo <= TOL_BF16 and es <= TOL_BF16 and e_early <= TOL_BF16
 
 
+def test_ragged_batch_growing_windows():
+    """Six sequences of different lengths (one empty, one shorter than a chunk)
+    at H=64, nonzero initial states, two-kernel path: the windows start at 7
+    chunks for six running sequences and grow to 32 as the shorter ones end.
+    Every sequence's outputs and final state on four sampled heads, and the
+    empty sequence's final state equal to its initial one."""
+    kda()
+    lens = [64 * 40, 64 * 3 + 5, 0, 64 * 70 + 1, 17, 64 * 33]
+    inp = workloads.recurrence_inputs(lens, H=64, d=128, dtype="bf16", chunk=64, s0_std=0.05,
+                                      seed=1010)
+    o, S = gpu_prefill(inp)
+    heads = [0, 17, 40, 63]
+    o_s, S_s = np64(o[:, heads]), np64(S[:, heads])
+    assert torch.equal(S[2].cpu(), inp.S0[2])
+    del o, S
+    o_ref, S_ref = oracle_on(inp, heads=heads)
+    eo, es = per_seq_errors(o_s, o_ref, S_s, S_ref, inp.cu_seqlens)
+    print(f"ragged batch, growing windows: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
 MIXER_HEADS = (0, 31, 63)
 
 
