@@ -37,7 +37,7 @@ using namespace sp;
 // ---------------------------------------------------------------- prep
 // grid (active sequences * H, chunks in the window): one workgroup of 4 waves
 // per (sequence rank, head, window chunk) runs the operand stages and exports
-// the tile.  order[rank] is the sequence.
+// the tile.  order[rank] is the sequence (order NULL: rank = sequence).
 // GM: the decay inputs' GateMode (per channel, per head, or the projection).
 template <int GM>
 __global__ void __launch_bounds__(256, 2)
@@ -47,7 +47,7 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
             int w0, int win, uint8_t* __restrict__ ws_tiles) {
     __shared__ __attribute__((aligned(16))) ChunkLds sm;
     const int slot = blockIdx.x / H, h = blockIdx.x - slot * H, cl = blockIdx.y;
-    const int n = order[slot];
+    const int n = order ? order[slot] : slot;
     int64_t tb, te;
     int nc;
     seq_chunks(cu, n, T, tb, te, nc);
@@ -98,7 +98,7 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
         }
     }
     const int slot = rp / H, h = rp - slot * H;
-    const int n = order[slot], pair = n * H + h;
+    const int n = order ? order[slot] : slot, pair = n * H + h;
     const int j0 = slice * DVS;
     int64_t tb, te;
     int nc;
@@ -236,17 +236,12 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
 }
 
 // Rank of every sequence by chunk count, longest first (ties by index):
-// order[rank] = sequence.  One thread per sequence; with rank_them false (too
-// many sequences to rank by comparison) the order is the identity.
+// order[rank] = sequence.  One thread per sequence.
 __global__ void __launch_bounds__(256)
-seq_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int64_t T, int rank_them,
+seq_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int64_t T,
                  int32_t* __restrict__ order) {
     const int n = blockIdx.x * 256 + threadIdx.x;
     if (n >= n_seqs) return;
-    if (!rank_them) {
-        order[n] = n;
-        return;
-    }
     int64_t b, e;
     int nc;
     seq_chunks(cu, n, T, b, e, nc);
@@ -291,10 +286,19 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gat
     uint8_t* tiles = reinterpret_cast<uint8_t*>(order) + order_bytes(n_seqs);
     const size_t tbytes = tile_bytes(n_seqs, H);
     const bool ranked = n_seqs <= RANK_MAX;
-    hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((n_seqs + 255) / 256)), dim3(256), 0,
-                       stream, cu, n_seqs, T, (int)ranked, order);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    // no table when the ranking is the identity (lengths already non-increasing)
+    bool identity = true;
+    for (int n = 0; n + 1 < n_seqs && identity; ++n)
+        identity = (cu_host[n + 1] - cu_host[n] + C - 1) / C >= (cu_host[n + 2] - cu_host[n + 1] + C - 1) / C;
+    hipError_t err = hipSuccess;
+    if (ranked && !identity) {
+        hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((n_seqs + 255) / 256)), dim3(256), 0,
+                           stream, cu, n_seqs, T, order);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    } else {
+        order = nullptr;
+    }
     auto prep = g.mode == GATE_HEAD   ? prep_kernel<GATE_HEAD>
                 : g.mode == GATE_PROJ ? prep_kernel<GATE_PROJ>
                                       : prep_kernel<GATE_CH>;
