@@ -203,6 +203,25 @@ struct Vec16<float> {
     }
 };
 
+// x moved between lanes by a DPP pattern within each row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of gl lanes (gl a power of two, at most 64), every
+// lane receiving its group's sum: quad swaps, then the half-row and row
+// mirrors pair quads and half-rows; across rows, lane shuffles.
+__device__ __forceinline__ float group_sum(float x, int gl) {
+    if (gl >= 2) x += dpp_f<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    if (gl >= 4) x += dpp_f<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    if (gl >= 8) x += dpp_f<0x141>(x);  // row_half_mirror
+    if (gl >= 16) x += dpp_f<0x140>(x); // row_mirror
+    if (gl >= 32) x += __shfl_xor(x, 16);
+    if (gl >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
 // grid: (ceil(T / run), ceil(channels / (256 VC))); block: 256 threads.
 // gl: lanes per normalised head (0: no normalisation).  run: tokens per
 // workgroup (longer runs re-read the 3-token history less often).
@@ -276,7 +295,7 @@ conv_prefill_wide_kernel(const Tin* __restrict__ x, const float* __restrict__ w,
             ss += yv[u] * yv[u];
         }
         if (gl) {
-            for (int off = gl >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+            ss = group_sum(ss, gl);
             const float scale = rsqrtf(ss + eps);
 #pragma unroll
             for (int u = 0; u < VC; ++u) yv[u] *= scale;
@@ -324,12 +343,14 @@ static hipError_t conv_prefill_t(const void* x, const float* w, const int32_t* c
     const bool wide = channels % VC == 0 &&
                       (l2_head_dim == 0 || (l2_head_dim % VC == 0 && gl <= 64 && !(gl & (gl - 1))));
     if (T > 0 && n_seqs > 0 && wide) {
-        // the longest run (fewest history re-reads) that still gives >= 1024
-        // workgroups; measured on 32768 x 8192 bf16: runs of 16, 64, 128, 256
-        // tokens took 0.30, 0.26, 0.255, 0.38 ms
+        // the longest run (fewest history re-reads) that still gives >= 768
+        // workgroups, three per CU; measured on 8192 channels of bf16 (L2 norm):
+        // T = 32768 with runs of 16, 64, 128, 256 tokens took 0.30, 0.26, 0.255,
+        // 0.38 ms; T = 24576 with runs of 64 and 128, 0.204 and 0.185 ms; T =
+        // 8192 with runs of 32 and 64, 0.057 and 0.064 ms
         const int64_t cblocks = (channels + 256 * VC - 1) / (256 * VC);
         int run = 128;
-        while (run > 16 && ((T + run - 1) / run) * cblocks < 1024) run >>= 1;
+        while (run > 16 && ((T + run - 1) / run) * cblocks < 768) run >>= 1;
         const int64_t runs = (T + run - 1) / run;
         const dim3 grid((unsigned)runs, (unsigned)cblocks);
         hipLaunchKernelGGL((conv_prefill_wide_kernel<Tin>), grid, dim3(256), 0, stream,
