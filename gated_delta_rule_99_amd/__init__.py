@@ -15,6 +15,7 @@ from .kda import (  # noqa: F401
     kda_decode_tokens,
     kda_prefill_chunked,
     kda_prefill_workspace_bytes,
+    kda_prefill_workspace_bytes_batch,
     kda_short_conv_decode,
     kda_short_conv_prefill,
     kda_state_bytes,

@@ -225,12 +225,12 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                         workspace_bytes, ws_need);
         if (!aligned16(workspace))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned workspace", fn);
-        if (overlaps(workspace, ws_need, q, n_qk * es) || overlaps(workspace, ws_need, k, n_qk * es) ||
-            overlaps(workspace, ws_need, v, n_qk * es) || overlaps(workspace, ws_need, g, gb) ||
-            overlaps(workspace, ws_need, a_log, ab) ||
-            overlaps(workspace, ws_need, beta, n_bt * 4) || overlaps(workspace, ws_need, o, n_qk * es) ||
-            overlaps(workspace, ws_need, initial_state, sbytes) ||
-            overlaps(workspace, ws_need, final_state, sbytes))
+        if (overlaps(workspace, workspace_bytes, q, n_qk * es) || overlaps(workspace, workspace_bytes, k, n_qk * es) ||
+            overlaps(workspace, workspace_bytes, v, n_qk * es) || overlaps(workspace, workspace_bytes, g, gb) ||
+            overlaps(workspace, workspace_bytes, a_log, ab) ||
+            overlaps(workspace, workspace_bytes, beta, n_bt * 4) || overlaps(workspace, workspace_bytes, o, n_qk * es) ||
+            overlaps(workspace, workspace_bytes, initial_state, sbytes) ||
+            overlaps(workspace, workspace_bytes, final_state, sbytes))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps another argument", fn);
     }
 
@@ -239,7 +239,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     if (mfma && workspace) {
         err = kda::launch_prefill_split(q, k, v, gt, beta, cu_seqlens_dev, cu_seqlens_host,
                                         n_seqs, T, H, initial_state, final_state, o, snap,
-                                        workspace, stream);
+                                        workspace, workspace_bytes, stream);
     } else if (mfma)
         err = kda::launch_prefill_fused(q, k, v, gt, beta, cu_seqlens_dev,
                                         n_seqs, T, H, initial_state, final_state, o, snap, stream);
@@ -247,6 +247,15 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
         err = kda::launch_prefill_vector(q, k, v, gt, beta, dtype, cu_seqlens_dev, n_seqs, T, H, d, chunk, initial_state,
                                          final_state, o, snap, stream);
     return hip_status(err, "kda_prefill_chunked launch");
+}
+
+size_t kda_prefill_workspace_bytes_batch(const int32_t* cu_seqlens_host, int n_seqs, int H,
+                                         int dk, int dv, int chunk, kda_dtype dtype) {
+    if (n_seqs <= 0 || H <= 0 || !mfma_shape(dtype, dk, dv, chunk)) return 0;
+    int64_t T = 0;
+    if (!cu_seqlens_host || check_cu("kda_prefill_workspace_bytes_batch", cu_seqlens_host, n_seqs, &T))
+        return kda::prefill_split_workspace_bytes(n_seqs, H);
+    return kda::prefill_split_workspace_bytes_batch(cu_seqlens_host, n_seqs, H);
 }
 
 size_t kda_prefill_workspace_bytes(int n_seqs, int H, int dk, int dv, int chunk,

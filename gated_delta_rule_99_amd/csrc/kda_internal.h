@@ -156,10 +156,12 @@ hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, Gat
 // prefill_split_workspace_bytes(n_seqs, H) bytes; cu_host: the validated host
 // copy of cu_seqlens (for the window plan).
 size_t prefill_split_workspace_bytes(int n_seqs, int H);
+size_t prefill_split_workspace_bytes_batch(const int32_t* cu_host, int n_seqs, int H);
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gate gate,
                                 const float* beta, const int32_t* cu, const int32_t* cu_host,
                                 int n_seqs, int64_t T, int H, const float* s0, float* s_final,
-                                void* o, Snapshots snap, void* workspace, hipStream_t stream);
+                                void* o, Snapshots snap, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 hipError_t launch_short_conv_prefill(const void* x, const float* w, kda_dtype dtype,
                                      const int32_t* cu, int n_seqs, int64_t T, int channels,

@@ -42,6 +42,8 @@ _SIGNATURES = {
                                    _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                                    ctypes.c_size_t, _vp]),
     "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "kda_prefill_workspace_bytes_batch": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32, _i32,
+                                                            _i32]),
     "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp,
                                _i32, _i32, _i32, _i32, _vp, _vp]),
     "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp,
@@ -157,6 +159,16 @@ def kda_prefill_workspace_bytes(n_seqs: int, H: int, dk: int, dv: int, chunk: in
     return int(load().kda_prefill_workspace_bytes(n_seqs, H, dk, dv, chunk, code))
 
 
+def kda_prefill_workspace_bytes_batch(cu_seqlens_host, H: int, dk: int, dv: int, chunk: int,
+                                      dtype: torch.dtype) -> int:
+    """Workspace for the longest windows of this batch (cu_seqlens_host: int32
+    CPU tensor)."""
+    cu = cu_seqlens_host.to(torch.int32).contiguous()
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_prefill_workspace_bytes_batch(cu.data_ptr(), cu.numel() - 1, H, dk, dv,
+                                                        chunk, code))
+
+
 _ws_cache: dict = {}
 
 
@@ -183,7 +195,7 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     Returns (o, final_state or None), or (o, final_state, snapshots) when
     snapshots is given.
 
-    workspace: "auto" (a cached device buffer of kda_prefill_workspace_bytes),
+    workspace: "auto" (a cached device buffer of kda_prefill_workspace_bytes_batch),
     a uint8 device tensor, or None (no workspace: the fused kernel).
     snapshots: None, True (allocate [n_seqs, longest // snap_interval, H, dk, dv]
     fp32 zeros) or such a tensor; entry [n, j] receives sequence n's state after
@@ -207,7 +219,7 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', a tensor or None")
-        need = kda_prefill_workspace_bytes(n_seqs, H, dk, dv, chunk, q.dtype)
+        need = kda_prefill_workspace_bytes_batch(cu_host, H, dk, dv, chunk, q.dtype)
         workspace = _workspace(need, q.device) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kda_prefill_chunked(

@@ -127,6 +127,31 @@ def test_prefill_workspace_bytes(lib):
     assert f(0, 64, 128, 128, 64, KDA_BF16) == 0
 
 
+def test_prefill_workspace_bytes_batch(lib):
+    """Windows of min(32, longest) chunks of every sequence while those tiles
+    stay within 4 GiB; never below the minimum; the minimum for an invalid
+    cu_seqlens_host; 0 for shapes without a workspace."""
+    f = lib.kda_prefill_workspace_bytes_batch
+    fixed = lambda n: n * 64 * 65536 + ((n * 4 + 255) // 256) * 256
+    # 64 sequences of 8 chunks: all 8 chunks of each
+    cu = cu_arr([512 * i for i in range(65)])
+    assert f(cu, 64, 64, 128, 128, 64, KDA_BF16) == fixed(64) + 8 * 64 * 64 * 66304
+    # 24 sequences of 2048 tokens: 32-chunk windows (3.26 GB of tiles)
+    cu = cu_arr([2048 * i for i in range(25)])
+    assert f(cu, 24, 64, 128, 128, 64, KDA_BF16) == fixed(24) + 32 * 24 * 64 * 66304
+    # 256 sequences of 4096 tokens: capped at 4 GiB of tiles (3 chunks)
+    cu = cu_arr([4096 * i for i in range(257)])
+    assert f(cu, 256, 64, 128, 128, 64, KDA_BF16) == fixed(256) + 3 * 256 * 64 * 66304
+    # one short sequence: the minimum (the 192 MiB budget's 32-chunk window)
+    cu = cu_arr([0, 100])
+    assert f(cu, 1, 64, 128, 128, 64, KDA_BF16) == \
+        lib.kda_prefill_workspace_bytes(1, 64, 128, 128, 64, KDA_BF16)
+    bad = cu_arr([0, 8, 4])
+    assert f(bad, 2, 64, 128, 128, 64, KDA_BF16) == \
+        lib.kda_prefill_workspace_bytes(2, 64, 128, 128, 64, KDA_BF16)
+    assert f(cu_arr([0, 100]), 1, 64, 64, 64, 64, KDA_BF16) == 0
+
+
 def test_prefill_nothing_to_do(lib):
     """n_seqs = 0 is valid and enqueues nothing."""
     assert prefill(lib, n=0, cu_host=cu_arr([0]), q=None, k=None, v=None, g=None, beta=None,

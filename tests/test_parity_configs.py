@@ -107,15 +107,17 @@ def test_config_packed_long():
 
 def test_ragged_batch_growing_windows():
     """Six sequences of different lengths (one empty, one shorter than a chunk)
-    at H=64, nonzero initial states, two-kernel path: the windows start at 7
-    chunks for six running sequences and grow to 32 as the shorter ones end.
-    Every sequence's outputs and final state on four sampled heads, and the
-    empty sequence's final state equal to its initial one."""
-    kda()
+    at H=64, nonzero initial states, two-kernel path with the minimum workspace:
+    the windows start at 7 chunks for six running sequences and grow to 32 as
+    the shorter ones end.  Every sequence's outputs and final state on four
+    sampled heads, and the empty sequence's final state equal to its initial
+    one."""
+    m = kda()
     lens = [64 * 40, 64 * 3 + 5, 0, 64 * 70 + 1, 17, 64 * 33]
     inp = workloads.recurrence_inputs(lens, H=64, d=128, dtype="bf16", chunk=64, s0_std=0.05,
                                       seed=1010)
-    o, S = gpu_prefill(inp)
+    need = m.kda_prefill_workspace_bytes(len(lens), 64, 128, 128, 64, torch.bfloat16)
+    o, S = gpu_prefill(inp, workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
     heads = [0, 17, 40, 63]
     o_s, S_s = np64(o[:, heads]), np64(S[:, heads])
     assert torch.equal(S[2].cpu(), inp.S0[2])
@@ -123,6 +125,27 @@ def test_ragged_batch_growing_windows():
     o_ref, S_ref = oracle_on(inp, heads=heads)
     eo, es = per_seq_errors(o_s, o_ref, S_s, S_ref, inp.cu_seqlens)
     print(f"ragged batch, growing windows: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_batch_with_long_windows():
+    """24 sequences of 2048 tokens at H=64 through the binding's default
+    workspace, which holds all 32 chunks of every sequence in one window; the
+    same batch with the minimum workspace (windows of 1 chunk) gives the same
+    result up to rounding.  Four sampled heads against the oracle."""
+    m = kda()
+    inp = workloads.recurrence_inputs([2048] * 24, H=64, d=128, dtype="bf16", chunk=64,
+                                      s0_std=0.05, seed=1011)
+    o, S = gpu_prefill(inp)
+    need = m.kda_prefill_workspace_bytes(24, 64, 128, 128, 64, torch.bfloat16)
+    o1, S1 = gpu_prefill(inp, workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    heads = [3, 30, 47, 60]
+    o_s, S_s = np64(o[:, heads]), np64(S[:, heads])
+    assert rel_fro(np64(o1[:, heads]), o_s) <= 1e-2
+    del o, S, o1, S1
+    o_ref, S_ref = oracle_on(inp, heads=heads)
+    eo, es = per_seq_errors(o_s, o_ref, S_s, S_ref, inp.cu_seqlens)
+    print(f"batch of 24 x 2048, 32-chunk windows: o {eo:.2e} S {es:.2e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
