@@ -252,9 +252,10 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
 size_t kda_prefill_workspace_bytes_batch(const int32_t* cu_seqlens_host, int n_seqs, int H,
                                          int dk, int dv, int chunk, kda_dtype dtype) {
     if (n_seqs <= 0 || H <= 0 || !mfma_shape(dtype, dk, dv, chunk)) return 0;
-    int64_t T = 0;
-    if (!cu_seqlens_host || check_cu("kda_prefill_workspace_bytes_batch", cu_seqlens_host, n_seqs, &T))
-        return kda::prefill_split_workspace_bytes(n_seqs, H);
+    // a query: an invalid table gets the minimum, and no error detail is set
+    bool valid = cu_seqlens_host && cu_seqlens_host[0] == 0;
+    for (int n = 0; valid && n < n_seqs; ++n) valid = cu_seqlens_host[n + 1] >= cu_seqlens_host[n];
+    if (!valid) return kda::prefill_split_workspace_bytes(n_seqs, H);
     return kda::prefill_split_workspace_bytes_batch(cu_seqlens_host, n_seqs, H);
 }
 
