@@ -72,6 +72,21 @@ def measured_traffic(kernel):
             rec["write_kib"] * 1024 * rec["write_scale"])
 
 
+def measured_mfma_busy(kernel):
+    """Share of SIMD cycles the matrix cores were busy over the kernel's
+    dispatches (SQ_VALU_MFMA_BUSY_CYCLES over SQ_BUSY_CU_CYCLES x 4 SIMDs) from
+    the committed counter record; None if absent or taken on other source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    m = rec.get("mfma")
+    if m is None or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return m["mfma_busy_cycles"] / (m["sq_busy_cu_cycles"] * m["simds_per_cu"])
+
+
 def prefill_algorithmic(T, H, d, chunk, with_s0, with_sfinal, g_bytes=4):
     """Algorithmic HBM bytes and flops of one prefill launch (bf16 q/k/v/o, fp32
     g/beta/state).  Bytes per token-head: q, k, v 3*2d, g 4d (2d for the bf16
@@ -261,6 +276,7 @@ def main():
                      "frac": alg_flops / (kern_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                      "attainable_frac": min(1.0, (alg_flops / alg_bytes) * HBM_PEAK_GBS * 1e9 /
                                             (BF16_MFMA_PEAK_TFLOPS * 1e12)),
+                     "rocprof_busy_frac": measured_mfma_busy(PREFILL_KERNEL),
                      "algorithmic_flops": alg_flops},
         })
         del q, k, v, g, beta, o, state
