@@ -192,6 +192,7 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
     __shared__ float s_qk[NWAVE];
     __shared__ float s_qkp[D];  // q_i * k_i (only summed directly when NT < 64)
     __shared__ __attribute__((aligned(16))) float s_part[2][RG][D];  // per-row-group partial sums
+    __shared__ __attribute__((aligned(16))) float s_y[2][D];         // full column sums
 
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;           // b * H + h
@@ -276,23 +277,46 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
         }
         __syncthreads();
 
-        // 4. full column sums, write value and output
+        // 4. full column sums, adding the row groups in order (the same order
+        // either way, so one call over n_tok tokens equals n_tok single steps)
         float Yk[VEC], Yq[VEC];
+        if constexpr (MULTI) {
+            // once per column: thread t sums one column of Y_k (t < D) or Y_q,
+            // then every thread reads its own columns (per token, 1/RG of the
+            // LDS reads of each thread summing its own columns, for one more
+            // barrier: faster from two tokens up, slower for one)
+            for (int idx = tid; idx < 2 * D; idx += NT) {
+                const int which = idx >= D, col = idx - which * D;
+                float acc = s_part[which][0][col];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            Yk[e] = s_part[0][0][c0 + e];
-            Yq[e] = s_part[1][0][c0 + e];
-        }
-        // the partial sums of the other row groups; a bounded unroll keeps the
-        // LDS reads in flight (registers) in check for 16 row groups
-        constexpr int RU = (VEC == 4 && !MULTI) ? RG : 4;
-#pragma unroll RU
-        for (int r = 1; r < RG; ++r)
+                for (int r = 1; r < RG; ++r) acc += s_part[which][r][col];
+                s_y[which][col] = acc;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                const float4 a = *reinterpret_cast<const float4*>(&s_y[0][c0 + e]);
+                const float4 c = *reinterpret_cast<const float4*>(&s_y[1][c0 + e]);
+                Yk[e] = a.x; Yk[e + 1] = a.y; Yk[e + 2] = a.z; Yk[e + 3] = a.w;
+                Yq[e] = c.x; Yq[e + 1] = c.y; Yq[e + 2] = c.z; Yq[e + 3] = c.w;
+            }
+        } else {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                Yk[e] += s_part[0][r][c0 + e];
-                Yq[e] += s_part[1][r][c0 + e];
+                Yk[e] = s_part[0][0][c0 + e];
+                Yq[e] = s_part[1][0][c0 + e];
             }
+            // the partial sums of the other row groups; a bounded unroll keeps
+            // the LDS reads in flight (registers) in check for 16 row groups
+            constexpr int RU = VEC == 4 ? RG : 4;
+#pragma unroll RU
+            for (int r = 1; r < RG; ++r)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    Yk[e] += s_part[0][r][c0 + e];
+                    Yq[e] += s_part[1][r][c0 + e];
+                }
+        }
         float qk = 0.f;
         if constexpr (NT % 64 == 0) {
 #pragma unroll
