@@ -256,7 +256,8 @@ seq_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int64_t T,
 }
 
 // Workspace: the fp32 state carry, the rank table, then the tiles of one
-// window (at most TILE_BUDGET bytes, at least one chunk of every sequence).
+// window.  The minimum holds TILE_BUDGET bytes of tiles, or MAX_WIN chunks of
+// every sequence if that is less, and at least one chunk of every sequence.
 static size_t order_bytes(int n_seqs) { return ((size_t)n_seqs * 4 + 255) & ~(size_t)255; }
 static size_t tile_bytes(int n_seqs, int H) {
     const size_t one = (size_t)n_seqs * H * TILE;
@@ -288,8 +289,9 @@ size_t prefill_split_workspace_bytes_batch(const int32_t* cu_host, int n_seqs, i
 
 // Windows run one after the other on the caller's stream: operand kernel, then
 // state pass.  (Running the operand kernel of the next window concurrently on a
-// second stream was measured slower: both kernels then share the HBM bandwidth
-// that the tile round trip already saturates.)
+// second stream was measured slower: a state-pass workgroup takes its CU's
+// whole register file, so the two kernels cannot share a CU, and both stream
+// the tiles through HBM.)
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gate g,
                                 const float* beta, const int32_t* cu, const int32_t* cu_host,
                                 int n_seqs, int64_t T, int H, const float* s0, float* s_final,
