@@ -134,14 +134,25 @@ hipError_t launch_state_init(void* state, kda_dtype state_dtype, int64_t n_elems
 //   CG = D/VEC column groups (VEC consecutive value columns per thread and row,
 //   one 16-byte access: VEC = 4 for fp32 states, 8 for bf16 states of D >= 64),
 //   RG row groups; thread (rg, cg) owns rows rg, rg+RG, rg+2RG, ... (RPT rows).
-// For D = 128: 256 threads holding 64 state elements each; the 64 lanes of a
-// wave read 1 KiB of consecutive rows per load instruction.
-template <int D, int VEC>
+// The 64 lanes of a wave read 1 KiB of consecutive rows per load instruction.
+// For D = 128:
+//   fp32 state, one token per call: 1024 threads of 16 elements each, compiled
+//     for at least 8 waves per SIMD (at most 64 VGPRs), so two workgroups share
+//     a CU.  Measured at 256 sequences x 64 heads: 0.334 ms per step against
+//     0.385 ms for 256 threads of 64 elements; 6 or 12 waves per SIMD, and 512
+//     threads, were 0.36-0.38 ms.
+//   fp32 state, several tokens: 256 threads of 64 elements (1024 threads were
+//     0.63 ms against 0.41 ms for four tokens: the per-token reductions and
+//     barriers then span 16 waves).
+//   bf16 state: 256 threads of 64 elements (512 threads were slower).
+template <int D, int VEC, bool MULTI>
 struct DecodeShape {
     static constexpr int CG = D / VEC;
-    static constexpr int RG = VEC == 4 ? (CG < 8 ? CG : 8) : (2 * CG < 16 ? 2 * CG : 16);
+    static constexpr int RG = VEC == 4 ? (CG < 8 ? CG : (CG == 32 && !MULTI ? 32 : 8))
+                                       : (2 * CG < 16 ? 2 * CG : 16);
     static constexpr int NT = CG * RG;
     static constexpr int RPT = D / RG;
+    static constexpr int MIN_WAVES = NT == 1024 ? 8 : 1;  // per SIMD
 };
 template <int D, typename TS>
 constexpr int decode_vec() { return sizeof(TS) == 2 && D >= 64 ? 8 : 4; }
@@ -174,14 +185,15 @@ __device__ __forceinline__ void in_store(Tin* p, const float (&x)[VEC]) {
 // and beta holds logits (GATE_PROJ); otherwise g is fp32, per key channel or,
 // with g_head, per head.
 template <int D, typename Tin, typename TS, bool MULTI, bool PROJ>
-__global__ void __launch_bounds__((DecodeShape<D, decode_vec<D, TS>()>::NT))
+__global__ void __launch_bounds__((DecodeShape<D, decode_vec<D, TS>(), MULTI>::NT),
+                                  (DecodeShape<D, decode_vec<D, TS>(), MULTI>::MIN_WAVES))
 decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ a_log,
               const float* __restrict__ beta, int g_head, TS* __restrict__ state, int64_t n_slots,
               const int32_t* __restrict__ slot_idx, int H, int n_tok,
               TS* __restrict__ token_states, Tin* __restrict__ o) {
     constexpr int VEC = decode_vec<D, TS>();
-    using S = DecodeShape<D, VEC>;
+    using S = DecodeShape<D, VEC, MULTI>;
     constexpr int NT = S::NT, CG = S::CG, RG = S::RG, RPT = S::RPT;
     constexpr int NWAVE = (NT + 63) / 64;
 
@@ -277,8 +289,10 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
         }
         __syncthreads();
 
-        // 4. full column sums, adding the row groups in order (the same order
-        // either way, so one call over n_tok tokens equals n_tok single steps)
+        // 4. full column sums, adding the row groups in order.  Where both
+        // kernels use the same row groups (bf16 states; D < 128), one call over
+        // n_tok tokens equals n_tok single steps bit for bit; for fp32 states of
+        // D = 128 the single-token kernel's 32 row groups regroup the sum.
         float Yk[VEC], Yq[VEC];
         if constexpr (MULTI) {
             // once per column: thread t sums one column of Y_k (t < D) or Y_q,
@@ -364,7 +378,9 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, G
                                   : decode_kernel<D, Tin, TS, true, false>)
                           : (proj ? decode_kernel<D, Tin, TS, false, true>
                                   : decode_kernel<D, Tin, TS, false, false>);
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(DecodeShape<D, decode_vec<D, TS>()>::NT),
+    constexpr int VEC = decode_vec<D, TS>();
+    const int nt = n_tok > 1 ? DecodeShape<D, VEC, true>::NT : DecodeShape<D, VEC, false>::NT;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(nt),
                        0, stream, (const Tin*)q, (const Tin*)k, (const Tin*)v,
                        static_cast<const float*>(g.g), g.a_log, beta, (int)(g.mode == GATE_HEAD),
                        (TS*)state, n_slots, slot_idx, H, n_tok, (TS*)token_states,
