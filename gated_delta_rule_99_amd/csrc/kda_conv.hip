@@ -170,36 +170,52 @@ conv_prefill_kernel(const Tin* __restrict__ x, const float* __restrict__ w,
 // shape allows it; the kernel above covers the rest.
 template <typename Tin>
 struct Vec16;
+// 16 bytes with the non-temporal hint: x and y stream through once.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t load16_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ void store16_nt(void* p, u32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 template <>
 struct Vec16<bf16_t> {
     static constexpr int VC = 8;
-    static __device__ __forceinline__ void load(const bf16_t* p, float (&x)[8]) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    static __device__ __forceinline__ void unpack(u32x4_t v, float (&x)[8]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[2 * e] = bf16_bits_to_f32(u[e] & 0xffffu);
-            x[2 * e + 1] = bf16_bits_to_f32(u[e] >> 16);
+            x[2 * e] = bf16_bits_to_f32(v[e] & 0xffffu);
+            x[2 * e + 1] = bf16_bits_to_f32(v[e] >> 16);
         }
     }
+    static __device__ __forceinline__ void load(const bf16_t* p, float (&x)[8]) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        unpack(u32x4_t{v.x, v.y, v.z, v.w}, x);
+    }
     static __device__ __forceinline__ void store(bf16_t* p, const float (&x)[8]) {
-        uint32_t u[4];
+        u32x4_t u;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             u[e] = (uint32_t)f32_to_bf16_bits(x[2 * e]) |
                    ((uint32_t)f32_to_bf16_bits(x[2 * e + 1]) << 16);
-        *reinterpret_cast<uint4*>(p) = make_uint4(u[0], u[1], u[2], u[3]);
+        store16_nt(p, u);
     }
 };
 template <>
 struct Vec16<float> {
     static constexpr int VC = 4;
+    static __device__ __forceinline__ void unpack(u32x4_t v, float (&x)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(v[e]);
+    }
     static __device__ __forceinline__ void load(const float* p, float (&x)[4]) {
         const float4 v = *reinterpret_cast<const float4*>(p);
         x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
     }
     static __device__ __forceinline__ void store(float* p, const float (&x)[4]) {
-        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+        store16_nt(p, u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]),
+                              __float_as_uint(x[2]), __float_as_uint(x[3])});
     }
 };
 
@@ -270,21 +286,9 @@ conv_prefill_wide_kernel(const Tin* __restrict__ x, const float* __restrict__ w,
     hist(t_begin - 3, h1);
     hist(t_begin - 2, h2);
     hist(t_begin - 1, h3);
-#pragma unroll 4
-    for (int64_t t = t_begin; t < t_end; ++t) {
-        if (t >= s_next) {  // a new sequence starts here: reload the window from its tail
-            while (n + 1 < n_seqs && (int64_t)cu[n + 1] <= t) ++n;
-            s_start = cu[n];
-            s_next = cu[n + 1];
-            hist(t - 3, h1);
-            hist(t - 2, h2);
-            hist(t - 1, h3);
-        }
-        float xv[VC], yv[VC];
-        if (act) Vec16<Tin>::load(x + (size_t)t * channels + ci, xv);
-        else
-#pragma unroll
-            for (int u = 0; u < VC; ++u) xv[u] = 0.f;
+    // one token: conv, optional L2 norm, store y[t]
+    auto step = [&](float (&xv)[VC], int64_t t) {
+        float yv[VC];
         float ss = 0.f;
 #pragma unroll
         for (int u = 0; u < VC; ++u) {
@@ -301,6 +305,46 @@ conv_prefill_wide_kernel(const Tin* __restrict__ x, const float* __restrict__ w,
             for (int u = 0; u < VC; ++u) yv[u] *= scale;
         }
         if (act) Vec16<Tin>::store(y + (size_t)t * channels + ci, yv);
+    };
+    // Blocks of TB tokens inside one sequence load their TB rows of x first
+    // (non-temporal), then run the steps; a block that would cross the run's
+    // end or a sequence start goes token by token.  The test is uniform over
+    // the workgroup, so the group sums' lanes stay together.  Measured on
+    // 3 x 32768 x 8192 bf16: 0.649 -> 0.615 ms (blocks of 8: 0.624; blocks
+    // without the hints: 0.637).
+    constexpr int TB = 4;
+    int64_t t = t_begin;
+    while (t < t_end) {
+        if (t + TB <= t_end && t + TB <= s_next) {
+            u32x4_t raw[TB];
+#pragma unroll
+            for (int j = 0; j < TB; ++j)
+                raw[j] = act ? load16_nt(x + (size_t)(t + j) * channels + ci)
+                             : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                float xv[VC];
+                Vec16<Tin>::unpack(raw[j], xv);
+                step(xv, t + j);
+            }
+            t += TB;
+            continue;
+        }
+        if (t >= s_next) {  // a new sequence starts here: reload the window from its tail
+            while (n + 1 < n_seqs && (int64_t)cu[n + 1] <= t) ++n;
+            s_start = cu[n];
+            s_next = cu[n + 1];
+            hist(t - 3, h1);
+            hist(t - 2, h2);
+            hist(t - 1, h3);
+        }
+        float xv[VC];
+        if (act) Vec16<Tin>::load(x + (size_t)t * channels + ci, xv);
+        else
+#pragma unroll
+            for (int u = 0; u < VC; ++u) xv[u] = 0.f;
+        step(xv, t);
+        ++t;
     }
 }
 
