@@ -166,8 +166,8 @@ __device__ __forceinline__ float chunk_beta(const ChunkIn& in, int lane) {
 // Kt, Qt, Kb (rows into LDS) and beta into LDS.  Hands Gam[ch0 + e] (lanes with
 // tg == 0) to gam_sink(ch0, gam4) and, for every lane, the Kb^T piece of channel
 // ch0 + e, tokens [8tg, 8tg + 8) as 8 packed bf16 to kbt_sink(i, tg, u32x4).
-template <int GM, typename GamSink, typename KbtSink>
-__device__ __forceinline__ void decay_stage(ChunkLds& sm, const ChunkIn& in, int p, int lane,
+template <int GM, typename L, typename GamSink, typename KbtSink>
+__device__ __forceinline__ void decay_stage(L& sm, const ChunkIn& in, int p, int lane,
                                             GamSink gam_sink, KbtSink kbt_sink) {
     const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
     if (p == 0) sm.beta[lane] = chunk_beta<GM>(in, lane);
@@ -255,7 +255,21 @@ __device__ __forceinline__ void decay_stage(ChunkLds& sm, const ChunkIn& in, int
 // N in both layouts and T's diagonal block by the nilpotent product
 // (I - N)(I + N^2)(I + N^4)(I + N^8) (a product and its transpose are one MFMA
 // with the operands swapped); off-diagonal blocks of N go to Tt's lower part.
-__device__ __forceinline__ void n_stage(ChunkLds& sm, int p, int lane) {
+// n_regs forms wave p's blocks in registers (reading Kt, Kb and beta), n_store
+// writes them to T and Tt.
+struct NRegs {
+    f32x4 Ta, Tb;   // T's diagonal block p, A and B layouts
+    f32x4 off[2];   // off-diagonal N blocks of wave p (n_off(p) of them)
+};
+__device__ __forceinline__ int n_off(int p) { return p < 2 ? 2 : 1; }
+// off-diagonal N block k of wave p: (1,0) (2,0) | (2,1) (3,0) | (3,1) | (3,2)
+__device__ __forceinline__ void n_off_block(int p, int k, int& rb, int& cb) {
+    rb = p == 0 ? 1 + k : p == 1 ? 2 + k : 3;
+    cb = p == 0 ? 0 : p == 1 ? 1 - k : p - 1;
+}
+
+template <typename L>
+__device__ __forceinline__ void n_regs(const L& sm, int p, int lane, NRegs& nr) {
     const int r = lane & 15, q4 = lane >> 4;
     f32x4 acc1 = Z4, acc2 = Z4;
 #pragma unroll
@@ -288,83 +302,117 @@ __device__ __forceinline__ void n_stage(ChunkLds& sm, int p, int lane) {
     const s16x4 x1a = cvt4(X1a);
     const f32x4 X2b = mma16(x1a, n4b, X1b), X2a = mma16(n4b, x1a, X1a);
     const s16x4 n8b = cvt4(N8b), x2a = cvt4(X2a);
-    const f32x4 Tb = mma16(x2a, n8b, X2b), Ta = mma16(n8b, x2a, X2a);
-    st4(sm.T + (16 * p + r) * LDT + 16 * p + 4 * q4, Ta);
-    st4(sm.Tt + (16 * p + r) * LDT + 16 * p + 4 * q4, Tb);
-    auto offdiag = [&](int rb, int cb) {  // N block (rb, cb), row-major, in Tt's lower part
-        f32x4 acc = Z4;
+    nr.Tb = mma16(x2a, n8b, X2b);
+    nr.Ta = mma16(n8b, x2a, X2a);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (k >= n_off(p)) break;
+        int rb, cb;
+        n_off_block(p, k, rb, cb);
+        f32x4 acc = Z4;  // N block (rb, cb), row-major
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             acc = mma32(ld8(sm.Kb + (16 * cb + r) * LDK + 32 * kk + 8 * q4),
                         ld8(sm.Kt + (16 * rb + r) * LDK + 32 * kk + 8 * q4), acc);
         const float bt = sm.beta[16 * rb + r];
         acc[0] *= bt; acc[1] *= bt; acc[2] *= bt; acc[3] *= bt;
-        st4(sm.Tt + (16 * rb + r) * LDT + 16 * cb + 4 * q4, acc);
-    };
-    if (p == 0) { offdiag(1, 0); offdiag(2, 0); }
-    else if (p == 1) { offdiag(2, 1); offdiag(3, 0); }
-    else if (p == 2) { offdiag(3, 1); }
-    else { offdiag(3, 2); }
+        nr.off[k] = acc;
+    }
+}
+
+template <typename L>
+__device__ __forceinline__ void n_store(L& sm, int p, int lane, const NRegs& nr) {
+    const int r = lane & 15, q4 = lane >> 4;
+    st4(sm.T + (16 * p + r) * LDT + 16 * p + 4 * q4, nr.Ta);
+    st4(sm.Tt + (16 * p + r) * LDT + 16 * p + 4 * q4, nr.Tb);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (k >= n_off(p)) break;
+        int rb, cb;
+        n_off_block(p, k, rb, cb);
+        st4(sm.Tt + (16 * rb + r) * LDT + 16 * cb + 4 * q4, nr.off[k]);
+    }
+}
+
+__device__ __forceinline__ void n_stage(ChunkLds& sm, int p, int lane) {
+    NRegs nr;
+    n_regs(sm, p, lane, nr);
+    n_store(sm, p, lane, nr);
 }
 
 // Merge stage (after the N stage is visible): wave 0 forms T's off-diagonal
-// blocks, T21 = -T22 N21 T11 at the 32- and 64-row levels; waves 1-3 form P.
-__device__ __forceinline__ void merge_stage(ChunkLds& sm, int p, int lane) {
+// blocks, T21 = -T22 N21 T11 at the 32- and 64-row levels (merge_t); waves 1-3
+// form P (p_tile: block (rb, cb) of lower(Qt Kb^T), p_store).
+template <typename L>
+__device__ __forceinline__ void merge_t(L& sm, int lane) {
     const int r = lane & 15, q4 = lane >> 4;
+    s16x4 bT10 = {0, 0, 0, 0}, aT32 = {0, 0, 0, 0};
+    s16x4 nblk[2];  // N_10, N_32
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+        const int o0 = 32 * p2;
+        nblk[p2] = ld4(sm.Tt + (o0 + 16 + r) * LDT + o0 + 4 * q4);
+    }
+    const s16x4 n20 = ld4(sm.Tt + (32 + r) * LDT + 4 * q4);
+    const s16x4 n21 = ld4(sm.Tt + (32 + r) * LDT + 16 + 4 * q4);
+    const s16x4 n30 = ld4(sm.Tt + (48 + r) * LDT + 4 * q4);
+    const s16x4 n31 = ld4(sm.Tt + (48 + r) * LDT + 16 + 4 * q4);
+    const s16x4 bT00 = ld4(sm.Tt + r * LDT + 4 * q4);
+    const s16x4 bT11 = ld4(sm.Tt + (16 + r) * LDT + 16 + 4 * q4);
+    const s16x4 aT22 = ld4(sm.T + (32 + r) * LDT + 32 + 4 * q4);
+    const s16x4 aT33 = ld4(sm.T + (48 + r) * LDT + 48 + 4 * q4);
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+        const int o0 = 32 * p2;
+        const s16x4 bTlo = p2 == 0 ? bT00 : ld4(sm.Tt + (32 + r) * LDT + 32 + 4 * q4);
+        const s16x4 aThi = p2 == 0 ? ld4(sm.T + (16 + r) * LDT + 16 + 4 * q4) : aT33;
+        const f32x4 X = mma16(nblk[p2], bTlo, Z4);
+        const s16x4 xb = cvt4(X);
+        const f32x4 Ya = neg4(mma16(xb, aThi, Z4));  // T block, A layout
+        st4(sm.T + (o0 + 16 + r) * LDT + o0 + 4 * q4, Ya);
+        if (p2 == 0) bT10 = cvt4(neg4(mma16(aThi, xb, Z4)));  // B layout
+        else aT32 = cvt4(Ya);
+    }
+    s16x4 xm[2][2];
+    xm[0][0] = cvt4(mma16(n21, bT10, mma16(n20, bT00, Z4)));
+    xm[0][1] = cvt4(mma16(n21, bT11, Z4));
+    xm[1][0] = cvt4(mma16(n31, bT10, mma16(n30, bT00, Z4)));
+    xm[1][1] = cvt4(mma16(n31, bT11, Z4));
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const f32x4 y0 = mma16(xm[0][bb], aT22, Z4);
+        const f32x4 y1 = mma16(xm[1][bb], aT33, mma16(xm[0][bb], aT32, Z4));
+        st4(sm.T + (32 + r) * LDT + 16 * bb + 4 * q4, neg4(y0));
+        st4(sm.T + (48 + r) * LDT + 16 * bb + 4 * q4, neg4(y1));
+    }
+}
+
+template <typename L>
+__device__ __forceinline__ f32x4 p_tile(const L& sm, int rb, int cb, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+    f32x4 acc = Z4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        acc = mma32(ld8(sm.Kb + (16 * cb + r) * LDK + 32 * kk + 8 * q4),
+                    ld8(sm.Qt + (16 * rb + r) * LDK + 32 * kk + 8 * q4), acc);
+    if (rb == cb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * q4 + e > r) acc[e] = 0.f;
+    }
+    return acc;
+}
+template <typename L>
+__device__ __forceinline__ void p_store(L& sm, int rb, int cb, int lane, f32x4 acc) {
+    const int r = lane & 15, q4 = lane >> 4;
+    st4(sm.P + (16 * rb + r) * LDT + 16 * cb + 4 * q4, acc);
+}
+
+__device__ __forceinline__ void merge_stage(ChunkLds& sm, int p, int lane) {
     if (p == 0) {
-        s16x4 bT10 = {0, 0, 0, 0}, aT32 = {0, 0, 0, 0};
-        s16x4 nblk[2];  // N_10, N_32
-#pragma unroll
-        for (int p2 = 0; p2 < 2; ++p2) {
-            const int o0 = 32 * p2;
-            nblk[p2] = ld4(sm.Tt + (o0 + 16 + r) * LDT + o0 + 4 * q4);
-        }
-        const s16x4 n20 = ld4(sm.Tt + (32 + r) * LDT + 4 * q4);
-        const s16x4 n21 = ld4(sm.Tt + (32 + r) * LDT + 16 + 4 * q4);
-        const s16x4 n30 = ld4(sm.Tt + (48 + r) * LDT + 4 * q4);
-        const s16x4 n31 = ld4(sm.Tt + (48 + r) * LDT + 16 + 4 * q4);
-        const s16x4 bT00 = ld4(sm.Tt + r * LDT + 4 * q4);
-        const s16x4 bT11 = ld4(sm.Tt + (16 + r) * LDT + 16 + 4 * q4);
-        const s16x4 aT22 = ld4(sm.T + (32 + r) * LDT + 32 + 4 * q4);
-        const s16x4 aT33 = ld4(sm.T + (48 + r) * LDT + 48 + 4 * q4);
-#pragma unroll
-        for (int p2 = 0; p2 < 2; ++p2) {
-            const int o0 = 32 * p2;
-            const s16x4 bTlo = p2 == 0 ? bT00 : ld4(sm.Tt + (32 + r) * LDT + 32 + 4 * q4);
-            const s16x4 aThi = p2 == 0 ? ld4(sm.T + (16 + r) * LDT + 16 + 4 * q4) : aT33;
-            const f32x4 X = mma16(nblk[p2], bTlo, Z4);
-            const s16x4 xb = cvt4(X);
-            const f32x4 Ya = neg4(mma16(xb, aThi, Z4));  // T block, A layout
-            st4(sm.T + (o0 + 16 + r) * LDT + o0 + 4 * q4, Ya);
-            if (p2 == 0) bT10 = cvt4(neg4(mma16(aThi, xb, Z4)));  // B layout
-            else aT32 = cvt4(Ya);
-        }
-        s16x4 xm[2][2];
-        xm[0][0] = cvt4(mma16(n21, bT10, mma16(n20, bT00, Z4)));
-        xm[0][1] = cvt4(mma16(n21, bT11, Z4));
-        xm[1][0] = cvt4(mma16(n31, bT10, mma16(n30, bT00, Z4)));
-        xm[1][1] = cvt4(mma16(n31, bT11, Z4));
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const f32x4 y0 = mma16(xm[0][bb], aT22, Z4);
-            const f32x4 y1 = mma16(xm[1][bb], aT33, mma16(xm[0][bb], aT32, Z4));
-            st4(sm.T + (32 + r) * LDT + 16 * bb + 4 * q4, neg4(y0));
-            st4(sm.T + (48 + r) * LDT + 16 * bb + 4 * q4, neg4(y1));
-        }
+        merge_t(sm, lane);
     } else {
-        auto ptile = [&](int rb, int cb) {
-            f32x4 acc = Z4;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                acc = mma32(ld8(sm.Kb + (16 * cb + r) * LDK + 32 * kk + 8 * q4),
-                            ld8(sm.Qt + (16 * rb + r) * LDK + 32 * kk + 8 * q4), acc);
-            if (rb == cb) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * q4 + e > r) acc[e] = 0.f;
-            }
-            st4(sm.P + (16 * rb + r) * LDT + 16 * cb + 4 * q4, acc);
-        };
+        auto ptile = [&](int rb, int cb) { p_store(sm, rb, cb, lane, p_tile(sm, rb, cb, lane)); };
         if (p == 1) { ptile(0, 0); ptile(1, 0); ptile(1, 1); }
         else if (p == 2) { ptile(2, 0); ptile(2, 1); ptile(2, 2); }
         else { ptile(3, 0); ptile(3, 1); ptile(3, 2); ptile(3, 3); }

@@ -36,17 +36,45 @@ constexpr size_t BATCH_TILES = (size_t)4 << 30;  // tiles of the preferred batch
 using namespace sp;
 
 // ---------------------------------------------------------------- prep
+// LDS of prep_kernel: the decay stage's Kt, Qt and Kb rows and beta.  Once the
+// N and P blocks are in registers, T, Tt and P take the place of Kt and Qt
+// (TpLds), so that a workgroup needs 52.5 KB and three fit a CU's 160 KB
+// (with T, Tt and P beside the rows, 80 KB: two).
+struct PrepLds {
+    uint16_t Kt[C * LDK];  // [t][i]
+    uint16_t Qt[C * LDK];  // [t][i]
+    uint16_t Kb[C * LDK];  // [t][i]
+    float beta[C];
+};
+struct TpLds {
+    uint16_t T[C * LDT];   // T [t][s]
+    uint16_t Tt[C * LDT];  // T^T [s][t] on the diagonal blocks, N [t][s] below them
+    uint16_t P[C * LDT];   // P [t][s]
+};
+static_assert(sizeof(TpLds) <= sizeof(PrepLds::Kt) + sizeof(PrepLds::Qt),
+              "T, Tt and P fit over the Kt and Qt rows");
+
+// Block k (row order) of the 16x16 blocks on and below the diagonal of a 4x4
+// grid: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+__device__ __forceinline__ void lower_block(int k, int& rb, int& cb) {
+    rb = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+    cb = k - rb * (rb + 1) / 2;
+}
+
 // grid (active sequences * H, chunks in the window): one workgroup of 4 waves
 // per (sequence rank, head, window chunk) runs the operand stages and exports
 // the tile.  order[rank] is the sequence (order NULL: rank = sequence).
 // GM: the decay inputs' GateMode (per channel, per head, or the projection).
+// Wave p forms P's blocks 2, 2, 3, 3 (p = 0..3) of the ten in row order,
+// beside its N blocks, while Kt and Qt are still in LDS.
 template <int GM>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 3)
 prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
             const float* __restrict__ beta,
             const int32_t* __restrict__ cu, const int32_t* __restrict__ order, int64_t T, int H,
             int w0, int win, uint8_t* __restrict__ ws_tiles) {
-    __shared__ __attribute__((aligned(16))) ChunkLds sm;
+    __shared__ __attribute__((aligned(16))) PrepLds sm;
+    TpLds& tp = *reinterpret_cast<TpLds*>(sm.Kt);
     const int slot = blockIdx.x / H, h = blockIdx.x - slot * H, cl = blockIdx.y;
     const int n = order ? order[slot] : slot;
     int64_t tb, te;
@@ -55,22 +83,47 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
     const int c = w0 + cl;
     if (c >= nc) return;
     const int tid = threadIdx.x, p = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, q4 = lane >> 4;
     const int64_t c0 = tb + (int64_t)c * C;
     const int L = (te - c0) < C ? (int)(te - c0) : C;
     const auto rt = window(ws_tiles + ((size_t)(slot * win + cl) * H + h) * TILE, TILE);
 
-    zero_tp(sm, tid, 256);
     ChunkIn in;
     load_chunk<GM>(in, q, k, g, beta, c0, L, H, h, p, lane);
     tile_beta<GM>(rt, in, p, lane);
     decay_stage<GM>(sm, in, p, lane, TileSinks{rt}, TileSinks{rt});
     __syncthreads();
     tile_export_kq(sm, rt, p, lane);
-    n_stage(sm, p, lane);
+    NRegs nr;
+    n_regs(sm, p, lane, nr);
+    const int pn = p < 2 ? 2 : 3, pk0 = p == 0 ? 0 : p == 1 ? 2 : p == 2 ? 4 : 7;
+    f32x4 pb[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        if (j >= pn) break;
+        int rb, cb;
+        lower_block(pk0 + j, rb, cb);
+        pb[j] = p_tile(sm, rb, cb, lane);
+    }
+    __syncthreads();  // Kt and Qt are read in full: T, Tt and P take their place
+    n_store(tp, p, lane, nr);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        if (j >= pn) break;
+        int rb, cb;
+        lower_block(pk0 + j, rb, cb);
+        p_store(tp, rb, cb, lane, pb[j]);
+    }
+    // the upper blocks the T and P exports read: (0,1) and (2,3)
+    if (p == 0 || p == 2) {
+        const int off = (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4;
+        st4(tp.T + off, Z4);
+        st4(tp.P + off, Z4);
+    }
     __syncthreads();
-    merge_stage(sm, p, lane);
+    if (p == 0) merge_t(tp, lane);
     __syncthreads();
-    tile_export_tp(sm, rt, p, lane);
+    tile_export_tp(tp, rt, p, lane);
 }
 
 // ---------------------------------------------------------------- state pass

@@ -67,8 +67,9 @@ __device__ __forceinline__ void tile_beta(__amdgpu_buffer_rsrc_t rt, const Chunk
 
 // Kt and Qt fragments out of LDS (wave p exports row block p); after the decay
 // stage is visible.
-__device__ __forceinline__ void tile_export_kq(const ChunkLds& sm, __amdgpu_buffer_rsrc_t rt,
-                                               int p, int lane) {
+template <typename L>
+__device__ __forceinline__ void tile_export_kq(const L& sm, __amdgpu_buffer_rsrc_t rt, int p,
+                                               int lane) {
     const int r = lane & 15, q4 = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -84,8 +85,9 @@ __device__ __forceinline__ void tile_export_kq(const ChunkLds& sm, __amdgpu_buff
 // T and P fragments out of LDS (wave p exports row block p); after the merge
 // stage is visible.  Both are lower triangular: the fragments of columns
 // 32..63 in row blocks 0 and 1 are zero and are neither stored nor read.
-__device__ __forceinline__ void tile_export_tp(const ChunkLds& sm, __amdgpu_buffer_rsrc_t rt,
-                                               int p, int lane) {
+template <typename L>
+__device__ __forceinline__ void tile_export_tp(const L& sm, __amdgpu_buffer_rsrc_t rt, int p,
+                                               int lane) {
     const int r = lane & 15, q4 = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < (p >= 2 ? 2 : 1); ++kk) {
