@@ -5,6 +5,8 @@
 //   G = Gam * S,  U = T diag(beta)(V - Kt G),  O = Qt G + P U,  S <- G + Kb^T U
 // (recurrence from page "Ling-3.1-flash: a 560B hybrid-attention MoE, counted
 // from its safetensors headers", section "How KDA and MLA split the work").
+// With R = diag(beta)(V - Kt G), U = T R; T is folded into Wb^T = Kb^T T and
+// PT = P T, so that  S <- G + Wb^T R  and  O = Qt G + PT R.
 //
 // Everything that does not depend on the state is done ONCE per (sequence,
 // head, chunk) by prep_kernel, chunk-parallel, and stored in a workspace as
@@ -39,7 +41,9 @@ using namespace sp;
 // LDS of prep_kernel: the decay stage's Kt, Qt and Kb rows and beta.  Once the
 // N and P blocks are in registers, T, Tt and P take the place of Kt and Qt
 // (TpLds), so that a workgroup needs 52.5 KB and three fit a CU's 160 KB
-// (with T, Tt and P beside the rows, 80 KB: two).
+// (with T, Tt and P beside the rows, 80 KB: two).  After the merge, T^T
+// replaces Tt and the Kb^T rows (from registers) go after P (KbtLds); Wb^T and
+// PT are then formed over the Kb^T rows and P.
 struct PrepLds {
     uint16_t Kt[C * LDK];  // [t][i]
     uint16_t Qt[C * LDK];  // [t][i]
@@ -48,11 +52,12 @@ struct PrepLds {
 };
 struct TpLds {
     uint16_t T[C * LDT];   // T [t][s]
-    uint16_t Tt[C * LDT];  // T^T [s][t] on the diagonal blocks, N [t][s] below them
-    uint16_t P[C * LDT];   // P [t][s]
+    uint16_t Tt[C * LDT];  // T^T [s][t] on the diagonal blocks, N [t][s] below them;
+                           // after the merge, all of T^T [u][s] (zero for s < u)
+    uint16_t P[C * LDT];   // P [t][s], then PT [t][u]
+    uint16_t Kbt[D * LDT]; // Kb^T [i][t], then Wb^T [i][u]
 };
-static_assert(sizeof(TpLds) <= sizeof(PrepLds::Kt) + sizeof(PrepLds::Qt),
-              "T, Tt and P fit over the Kt and Qt rows");
+static_assert(sizeof(TpLds) <= sizeof(PrepLds), "the folded operands fit the stage rows");
 
 // Block k (row order) of the 16x16 blocks on and below the diagonal of a 4x4
 // grid: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
@@ -61,12 +66,30 @@ __device__ __forceinline__ void lower_block(int k, int& rb, int& cb) {
     cb = k - rb * (rb + 1) / 2;
 }
 
+// The decay stage's sinks in prep_kernel: Gam to the tile, the Kb^T pieces of
+// channels ch0 .. ch0 + 3 (ch0 a multiple of 4) into registers.
+struct PrepSinks {
+    __amdgpu_buffer_rsrc_t rt;
+    u32x4* kbt;
+    __device__ __forceinline__ void operator()(int ch0, const float (&gam)[4]) const {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(gam[0]), __float_as_uint(gam[1]), __float_as_uint(gam[2]),
+                  __float_as_uint(gam[3])},
+            rt, OFFW_GAM + 4 * ch0, 0, 0);
+    }
+    __device__ __forceinline__ void operator()(int i, int tg, u32x4 piece) const {
+        kbt[i & 3] = piece;
+    }
+};
+
 // grid (active sequences * H, chunks in the window): one workgroup of 4 waves
 // per (sequence rank, head, window chunk) runs the operand stages and exports
-// the tile.  order[rank] is the sequence (order NULL: rank = sequence).
-// GM: the decay inputs' GateMode (per channel, per head, or the projection).
-// Wave p forms P's blocks 2, 2, 3, 3 (p = 0..3) of the ten in row order,
-// beside its N blocks, while Kt and Qt are still in LDS.
+// the tile (layout TILE_W in kda_state_pass.h).  order[rank] is the sequence
+// (order NULL: rank = sequence).  GM: the decay inputs' GateMode (per channel,
+// per head, or the projection).  Wave p forms P's blocks 2, 2, 3, 3 (p = 0..3)
+// of the ten in row order beside its N blocks, while Kt and Qt are still in
+// LDS; after the merge, rows [32p, 32p + 32) of Wb^T = Kb^T T and row block p
+// of PT = P T.
 template <int GM>
 __global__ void __launch_bounds__(256, 3)
 prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
@@ -86,12 +109,16 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
     const int r = lane & 15, q4 = lane >> 4;
     const int64_t c0 = tb + (int64_t)c * C;
     const int L = (te - c0) < C ? (int)(te - c0) : C;
-    const auto rt = window(ws_tiles + ((size_t)(slot * win + cl) * H + h) * TILE, TILE);
+    const auto rt = window(ws_tiles + ((size_t)(slot * win + cl) * H + h) * TILE_W, TILE_W);
 
     ChunkIn in;
     load_chunk<GM>(in, q, k, g, beta, c0, L, H, h, p, lane);
-    tile_beta<GM>(rt, in, p, lane);
-    decay_stage<GM>(sm, in, p, lane, TileSinks{rt}, TileSinks{rt});
+    if (p == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(chunk_beta<GM>(in, lane)), rt,
+                                              OFFW_BETA + 4 * lane, 0, 0);
+    u32x4 kbt[4];  // Kb^T pieces: channel ch0 + e, tokens [8tg, 8tg + 8)
+    const PrepSinks sinks{rt, kbt};
+    decay_stage<GM>(sm, in, p, lane, sinks, sinks);
     __syncthreads();
     tile_export_kq(sm, rt, p, lane);
     NRegs nr;
@@ -114,24 +141,88 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
         lower_block(pk0 + j, rb, cb);
         p_store(tp, rb, cb, lane, pb[j]);
     }
-    // the upper blocks the T and P exports read: (0,1) and (2,3)
-    if (p == 0 || p == 2) {
-        const int off = (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4;
-        st4(tp.T + off, Z4);
-        st4(tp.P + off, Z4);
-    }
+    if (p == 0 || p == 2)  // P's upper blocks that PT's k-steps read: (0,1), (2,3)
+        st4(tp.P + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
     __syncthreads();
     if (p == 0) merge_t(tp, lane);
     __syncthreads();
-    tile_export_tp(tp, rt, p, lane);
+    // T^T over Tt (zero below its diagonal), Kb^T rows from registers
+    for (int e = tid; e < C * C; e += 256) {
+        const int s_ = e >> 6, u = e & 63;
+        tp.Tt[u * LDT + s_] = s_ >= u ? tp.T[s_ * LDT + u] : (uint16_t)0;
+    }
+    {
+        const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<u32x4*>(tp.Kbt + (ch0 + e) * LDT + 8 * tg) = kbt[e];
+    }
+    __syncthreads();
+    // Wb^T rows [32p, 32p + 32): Wb^T[i][u] = sum_{s >= u} Kb^T[i][s] T[s][u]
+    f32x4 wacc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int ub = 0; ub < 4; ++ub) {
+            f32x4 acc = Z4;
+#pragma unroll
+            for (int kk = (ub >= 2 ? 1 : 0); kk < 2; ++kk)
+                acc = mma32(ld8(tp.Tt + (16 * ub + r) * LDT + 32 * kk + 8 * q4),
+                            ld8(tp.Kbt + (32 * p + 16 * a + r) * LDT + 32 * kk + 8 * q4), acc);
+            wacc[a][ub] = acc;
+        }
+    // PT row block p: PT[t][u] = sum_{u <= s <= t} P[t][s] T[s][u]; the
+    // exported blocks, (0,1) and (2,3) coming out zero
+    const int nk = p >= 2 ? 2 : 1, nub = p >= 2 ? 4 : 2;
+    f32x4 pacc[4];
+#pragma unroll
+    for (int ub = 0; ub < 4; ++ub) {
+        if (ub >= nub) break;
+        f32x4 acc = Z4;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk >= nk) break;
+            acc = mma32(ld8(tp.Tt + (16 * ub + r) * LDT + 32 * kk + 8 * q4),
+                        ld8(tp.P + (16 * p + r) * LDT + 32 * kk + 8 * q4), acc);
+        }
+        pacc[ub] = acc;
+    }
+    __syncthreads();  // every read of Kb^T and P is done: they take Wb^T and PT
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int ub = 0; ub < 4; ++ub)
+            st4(tp.Kbt + (32 * p + 16 * a + r) * LDT + 16 * ub + 4 * q4, wacc[a][ub]);
+#pragma unroll
+    for (int ub = 0; ub < 4; ++ub) {
+        if (ub >= nub) break;
+        st4(tp.P + (16 * p + r) * LDT + 16 * ub + 4 * q4, pacc[ub]);
+    }
+    __syncthreads();
+    // exports: Wb^T fragments [a][kk] of rows 32p + 16a, PT fragments of row block p
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                as_u4(ld8(tp.Kbt + (32 * p + 16 * a + r) * LDT + 32 * kk + 8 * q4)), rt,
+                OFFW_WBT + ((p * 4 + a * 2 + kk) * 64 + lane) * 16, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        if (kk >= nk) break;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            as_u4(ld8(tp.P + (16 * p + r) * LDT + 32 * kk + 8 * q4)), rt,
+            OFFW_PT + ((p * 2 + kk) * 64 + lane) * 16, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------- state pass
 // grid n_pairs * NS, n_pairs = (ranked sequences in the window) * H, the slices
-// of one head placed on one XCD; 8 waves, the roles and barriers of the state
-// pass pieces in kda_state_pass.h.  Fragments come straight from the tiles into
-// registers, two chunks ahead (three register sets in rotation), spread over
-// the step's segments.
+// of one head placed on one XCD; 8 waves: the chain waves form R, then
+// S <- G + Wb^T R and the next G; the output waves form Z = Qt G, then
+// O = Z + PT R; two barriers per chunk (R complete, next G complete).
+// Fragments come straight from the tiles into registers, two chunks ahead
+// (three register sets in rotation), spread over the step's segments.
 __global__ void __launch_bounds__(512)
 state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
              const int32_t* __restrict__ order, int64_t T, int H,
@@ -190,8 +281,8 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
     };
     auto tile_rsrc = [&](int c) {
         const int cc = c < c_end ? c : c_beg;  // keep the address inside the workspace
-        return window(ws_tiles + ((size_t)(slot * win + (cc - w0)) * H + h) * TILE,
-                      c < c_end ? TILE : 0);
+        return window(ws_tiles + ((size_t)(slot * win + (cc - w0)) * H + h) * TILE_W,
+                      c < c_end ? TILE_W : 0);
     };
     // this lane's (row, column) of the chunk in the accumulator layout, as a
     // byte offset from the slice's first element of the chunk's first row
@@ -215,27 +306,26 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
                     const int i = 32 * cw + 16 * a + 4 * q4 + e, j = 16 * jb + r;
                     S[a][jb][e] = s_in ? s_in[sidx + (size_t)i * D + j0 + j] : 0.f;
                 }
-        auto load_a = [&](int c, ChainFrags& f) {
-            chain_load_a(f, tile_rsrc(c), vo_rsrc(v, c), xoff, cw, lane);
+        auto load_a = [&](int c, ChainFragsW& f) {
+            chainw_load_a(f, tile_rsrc(c), vo_rsrc(v, c), xoff, cw, lane);
         };
-        auto load_b = [&](int c, ChainFrags& f) { chain_load_b(f, tile_rsrc(c), cw, lane); };
-        ChainFrags F0, F1, F2;
+        auto load_b = [&](int c, ChainFragsW& f) { chainw_load_b(f, tile_rsrc(c), cw, lane); };
+        ChainFragsW F0, F1, F2;
         load_a(c_beg, F0);
         load_b(c_beg, F0);
         load_a(c_beg + 1, F1);
         load_b(c_beg + 1, F1);
         chain_scale_store(sm, S, F0.gam, cw, lane);
         __syncthreads();
-        auto step = [&](int c, const ChainFrags& cur, const ChainFrags& nxt, ChainFrags& later) {
+        auto step = [&](int c, const ChainFragsW& cur, const ChainFragsW& nxt,
+                        ChainFragsW& later) {
             chain_stage_v(sm, cur.v, xrow, xcol);
             load_a(c + 2, later);
             chain_yr(sm, cur, cw, lane);
             __syncthreads();
             load_b(c + 2, later);
-            chain_u(sm, cur, cw, lane);
-            __syncthreads();
-            chain_s(sm, cur, nxt.gam, c + 1 < c_end, S,
-                    snapshot_at(snap, n, h, H, D, (int64_t)(c + 1) * C, te - tb), j0, cw, lane);
+            chainw_s(sm, cur, nxt.gam, c + 1 < c_end, S,
+                     snapshot_at(snap, n, h, H, D, (int64_t)(c + 1) * C, te - tb), j0, cw, lane);
             __syncthreads();
         };
         int c = c_beg;
@@ -259,8 +349,8 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
         }
     } else {
         // ============================================================ output
-        auto load_a = [&](int c, OutFrags& f) { out_load_a(f, tile_rsrc(c), cw, lane); };
-        auto load_b = [&](int c, OutFrags& f) { out_load_b(f, tile_rsrc(c), cw, lane); };
+        auto load_a = [&](int c, OutFrags& f) { outw_load_a(f, tile_rsrc(c), cw, lane); };
+        auto load_b = [&](int c, OutFrags& f) { outw_load_b(f, tile_rsrc(c), cw, lane); };
         OutFrags F0, F1, F2;
         load_a(c_beg, F0);
         load_b(c_beg, F0);
@@ -271,8 +361,7 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
             f32x4 Zc[2];
             out_z(sm, cur, Zc, lane);
             __syncthreads();
-            __syncthreads();
-            __builtin_amdgcn_raw_buffer_store_b128(out_o(sm, cur, Zc, cw, lane, xrow, xcol),
+            __builtin_amdgcn_raw_buffer_store_b128(outw_o(sm, cur, Zc, cw, lane, xrow, xcol),
                                                    vo_rsrc(o, c), xoff, 0, 0);
             load_a(c + 2, later);
             load_b(c + 2, later);
@@ -313,7 +402,7 @@ seq_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int64_t T,
 // every sequence if that is less, and at least one chunk of every sequence.
 static size_t order_bytes(int n_seqs) { return ((size_t)n_seqs * 4 + 255) & ~(size_t)255; }
 static size_t tile_bytes(int n_seqs, int H) {
-    const size_t one = (size_t)n_seqs * H * TILE;
+    const size_t one = (size_t)n_seqs * H * TILE_W;
     const size_t most = one * MAX_WIN < TILE_BUDGET ? one * MAX_WIN : TILE_BUDGET;
     return most > one ? most : one;
 }
@@ -333,7 +422,7 @@ size_t prefill_split_workspace_bytes_batch(const int32_t* cu_host, int n_seqs, i
         const int nc = (int)(((int64_t)cu_host[n + 1] - cu_host[n] + C - 1) / C);
         longest = nc > longest ? nc : longest;
     }
-    const size_t one = (size_t)n_seqs * H * TILE;
+    const size_t one = (size_t)n_seqs * H * TILE_W;
     size_t win = longest < MAX_WIN ? (size_t)longest : (size_t)MAX_WIN;
     if (one && win * one > BATCH_TILES) win = BATCH_TILES / one;
     const size_t want = (size_t)n_seqs * H * D * D * 4 + order_bytes(n_seqs) + win * one;
@@ -388,7 +477,7 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gat
         while (active < n_seqs && len[active] > w0) ++active;
         if (!ranked) active = n_seqs;  // identity order: every sequence takes part
         const int visit = w0 == 0 ? n_seqs : active;
-        size_t w = active ? tbytes / ((size_t)active * H * TILE) : 1;
+        size_t w = active ? tbytes / ((size_t)active * H * TILE_W) : 1;
         const int win = w < 1 ? 1 : (w > (size_t)MAX_WIN ? MAX_WIN : (int)w);
         const int rows = max_chunks - w0 < win ? max_chunks - w0 : win;
         if (rows > 0 && active > 0) {

@@ -187,7 +187,8 @@ __device__ __forceinline__ void chain_stage_v(StateLds& sm, const uint4& v, int 
 }
 
 // [A] Y = Kt G; R = diag(beta)(V - Y) into Rt.
-__device__ __forceinline__ void chain_yr(StateLds& sm, const ChainFrags& cur, int cw, int lane) {
+template <typename Frags>
+__device__ __forceinline__ void chain_yr(StateLds& sm, const Frags& cur, int cw, int lane) {
     const int r = lane & 15, q4 = lane >> 4;
     f32x4 Y[2] = {Z4, Z4};
 #pragma unroll
@@ -267,6 +268,104 @@ __device__ __forceinline__ u32x4 out_o(StateLds& sm, const OutFrags& cur, const 
     for (int jb = 0; jb < 2; ++jb) {
         f32x4 acc = mma32(cur.P[0], ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
         if (cw >= 2) acc = mma32(cur.P[1], ld8(sm.Ut + (16 * jb + r) * LDT + 32 + 8 * q4), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint4 x = *reinterpret_cast<const uint4*>(sm.O + xrow * LDX + xcol);
+    return u32x4{x.x, x.y, x.z, x.w};
+}
+
+// ------------------------------------------------ state pass with T folded in
+// The two-kernel path folds T into the operands that follow it: with
+// U = T R,  S <- G + Kb^T U = G + Wb^T R  and  O = Z + P U = Z + PT R, where
+// Wb^T = Kb^T T (d_k x C) and PT = P T (C x C, lower triangular) do not depend
+// on the state and are formed by the operand kernel.  The chain then needs no
+// U, and a chunk takes two barriers: R complete, next G complete.  Tile byte
+// offsets (same fragment layouts as above; T is not stored):
+//   0 Kt, 16384 Qt, 32768 Wb^T (as Kb^T), 49152 PT (as P), 57344 beta[64],
+//   57600 Gam[128].
+constexpr int TILE_W = 58112;
+constexpr int OFFW_KT = 0, OFFW_QT = 16384, OFFW_WBT = 32768, OFFW_PT = 49152,
+              OFFW_BETA = 57344, OFFW_GAM = 57600;
+static_assert(TILE_W % 256 == 0, "tiles stay 256-byte aligned");
+
+struct ChainFragsW {
+    bf16x8 K[4], W[2][2];
+    float4 bet, gam[2];
+    uint4 v;  // V[16c + (lane >> 2)][8 (lane & 3) + 0..7]
+};
+
+// Kt, beta, Gam and this lane's piece of V (first half); Wb^T (second half).
+__device__ __forceinline__ void chainw_load_a(ChainFragsW& f, __amdgpu_buffer_rsrc_t rt,
+                                              __amdgpu_buffer_rsrc_t rv, int xoff, int cw,
+                                              int lane) {
+    const int q4 = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) f.K[kk] = ld_frag(rt, OFFW_KT + ((cw * 4 + kk) * 64 + lane) * 16);
+    f.bet = ld_f4(rt, OFFW_BETA + (16 * cw + 4 * q4) * 4);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) f.gam[a] = ld_f4(rt, OFFW_GAM + (32 * cw + 16 * a + 4 * q4) * 4);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, xoff, 0, 0);
+    f.v = make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void chainw_load_b(ChainFragsW& f, __amdgpu_buffer_rsrc_t rt, int cw,
+                                              int lane) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            f.W[a][kk] = ld_frag(rt, OFFW_WBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16);
+}
+__device__ __forceinline__ void outw_load_a(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
+                                            int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) f.Q[kk] = ld_frag(rt, OFFW_QT + ((cw * 4 + kk) * 64 + lane) * 16);
+}
+__device__ __forceinline__ void outw_load_b(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
+                                            int lane) {
+    f.P[0] = ld_frag(rt, OFFW_PT + (cw * 2 * 64 + lane) * 16);
+    if (cw >= 2) f.P[1] = ld_frag(rt, OFFW_PT + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
+}
+
+// [C] S <- G + Wb^T R (R from Rt); the raw S to snp (a snapshot) when snp is
+// set; with more, the next G = Gam' S into Gt.
+__device__ __forceinline__ void chainw_s(StateLds& sm, const ChainFragsW& cur,
+                                         const float4 (&gam_next)[2], bool more, StateFrag& S,
+                                         float* snp, int j0, int cw, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        const bf16x8 r0 = ld8(sm.Rt + (16 * jb + r) * LDT + 8 * q4);
+        const bf16x8 r1 = ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            f32x4 s = mma32(cur.W[a][1], r1, mma32(cur.W[a][0], r0, S[a][jb]));
+            if (snp) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    snp[(size_t)(32 * cw + 16 * a + 4 * q4 + e) * D + j0 + 16 * jb + r] = s[e];
+            }
+            if (more) {
+                s[0] *= gam_next[a].x; s[1] *= gam_next[a].y;
+                s[2] *= gam_next[a].z; s[3] *= gam_next[a].w;
+                st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, s);
+            }
+            S[a][jb] = s;
+        }
+    }
+}
+
+// [C] O = Z + PT R, staged through this wave's rows; returns this lane's
+// 16-byte piece (row xrow, columns xcol ..) for one store.
+__device__ __forceinline__ u32x4 outw_o(StateLds& sm, const OutFrags& cur, const f32x4 (&Zc)[2],
+                                        int cw, int lane, int xrow, int xcol) {
+    const int r = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        f32x4 acc = mma32(cur.P[0], ld8(sm.Rt + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
+        if (cw >= 2) acc = mma32(cur.P[1], ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4), acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[e]);

@@ -112,15 +112,15 @@ def test_prefill_rejects(lib, kw, status, needle):
 
 def test_prefill_workspace_bytes(lib):
     """State carry (64 KiB per sequence and head), the rank table (4 bytes per
-    sequence, rounded up to 256) and a window of 66 304-byte chunk tiles; 0 for
+    sequence, rounded up to 256) and a window of 58 112-byte chunk tiles; 0 for
     shapes that run without a workspace."""
     f = lib.kda_prefill_workspace_bytes
     # one sequence, 64 heads: a full 32-chunk window is below the 192 MiB budget
-    assert f(1, 64, 128, 128, 64, KDA_BF16) == 64 * 65536 + 256 + 32 * 64 * 66304
+    assert f(1, 64, 128, 128, 64, KDA_BF16) == 64 * 65536 + 256 + 32 * 64 * 58112
     # four sequences, 64 heads: the 192 MiB budget
     assert f(4, 64, 128, 128, 64, KDA_BF16) == 4 * 64 * 65536 + 256 + (192 << 20)
     # large batches keep one chunk per sequence and head
-    assert f(256, 64, 128, 128, 64, KDA_BF16) == 256 * 64 * (65536 + 66304) + 1024
+    assert f(256, 64, 128, 128, 64, KDA_BF16) == 256 * 64 * (65536 + 58112) + 1024
     assert f(1, 64, 128, 128, 64, KDA_F32) == 0
     assert f(1, 64, 64, 64, 64, KDA_BF16) == 0
     assert f(1, 64, 128, 128, 32, KDA_BF16) == 0
@@ -135,13 +135,13 @@ def test_prefill_workspace_bytes_batch(lib):
     fixed = lambda n: n * 64 * 65536 + ((n * 4 + 255) // 256) * 256
     # 64 sequences of 8 chunks: all 8 chunks of each
     cu = cu_arr([512 * i for i in range(65)])
-    assert f(cu, 64, 64, 128, 128, 64, KDA_BF16) == fixed(64) + 8 * 64 * 64 * 66304
-    # 24 sequences of 2048 tokens: 32-chunk windows (3.26 GB of tiles)
+    assert f(cu, 64, 64, 128, 128, 64, KDA_BF16) == fixed(64) + 8 * 64 * 64 * 58112
+    # 24 sequences of 2048 tokens: 32-chunk windows (2.86 GB of tiles)
     cu = cu_arr([2048 * i for i in range(25)])
-    assert f(cu, 24, 64, 128, 128, 64, KDA_BF16) == fixed(24) + 32 * 24 * 64 * 66304
-    # 256 sequences of 4096 tokens: capped at 4 GiB of tiles (3 chunks)
+    assert f(cu, 24, 64, 128, 128, 64, KDA_BF16) == fixed(24) + 32 * 24 * 64 * 58112
+    # 256 sequences of 4096 tokens: capped at 4 GiB of tiles (4 chunks)
     cu = cu_arr([4096 * i for i in range(257)])
-    assert f(cu, 256, 64, 128, 128, 64, KDA_BF16) == fixed(256) + 3 * 256 * 64 * 66304
+    assert f(cu, 256, 64, 128, 128, 64, KDA_BF16) == fixed(256) + 4 * 256 * 64 * 58112
     # one short sequence: the minimum (the 192 MiB budget's 32-chunk window)
     cu = cu_arr([0, 100])
     assert f(cu, 1, 64, 128, 128, 64, KDA_BF16) == \
