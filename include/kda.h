@@ -190,7 +190,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
  * the shape runs a path that needs none.  Depends only on n_seqs and H for the
  * matrix-core shapes: a state carry (64 KiB per sequence and head), a table of
  * the sequences ranked by length (4 bytes per sequence, rounded up to 256),
- * and the per-chunk operand tiles (66 304 bytes per chunk and head) of one
+ * and the per-chunk operand tiles (58 112 bytes per chunk and head) of one
  * window: 192 MiB, or 32 chunks of every sequence if that is less, and at least
  * one chunk of every sequence.  The sequences still running at a window's
  * start share its tiles, so windows grow as shorter sequences end (up to 32
