@@ -342,8 +342,19 @@ __device__ __forceinline__ void n_stage(ChunkLds& sm, int p, int lane) {
 
 // Merge stage (after the N stage is visible): wave 0 forms T's off-diagonal
 // blocks, T21 = -T22 N21 T11 at the 32- and 64-row levels (merge_t); waves 1-3
-// form P (p_tile: block (rb, cb) of lower(Qt Kb^T), p_store).
-template <typename L>
+// form P (p_tile: block (rb, cb) of lower(Qt Kb^T), p_store).  With FORM_TT,
+// merge_t also leaves all of T^T in Tt: each N block is zeroed once read (T^T
+// is zero below its diagonal; Tt's diagonal blocks already hold T's diagonal
+// blocks transposed) and each T block it forms is also written transposed.
+// Store 4 values of one row of an A-layout block into a transposed block:
+// x[e] (row r, column 4 q4 + e) to base[(4 q4 + e) * LDT + r].
+__device__ __forceinline__ void st4_tr(uint16_t* base, f32x4 x, int r, int q4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        base[(4 * q4 + e) * LDT + r] = __builtin_bit_cast(uint16_t, (__bf16)x[e]);
+}
+
+template <bool FORM_TT = false, typename L>
 __device__ __forceinline__ void merge_t(L& sm, int lane) {
     const int r = lane & 15, q4 = lane >> 4;
     s16x4 bT10 = {0, 0, 0, 0}, aT32 = {0, 0, 0, 0};
@@ -361,6 +372,14 @@ __device__ __forceinline__ void merge_t(L& sm, int lane) {
     const s16x4 bT11 = ld4(sm.Tt + (16 + r) * LDT + 16 + 4 * q4);
     const s16x4 aT22 = ld4(sm.T + (32 + r) * LDT + 32 + 4 * q4);
     const s16x4 aT33 = ld4(sm.T + (48 + r) * LDT + 48 + 4 * q4);
+    if constexpr (FORM_TT) {  // the N blocks this lane read: zero (below T^T's diagonal)
+        st4(sm.Tt + (16 + r) * LDT + 4 * q4, Z4);
+        st4(sm.Tt + (48 + r) * LDT + 32 + 4 * q4, Z4);
+        st4(sm.Tt + (32 + r) * LDT + 4 * q4, Z4);
+        st4(sm.Tt + (32 + r) * LDT + 16 + 4 * q4, Z4);
+        st4(sm.Tt + (48 + r) * LDT + 4 * q4, Z4);
+        st4(sm.Tt + (48 + r) * LDT + 16 + 4 * q4, Z4);
+    }
 #pragma unroll
     for (int p2 = 0; p2 < 2; ++p2) {
         const int o0 = 32 * p2;
@@ -370,6 +389,7 @@ __device__ __forceinline__ void merge_t(L& sm, int lane) {
         const s16x4 xb = cvt4(X);
         const f32x4 Ya = neg4(mma16(xb, aThi, Z4));  // T block, A layout
         st4(sm.T + (o0 + 16 + r) * LDT + o0 + 4 * q4, Ya);
+        if constexpr (FORM_TT) st4_tr(sm.Tt + o0 * LDT + o0 + 16, Ya, r, q4);
         if (p2 == 0) bT10 = cvt4(neg4(mma16(aThi, xb, Z4)));  // B layout
         else aT32 = cvt4(Ya);
     }
@@ -380,10 +400,14 @@ __device__ __forceinline__ void merge_t(L& sm, int lane) {
     xm[1][1] = cvt4(mma16(n31, bT11, Z4));
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-        const f32x4 y0 = mma16(xm[0][bb], aT22, Z4);
-        const f32x4 y1 = mma16(xm[1][bb], aT33, mma16(xm[0][bb], aT32, Z4));
-        st4(sm.T + (32 + r) * LDT + 16 * bb + 4 * q4, neg4(y0));
-        st4(sm.T + (48 + r) * LDT + 16 * bb + 4 * q4, neg4(y1));
+        const f32x4 y0 = neg4(mma16(xm[0][bb], aT22, Z4));
+        const f32x4 y1 = neg4(mma16(xm[1][bb], aT33, mma16(xm[0][bb], aT32, Z4)));
+        st4(sm.T + (32 + r) * LDT + 16 * bb + 4 * q4, y0);
+        st4(sm.T + (48 + r) * LDT + 16 * bb + 4 * q4, y1);
+        if constexpr (FORM_TT) {
+            st4_tr(sm.Tt + (16 * bb) * LDT + 32, y0, r, q4);
+            st4_tr(sm.Tt + (16 * bb) * LDT + 48, y1, r, q4);
+        }
     }
 }
 

@@ -42,8 +42,8 @@ using namespace sp;
 // N and P blocks are in registers, T, Tt and P take the place of Kt and Qt
 // (TpLds), so that a workgroup needs 52.5 KB and three fit a CU's 160 KB
 // (with T, Tt and P beside the rows, 80 KB: two).  After the merge, T^T
-// replaces Tt and the Kb^T rows (from registers) go after P (KbtLds); Wb^T and
-// PT are then formed over the Kb^T rows and P.
+// replaces Tt, the Kb^T rows (kept in registers since the decay stage) go after
+// P, and Wb^T and PT are formed over the Kb^T rows and T.
 struct PrepLds {
     uint16_t Kt[C * LDK];  // [t][i]
     uint16_t Qt[C * LDK];  // [t][i]
@@ -51,10 +51,10 @@ struct PrepLds {
     float beta[C];
 };
 struct TpLds {
-    uint16_t T[C * LDT];   // T [t][s]
+    uint16_t T[C * LDT];   // T [t][s], then PT [t][u]
     uint16_t Tt[C * LDT];  // T^T [s][t] on the diagonal blocks, N [t][s] below them;
                            // after the merge, all of T^T [u][s] (zero for s < u)
-    uint16_t P[C * LDT];   // P [t][s], then PT [t][u]
+    uint16_t P[C * LDT];   // P [t][s]
     uint16_t Kbt[D * LDT]; // Kb^T [i][t], then Wb^T [i][u]
 };
 static_assert(sizeof(TpLds) <= sizeof(PrepLds), "the folded operands fit the stage rows");
@@ -132,7 +132,7 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
         lower_block(pk0 + j, rb, cb);
         pb[j] = p_tile(sm, rb, cb, lane);
     }
-    __syncthreads();  // Kt and Qt are read in full: T, Tt and P take their place
+    __syncthreads();  // the stage rows are read in full: T, Tt, P and Kb^T take their place
     n_store(tp, p, lane, nr);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -143,14 +143,6 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
     }
     if (p == 0 || p == 2)  // P's upper blocks that PT's k-steps read: (0,1), (2,3)
         st4(tp.P + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
-    __syncthreads();
-    if (p == 0) merge_t(tp, lane);
-    __syncthreads();
-    // T^T over Tt (zero below its diagonal), Kb^T rows from registers
-    for (int e = tid; e < C * C; e += 256) {
-        const int s_ = e >> 6, u = e & 63;
-        tp.Tt[u * LDT + s_] = s_ >= u ? tp.T[s_ * LDT + u] : (uint16_t)0;
-    }
     {
         const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
 #pragma unroll
@@ -158,7 +150,10 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
             *reinterpret_cast<u32x4*>(tp.Kbt + (ch0 + e) * LDT + 8 * tg) = kbt[e];
     }
     __syncthreads();
+    if (p == 0) merge_t<true>(tp, lane);  // T's off-diagonal blocks; all of T^T in Tt
+    __syncthreads();
     // Wb^T rows [32p, 32p + 32): Wb^T[i][u] = sum_{s >= u} Kb^T[i][s] T[s][u]
+    // (computed transposed, so that a lane's 4 results lie along a row)
     f32x4 wacc[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -174,7 +169,6 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
     // PT row block p: PT[t][u] = sum_{u <= s <= t} P[t][s] T[s][u]; the
     // exported blocks, (0,1) and (2,3) coming out zero
     const int nk = p >= 2 ? 2 : 1, nub = p >= 2 ? 4 : 2;
-    f32x4 pacc[4];
 #pragma unroll
     for (int ub = 0; ub < 4; ++ub) {
         if (ub >= nub) break;
@@ -185,20 +179,20 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
             acc = mma32(ld8(tp.Tt + (16 * ub + r) * LDT + 32 * kk + 8 * q4),
                         ld8(tp.P + (16 * p + r) * LDT + 32 * kk + 8 * q4), acc);
         }
-        pacc[ub] = acc;
+        st4(tp.T + (16 * p + r) * LDT + 16 * ub + 4 * q4, acc);  // T is no longer read
     }
-    __syncthreads();  // every read of Kb^T and P is done: they take Wb^T and PT
+    // Wb^T over this wave's own Kb^T rows: every store needs an MFMA result
+    // that has consumed the loads of the columns it overwrites (those of ub >= 2
+    // write only columns that the loads they wait for cover), and LDS accesses
+    // of one wave complete in order
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int ub = 0; ub < 4; ++ub)
             st4(tp.Kbt + (32 * p + 16 * a + r) * LDT + 16 * ub + 4 * q4, wacc[a][ub]);
-#pragma unroll
-    for (int ub = 0; ub < 4; ++ub) {
-        if (ub >= nub) break;
-        st4(tp.P + (16 * p + r) * LDT + 16 * ub + 4 * q4, pacc[ub]);
-    }
-    __syncthreads();
+    // the exports read what other lanes of this wave wrote
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     // exports: Wb^T fragments [a][kk] of rows 32p + 16a, PT fragments of row block p
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -211,7 +205,7 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
     for (int kk = 0; kk < 2; ++kk) {
         if (kk >= nk) break;
         __builtin_amdgcn_raw_buffer_store_b128(
-            as_u4(ld8(tp.P + (16 * p + r) * LDT + 32 * kk + 8 * q4)), rt,
+            as_u4(ld8(tp.T + (16 * p + r) * LDT + 32 * kk + 8 * q4)), rt,
             OFFW_PT + ((p * 2 + kk) * 64 + lane) * 16, 0, 0);
     }
 }
