@@ -122,7 +122,14 @@ kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, i
  *   q, k            : [T, H, dk] dtype       v, o : [T, H, dv] dtype
  *   g               : [T, H, dk] fp32 (log decay; alpha = exp(g)), [T, H] fp32
  *                     with gate = KDA_GATE_HEAD, or the decay projection
- *                     [T, H, dk] in dtype with gate = KDA_GATE_PROJ
+ *                     [T, H, dk] in dtype with gate = KDA_GATE_PROJ.  Range:
+ *                     the chunked form scales operands by the exponential of
+ *                     the cumulative log decay inside a chunk, so the sum of g
+ *                     over any chunk (per channel) must stay above about -85;
+ *                     below about -88 the scale factors overflow fp32 and the
+ *                     outputs are not finite.  Tested to -78.7 with chunk 64
+ *                     (alpha ~ 0.3 per token); a smaller chunk widens the range.
+ *                     kda_decode_step and kda_decode_tokens have no such limit.
  *   a_log           : [H] fp32 with KDA_GATE_PROJ, else NULL
  *   beta            : [T, H] fp32 (logits with KDA_GATE_PROJ)
  *   cu_seqlens_dev  : [n_seqs + 1] int32 on the device

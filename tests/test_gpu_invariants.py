@@ -4,7 +4,8 @@ import pytest
 import torch
 
 import workloads
-from kda_testutil import TOL_BF16, dev, gpu_or_skip, gpu_prefill, np64, rel_fro
+from kda_testutil import (TOL_BF16, dev, gpu_or_skip, gpu_prefill, np64, oracle_on,
+                          per_seq_errors, rel_fro)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +70,28 @@ def test_split_and_fused_agree():
     e = max(rel_fro(np64(o1), np64(o2)), rel_fro(np64(S1), np64(S2)))
     print(f"split vs fused: {e:.2e}")
     assert e <= TOL_BF16 / 4
+
+
+@pytest.mark.parametrize("workspace", ["auto", None])
+def test_strong_decay_within_range(workspace):
+    """Decay strong enough (alpha ~ 0.3 per token and channel) that a 64-token
+    chunk's cumulative log decay reaches about -77 in some channels: the
+    matrix-core paths reference the decay to the chunk's end, so their factor
+    e^(b_t - b_C) then reaches ~e^77, near the fp32 limit (~e^88).  Both paths
+    still match the oracle."""
+    kda()
+    inp = workloads.recurrence_inputs([256, 100], H=2, d=128, dtype="bf16", g_mu=-0.84,
+                                      g_sigma=0.1, s0_std=0.3, seed=25)
+    cu = [int(c) for c in inp.cu_seqlens]
+    lows = [float(inp.g[t:min(t + 64, cu[n + 1])].sum(0).min())
+            for n in range(len(cu) - 1) for t in range(cu[n], cu[n + 1], 64)]
+    assert -88.0 < min(lows) < -70.0, min(lows)
+    o, S = gpu_prefill(inp, workspace=workspace)
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
+    print(f"strong decay ({'two-kernel' if workspace else 'fused'}), lowest chunk "
+          f"log decay {min(lows):.1f}: o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
 def test_handoff_prefill_prefill():
