@@ -144,15 +144,23 @@ hipError_t launch_state_init(void* state, kda_dtype state_dtype, int64_t n_elems
 //   fp32 state, several tokens: 256 threads of 64 elements (1024 threads were
 //     0.63 ms against 0.41 ms for four tokens: the per-token reductions and
 //     barriers then span 16 waves).
-//   bf16 state: 256 threads of 64 elements (512 threads were slower).
+//   bf16 state, one token per call: 1024 threads of 16 elements (2 rows of 8
+//     columns), at least 8 waves per SIMD, and the column sums formed once per
+//     column (as with several tokens): 0.1775 ms against 0.1833 ms for 256
+//     threads of 64 elements; 512 threads of 32 were 0.187-0.29 ms.
+//   bf16 state, several tokens: 256 threads of 64 elements.
+// COL_SUMS: the column sums over the row groups are formed once per column into
+// LDS and read back (faster with several tokens, or with 64 row groups), rather
+// than by every thread for its own columns.
 template <int D, int VEC, bool MULTI>
 struct DecodeShape {
     static constexpr int CG = D / VEC;
     static constexpr int RG = VEC == 4 ? (CG < 8 ? CG : (CG == 32 && !MULTI ? 32 : 8))
-                                       : (2 * CG < 16 ? 2 * CG : 16);
+                                       : (CG == 16 && !MULTI ? 64 : (2 * CG < 16 ? 2 * CG : 16));
     static constexpr int NT = CG * RG;
     static constexpr int RPT = D / RG;
     static constexpr int MIN_WAVES = NT == 1024 ? 8 : 1;  // per SIMD
+    static constexpr bool COL_SUMS = MULTI || RG >= 64;
 };
 template <int D, typename TS>
 constexpr int decode_vec() { return sizeof(TS) == 2 && D >= 64 ? 8 : 4; }
@@ -290,15 +298,16 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
         __syncthreads();
 
         // 4. full column sums, adding the row groups in order.  Where both
-        // kernels use the same row groups (bf16 states; D < 128), one call over
-        // n_tok tokens equals n_tok single steps bit for bit; for fp32 states of
-        // D = 128 the single-token kernel's 32 row groups regroup the sum.
+        // kernels use the same row groups (D < 128), one call over n_tok tokens
+        // equals n_tok single steps bit for bit (fp32 states); for D = 128 the
+        // single-token kernel's row groups (32 for fp32 states, 64 for bf16)
+        // regroup the sum.
         float Yk[VEC], Yq[VEC];
-        if constexpr (MULTI) {
+        if constexpr (S::COL_SUMS) {
             // once per column: thread t sums one column of Y_k (t < D) or Y_q,
             // then every thread reads its own columns (per token, 1/RG of the
             // LDS reads of each thread summing its own columns, for one more
-            // barrier: faster from two tokens up, slower for one)
+            // barrier: faster from two tokens up, and with 64 row groups)
             for (int idx = tid; idx < 2 * D; idx += NT) {
                 const int which = idx >= D, col = idx - which * D;
                 float acc = s_part[which][0][col];

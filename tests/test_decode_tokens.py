@@ -86,12 +86,12 @@ def test_decode_tokens_snapshots_match_prefixes():
 def test_decode_tokens_equals_single_steps(state_dtype):
     """One call over n_tok tokens against n_tok single-token decode steps.
     fp32 states: the call keeps the state in fp32 registers between tokens,
-    exactly what a round trip through memory holds; the single-token kernel sums
-    columns over 32 row groups of 4 rows and the multi-token kernel over 8 of
-    16, so the two agree to fp32 rounding.  bf16 states: single steps round the
-    state after every token and the call only once at its end, so only the first
-    token's outputs are comparable, and they are equal bit for bit (both kernels
-    use the same row groups there)."""
+    exactly what a round trip through memory holds, so the two agree to fp32
+    rounding (at d = 128 the single-token kernel sums columns over 32 row
+    groups of 4 rows, the multi-token kernel over 8 of 16).  bf16 states:
+    single steps round the state after every token and the call only once at
+    its end, so only the first token's outputs are comparable (64 row groups
+    against 16: fp32 rounding, then one bf16 rounding of o)."""
     m = kda()
     B, n_tok, H, d = 4, 3, 2, 128
     inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", s0_std=0.3, seed=72)
@@ -105,15 +105,17 @@ def test_decode_tokens_equals_single_steps(state_dtype):
                                       dev(inp.g[rows]), dev(inp.beta[rows]), s_single))
     torch.cuda.synchronize()
     o_single = torch.stack(outs, dim=1)
-    if state_dtype == torch.bfloat16:
-        assert torch.equal(o_multi[:, 0], o_single[:, 0])
-        return
     # outputs are bf16: fp32 regrouping may move one across a rounding boundary
+    if state_dtype == torch.bfloat16:
+        o_multi, o_single = o_multi[:, :1], o_single[:, :1]
     assert torch.allclose(o_multi.float(), o_single.float(), rtol=2.0 ** -7, atol=1e-6)
     eo = rel_fro(np64(o_multi), np64(o_single))
-    es = rel_fro(np64(s_multi), np64(s_single))
-    print(f"multi vs single steps, fp32 state: o {eo:.2e} S {es:.2e}")
-    assert eo <= 1e-4 and es <= 1e-6
+    print(f"multi vs single steps, {state_dtype} state: o {eo:.2e}")
+    assert eo <= 1e-4
+    if state_dtype == torch.float32:
+        es = rel_fro(np64(s_multi), np64(s_single))
+        print(f"  S {es:.2e}")
+        assert es <= 1e-6
 
 
 def test_decode_tokens_out_of_range_slot():
