@@ -75,7 +75,7 @@ struct PrepSinks {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{__float_as_uint(gam[0]), __float_as_uint(gam[1]), __float_as_uint(gam[2]),
                   __float_as_uint(gam[3])},
-            rt, OFFW_GAM + 4 * ch0, 0, 0);
+            rt, OFF_GAM + 4 * ch0, 0, 0);
     }
     __device__ __forceinline__ void operator()(int i, int tg, u32x4 piece) const {
         kbt[i & 3] = piece;
@@ -84,7 +84,7 @@ struct PrepSinks {
 
 // grid (active sequences * H, chunks in the window): one workgroup of 4 waves
 // per (sequence rank, head, window chunk) runs the operand stages and exports
-// the tile (layout TILE_W in kda_state_pass.h).  order[rank] is the sequence
+// the tile (layout in kda_state_pass.h).  order[rank] is the sequence
 // (order NULL: rank = sequence).  GM: the decay inputs' GateMode (per channel,
 // per head, or the projection).  Wave p forms P's blocks 2, 2, 3, 3 (p = 0..3)
 // of the ten in row order beside its N blocks, while Kt and Qt are still in
@@ -109,13 +109,13 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
     const int r = lane & 15, q4 = lane >> 4;
     const int64_t c0 = tb + (int64_t)c * C;
     const int L = (te - c0) < C ? (int)(te - c0) : C;
-    const auto rt = window(ws_tiles + ((size_t)(slot * win + cl) * H + h) * TILE_W, TILE_W);
+    const auto rt = window(ws_tiles + ((size_t)(slot * win + cl) * H + h) * TILE, TILE);
 
     ChunkIn in;
     load_chunk<GM>(in, q, k, g, beta, c0, L, H, h, p, lane);
     if (p == 0)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(chunk_beta<GM>(in, lane)), rt,
-                                              OFFW_BETA + 4 * lane, 0, 0);
+                                              OFF_BETA + 4 * lane, 0, 0);
     u32x4 kbt[4];  // Kb^T pieces: channel ch0 + e, tokens [8tg, 8tg + 8)
     const PrepSinks sinks{rt, kbt};
     decay_stage<GM>(sm, in, p, lane, sinks, sinks);
@@ -200,13 +200,13 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
         for (int kk = 0; kk < 2; ++kk)
             __builtin_amdgcn_raw_buffer_store_b128(
                 as_u4(ld8(tp.Kbt + (32 * p + 16 * a + r) * LDT + 32 * kk + 8 * q4)), rt,
-                OFFW_WBT + ((p * 4 + a * 2 + kk) * 64 + lane) * 16, 0, 0);
+                OFF_WBT + ((p * 4 + a * 2 + kk) * 64 + lane) * 16, 0, 0);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         if (kk >= nk) break;
         __builtin_amdgcn_raw_buffer_store_b128(
             as_u4(ld8(tp.T + (16 * p + r) * LDT + 32 * kk + 8 * q4)), rt,
-            OFFW_PT + ((p * 2 + kk) * 64 + lane) * 16, 0, 0);
+            OFF_PT + ((p * 2 + kk) * 64 + lane) * 16, 0, 0);
     }
 }
 
@@ -275,8 +275,8 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
     };
     auto tile_rsrc = [&](int c) {
         const int cc = c < c_end ? c : c_beg;  // keep the address inside the workspace
-        return window(ws_tiles + ((size_t)(slot * win + (cc - w0)) * H + h) * TILE_W,
-                      c < c_end ? TILE_W : 0);
+        return window(ws_tiles + ((size_t)(slot * win + (cc - w0)) * H + h) * TILE,
+                      c < c_end ? TILE : 0);
     };
     // this lane's (row, column) of the chunk in the accumulator layout, as a
     // byte offset from the slice's first element of the chunk's first row
@@ -396,7 +396,7 @@ seq_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int64_t T,
 // every sequence if that is less, and at least one chunk of every sequence.
 static size_t order_bytes(int n_seqs) { return ((size_t)n_seqs * 4 + 255) & ~(size_t)255; }
 static size_t tile_bytes(int n_seqs, int H) {
-    const size_t one = (size_t)n_seqs * H * TILE_W;
+    const size_t one = (size_t)n_seqs * H * TILE;
     const size_t most = one * MAX_WIN < TILE_BUDGET ? one * MAX_WIN : TILE_BUDGET;
     return most > one ? most : one;
 }
@@ -416,7 +416,7 @@ size_t prefill_split_workspace_bytes_batch(const int32_t* cu_host, int n_seqs, i
         const int nc = (int)(((int64_t)cu_host[n + 1] - cu_host[n] + C - 1) / C);
         longest = nc > longest ? nc : longest;
     }
-    const size_t one = (size_t)n_seqs * H * TILE_W;
+    const size_t one = (size_t)n_seqs * H * TILE;
     size_t win = longest < MAX_WIN ? (size_t)longest : (size_t)MAX_WIN;
     if (one && win * one > BATCH_TILES) win = BATCH_TILES / one;
     const size_t want = (size_t)n_seqs * H * D * D * 4 + order_bytes(n_seqs) + win * one;
@@ -471,7 +471,7 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gat
         while (active < n_seqs && len[active] > w0) ++active;
         if (!ranked) active = n_seqs;  // identity order: every sequence takes part
         const int visit = w0 == 0 ? n_seqs : active;
-        size_t w = active ? tbytes / ((size_t)active * H * TILE_W) : 1;
+        size_t w = active ? tbytes / ((size_t)active * H * TILE) : 1;
         const int win = w < 1 ? 1 : (w > (size_t)MAX_WIN ? MAX_WIN : (int)w);
         const int rows = max_chunks - w0 < win ? max_chunks - w0 : win;
         if (rows > 0 && active > 0) {

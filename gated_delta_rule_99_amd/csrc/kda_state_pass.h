@@ -1,27 +1,31 @@
 // Operand tiles and the pieces of the state pass of the two-kernel prefill
-// (kda_prefill_split.hip): the tile layout, the exports that write a tile from
-// the operand stages' LDS, and the chain and output waves' per-chunk steps.
+// (kda_prefill_split.hip), and the per-chunk steps the fused kernel
+// (kda_prefill_fused.hip) shares with it.
 //
-// A tile holds everything the state pass needs of one (sequence, head, chunk)
-// that does not depend on the state, in the exact lane order of the state
-// pass's MFMA operands, so that each lane reads one contiguous 16-byte
-// fragment.  Byte offsets:
-//   0      Kt fragments   [row block c 0..3][kk 0..3][lane 64][16 B]
-//   16384  Qt fragments   same
-//   32768  Kb^T fragments [c 0..3][a 0..1][kk 0..1][lane][16 B]   (rows 32c+16a)
-//   49152  T fragments    [c 0..3][kk 0..1][lane][16 B]
-//   57344  P fragments    same
-//   65536  beta[64] fp32, 65792 Gam[128] fp32
+// A tile holds everything the two-kernel state pass needs of one (sequence,
+// head, chunk) that does not depend on the state, in the exact lane order of
+// its MFMA operands, so that each lane reads one contiguous 16-byte fragment.
+// T is folded into the operands that follow it: Wb^T = Kb^T T and PT = P T.
+// Byte offsets:
+//   0      Kt fragments    [row block c 0..3][kk 0..3][lane 64][16 B]
+//   16384  Qt fragments    same
+//   32768  Wb^T fragments  [c 0..3][a 0..1][kk 0..1][lane][16 B]   (rows 32c+16a)
+//   49152  PT fragments    [c 0..3][kk 0..1][lane][16 B] (zero fragments skipped)
+//   57344  beta[64] fp32, 57600 Gam[128] fp32
 //
 // State pass of one (sequence, head, 32-column slice of the state), 8 waves
 // (recurrence from page "Ling-3.1-flash: a 560B hybrid-attention MoE, counted
 // from its safetensors headers", section "How KDA and MLA split the work"):
-// waves 0-3 carry the chain that the next chunk depends on,
-//   Y = Kt G,  R = diag(beta)(V - Y),  U = T R,  S <- G + Kb^T U,  G' = Gam' S;
-// waves 4-7 produce the output off that chain, Z = Qt G and O = Z + P U.
-// Wave c of either group owns rows [16c, 16c+16) of the chunk (Y, R, U, Z, O)
-// and chain wave c owns state rows [32c, 32c+32) of the slice.  Per chunk the
-// two groups meet at three barriers: R complete, U complete, next G complete.
+// waves 0-3 carry the chain that the next chunk depends on, waves 4-7 produce
+// the output off that chain.  Wave c of either group owns rows [16c, 16c+16) of
+// the chunk and chain wave c owns state rows [32c, 32c+32) of the slice.
+//   two-kernel path (chainw_*, outw_*; two barriers per chunk: R complete,
+//   next G complete):
+//     chain  Y = Kt G,  R = diag(beta)(V - Y),  S <- G + Wb^T R,  G' = Gam' S
+//     output Z = Qt G,  O = Z + PT R
+//   fused kernel (chain_*, out_*; three barriers: R, U, next G):
+//     chain  Y = Kt G,  R = diag(beta)(V - Y),  U = T R,  S <- G + Kb^T U
+//     output Z = Qt G,  O = Z + P U
 // V and O move with one 16-byte access per lane (16 rows x 32 columns per wave)
 // and are turned into the accumulator layout (lane (r, q4) holds rows 4q4 + e
 // of column r) through a staging tile that only the wave itself touches.
@@ -33,38 +37,13 @@ namespace kda {
 namespace co {
 
 constexpr int DVS = 32, NS = D / DVS;  // state columns per workgroup, slices per head
-constexpr int TILE = 66304;
-constexpr int OFF_KT = 0, OFF_QT = 16384, OFF_KBT = 32768, OFF_T = 49152, OFF_P = 57344,
-              OFF_BETA = 65536, OFF_GAM = 65792;
+constexpr int TILE = 58112;
+constexpr int OFF_KT = 0, OFF_QT = 16384, OFF_WBT = 32768, OFF_PT = 49152, OFF_BETA = 57344,
+              OFF_GAM = 57600;
+static_assert(TILE % 256 == 0, "tiles stay 256-byte aligned");
 constexpr int LDX = 40;  // row stride (bf16) of the V and O staging tiles
 
 // ---------------------------------------------------------------- tile export
-// The decay stage's sinks: Gam and the Kb^T fragments go straight to the tile.
-struct TileSinks {
-    __amdgpu_buffer_rsrc_t rt;
-    __device__ __forceinline__ void operator()(int ch0, const float (&gam)[4]) const {
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4{__float_as_uint(gam[0]), __float_as_uint(gam[1]), __float_as_uint(gam[2]),
-                  __float_as_uint(gam[3])},
-            rt, OFF_GAM + 4 * ch0, 0, 0);
-    }
-    __device__ __forceinline__ void operator()(int i, int tg, u32x4 piece) const {
-        // Kb^T fragment (row block i / 16, k block tg / 4), lane (i % 16, tg % 4)
-        const int blk = (i >> 5) * 4 + ((i >> 4) & 1) * 2 + (tg >> 2);
-        const int ln = (i & 15) + 16 * (tg & 3);
-        __builtin_amdgcn_raw_buffer_store_b128(piece, rt, OFF_KBT + (blk * 64 + ln) * 16, 0, 0);
-    }
-};
-
-// beta of the chunk (wave 0 holds one token per lane).
-template <int GM>
-__device__ __forceinline__ void tile_beta(__amdgpu_buffer_rsrc_t rt, const ChunkIn& in, int p,
-                                          int lane) {
-    if (p == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(chunk_beta<GM>(in, lane)), rt,
-                                              OFF_BETA + 4 * lane, 0, 0);
-}
-
 // Kt and Qt fragments out of LDS (wave p exports row block p); after the decay
 // stage is visible.
 template <typename L>
@@ -78,24 +57,6 @@ __device__ __forceinline__ void tile_export_kq(const L& sm, __amdgpu_buffer_rsrc
         __builtin_amdgcn_raw_buffer_store_b128(as_u4(a), rt, OFF_KT + ((p * 4 + kk) * 64 + lane) * 16,
                                                0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(as_u4(b), rt, OFF_QT + ((p * 4 + kk) * 64 + lane) * 16,
-                                               0, 0);
-    }
-}
-
-// T and P fragments out of LDS (wave p exports row block p); after the merge
-// stage is visible.  Both are lower triangular: the fragments of columns
-// 32..63 in row blocks 0 and 1 are zero and are neither stored nor read.
-template <typename L>
-__device__ __forceinline__ void tile_export_tp(const L& sm, __amdgpu_buffer_rsrc_t rt, int p,
-                                               int lane) {
-    const int r = lane & 15, q4 = lane >> 4;
-#pragma unroll
-    for (int kk = 0; kk < (p >= 2 ? 2 : 1); ++kk) {
-        const bf16x8 a = ld8(sm.T + (16 * p + r) * LDT + 32 * kk + 8 * q4);
-        const bf16x8 b = ld8(sm.P + (16 * p + r) * LDT + 32 * kk + 8 * q4);
-        __builtin_amdgcn_raw_buffer_store_b128(as_u4(a), rt, OFF_T + ((p * 2 + kk) * 64 + lane) * 16,
-                                               0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(as_u4(b), rt, OFF_P + ((p * 2 + kk) * 64 + lane) * 16,
                                                0, 0);
     }
 }
@@ -125,42 +86,6 @@ __device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t rt, int off) {
     const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0);
     return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
                        __uint_as_float(x[3]));
-}
-
-// Chain fragments, first half: Kt, beta, Gam, and this lane's piece of V
-// (rv: the chunk's V rows of the slice; xoff: the piece's byte offset).
-__device__ __forceinline__ void chain_load_a(ChainFrags& f, __amdgpu_buffer_rsrc_t rt,
-                                             __amdgpu_buffer_rsrc_t rv, int xoff, int cw,
-                                             int lane) {
-    const int q4 = lane >> 4;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) f.K[kk] = ld_frag(rt, OFF_KT + ((cw * 4 + kk) * 64 + lane) * 16);
-    f.bet = ld_f4(rt, OFF_BETA + (16 * cw + 4 * q4) * 4);
-#pragma unroll
-    for (int a = 0; a < 2; ++a) f.gam[a] = ld_f4(rt, OFF_GAM + (32 * cw + 16 * a + 4 * q4) * 4);
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, xoff, 0, 0);
-    f.v = make_uint4(x[0], x[1], x[2], x[3]);
-}
-// Chain fragments, second half: Kb^T and T.
-__device__ __forceinline__ void chain_load_b(ChainFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
-                                             int lane) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            f.Kb[a][kk] = ld_frag(rt, OFF_KBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16);
-    f.T[0] = ld_frag(rt, OFF_T + (cw * 2 * 64 + lane) * 16);
-    if (cw >= 2) f.T[1] = ld_frag(rt, OFF_T + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
-}
-__device__ __forceinline__ void out_load_a(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
-                                           int lane) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) f.Q[kk] = ld_frag(rt, OFF_QT + ((cw * 4 + kk) * 64 + lane) * 16);
-}
-__device__ __forceinline__ void out_load_b(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
-                                           int lane) {
-    f.P[0] = ld_frag(rt, OFF_P + (cw * 2 * 64 + lane) * 16);
-    if (cw >= 2) f.P[1] = ld_frag(rt, OFF_P + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
 }
 
 // S[a][jb] holds S[32cw + 16a + 4q4 + e][16jb + r] of the slice.
@@ -277,20 +202,9 @@ __device__ __forceinline__ u32x4 out_o(StateLds& sm, const OutFrags& cur, const 
     return u32x4{x.x, x.y, x.z, x.w};
 }
 
-// ------------------------------------------------ state pass with T folded in
-// The two-kernel path folds T into the operands that follow it: with
-// U = T R,  S <- G + Kb^T U = G + Wb^T R  and  O = Z + P U = Z + PT R, where
-// Wb^T = Kb^T T (d_k x C) and PT = P T (C x C, lower triangular) do not depend
-// on the state and are formed by the operand kernel.  The chain then needs no
-// U, and a chunk takes two barriers: R complete, next G complete.  Tile byte
-// offsets (same fragment layouts as above; T is not stored):
-//   0 Kt, 16384 Qt, 32768 Wb^T (as Kb^T), 49152 PT (as P), 57344 beta[64],
-//   57600 Gam[128].
-constexpr int TILE_W = 58112;
-constexpr int OFFW_KT = 0, OFFW_QT = 16384, OFFW_WBT = 32768, OFFW_PT = 49152,
-              OFFW_BETA = 57344, OFFW_GAM = 57600;
-static_assert(TILE_W % 256 == 0, "tiles stay 256-byte aligned");
-
+// ------------------------------------------------ two-kernel path, T folded in
+// With U = T R:  S <- G + Kb^T U = G + Wb^T R  and  O = Z + P U = Z + PT R.  The
+// chain then needs no U, and a chunk takes two barriers.
 struct ChainFragsW {
     bf16x8 K[4], W[2][2];
     float4 bet, gam[2];
@@ -303,10 +217,10 @@ __device__ __forceinline__ void chainw_load_a(ChainFragsW& f, __amdgpu_buffer_rs
                                               int lane) {
     const int q4 = lane >> 4;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) f.K[kk] = ld_frag(rt, OFFW_KT + ((cw * 4 + kk) * 64 + lane) * 16);
-    f.bet = ld_f4(rt, OFFW_BETA + (16 * cw + 4 * q4) * 4);
+    for (int kk = 0; kk < 4; ++kk) f.K[kk] = ld_frag(rt, OFF_KT + ((cw * 4 + kk) * 64 + lane) * 16);
+    f.bet = ld_f4(rt, OFF_BETA + (16 * cw + 4 * q4) * 4);
 #pragma unroll
-    for (int a = 0; a < 2; ++a) f.gam[a] = ld_f4(rt, OFFW_GAM + (32 * cw + 16 * a + 4 * q4) * 4);
+    for (int a = 0; a < 2; ++a) f.gam[a] = ld_f4(rt, OFF_GAM + (32 * cw + 16 * a + 4 * q4) * 4);
     const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, xoff, 0, 0);
     f.v = make_uint4(x[0], x[1], x[2], x[3]);
 }
@@ -316,17 +230,17 @@ __device__ __forceinline__ void chainw_load_b(ChainFragsW& f, __amdgpu_buffer_rs
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            f.W[a][kk] = ld_frag(rt, OFFW_WBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16);
+            f.W[a][kk] = ld_frag(rt, OFF_WBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16);
 }
 __device__ __forceinline__ void outw_load_a(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
                                             int lane) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) f.Q[kk] = ld_frag(rt, OFFW_QT + ((cw * 4 + kk) * 64 + lane) * 16);
+    for (int kk = 0; kk < 4; ++kk) f.Q[kk] = ld_frag(rt, OFF_QT + ((cw * 4 + kk) * 64 + lane) * 16);
 }
 __device__ __forceinline__ void outw_load_b(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
                                             int lane) {
-    f.P[0] = ld_frag(rt, OFFW_PT + (cw * 2 * 64 + lane) * 16);
-    if (cw >= 2) f.P[1] = ld_frag(rt, OFFW_PT + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
+    f.P[0] = ld_frag(rt, OFF_PT + (cw * 2 * 64 + lane) * 16);
+    if (cw >= 2) f.P[1] = ld_frag(rt, OFF_PT + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
 }
 
 // [C] S <- G + Wb^T R (R from Rt); the raw S to snp (a snapshot) when snp is
