@@ -26,6 +26,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "KDA layer tokens/s (H=64,d=128 prefill); decode state GB/s vs HBM peak"
+# Context from the pages, not targets.  Page "Ling-3.1-flash and the 7:1 hybrid: how
+# much KV cache does a 560B model need at 1M tokens?": the model's 63 KDA layers keep a
+# constant fp32 state of 264.2 MB per sequence (section "How big is the cache per token,
+# exactly?"), and the Kimi Linear report claims up to 6x faster decoding at 1M tokens for
+# its hybrid against full attention, on hardware the page does not name (section "Why
+# would a model keep only 9 full-attention layers?").
+KDA_LAYERS = 63
+KIMI_LINEAR_DECODE_CLAIM = ("up to 6x faster decoding at 1M tokens (Kimi Linear hybrid "
+                            "against full attention; hardware not stated)")
 # The prefill is one call of kda_prefill_chunked: per window of up to 32 chunks, a
 # chunk-parallel operand kernel (prep_kernel) then the state pass (state_kernel).
 # Its roofline is taken over the whole call.
@@ -375,6 +384,15 @@ def main():
             result.update({"value": B / (step_ms * 1e-3), "unit": "tokens/s",
                            "ms_per_step": step_ms})
         result["decode"] = dec
+        # one decode step of all 63 KDA layers for one sequence reads and writes the
+        # whole 63-layer state once: its time at the measured state bandwidth
+        model_state = KDA_LAYERS * kda.kda_state_bytes(H, d, d)
+        result["pages_context"] = {
+            "kda_state_bytes_per_sequence_63_layers": model_state,
+            "decode_state_us_per_token_63_layers": 2 * model_state / (gbs * 1e9) * 1e6,
+            "decode_tokens_per_s_63_layers_state_bound": gbs * 1e9 / (2 * model_state),
+            "kimi_linear_decode_claim": KIMI_LINEAR_DECODE_CLAIM,
+        }
         del q, k, v, g, beta, state, o, inp
 
     if args.only == "decode_bf16_state" or (args.only is None and not args.no_decode):
