@@ -52,14 +52,24 @@
 extern "C" {
 #endif
 
-typedef enum kda_status {
+/* The enumerations are int-sized in C.  Compiled as C++ they get int as their
+ * fixed underlying type, so that any int a caller passes (an out-of-range code
+ * included, which the entry points reject) is a valid value of the parameter's
+ * type rather than undefined behaviour. */
+#ifdef __cplusplus
+#define KDA_ENUM_BASE : int
+#else
+#define KDA_ENUM_BASE
+#endif
+
+typedef enum kda_status KDA_ENUM_BASE {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad cu_seqlens */
     KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k != d_v) */
     KDA_ERR_HIP = 3               /* a HIP runtime call failed; see kda_last_error_detail */
 } kda_status;
 
-typedef enum kda_dtype {
+typedef enum kda_dtype KDA_ENUM_BASE {
     KDA_F32 = 0,
     KDA_BF16 = 1
 } kda_dtype;
@@ -69,7 +79,7 @@ typedef enum kda_dtype {
  * page "Ling-3.1-flash and the 7:1 hybrid: how much KV cache does a 560B model
  * need at 1M tokens?" (section "Why would a model keep only 9 full-attention
  * layers?") names as the layer KDA extends with finer-grained gating. */
-typedef enum kda_gate {
+typedef enum kda_gate KDA_ENUM_BASE {
     KDA_GATE_CHANNEL = 0, /* g [tokens, H, d_k] fp32: alpha_t per key channel (KDA) */
     KDA_GATE_HEAD = 1,    /* g [tokens, H] fp32: one alpha_t per head, all channels */
     KDA_GATE_PROJ = 2     /* gate prologue fused in: see below */
