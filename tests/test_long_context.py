@@ -1,0 +1,82 @@
+"""One sequence of 1 048 576 tokens, the 1M-token context that page "Ling-3.1-flash
+and the 7:1 hybrid: how much KV cache does a 560B model need at 1M tokens?" is
+about, through the two-kernel prefill at H = 32, d = 128: q, k and v hold
+4.3e9 elements each, so element offsets pass 2^31 (the long packed workload
+stays below it).  Inputs are drawn on the device from a seeded generator, in
+slices, with the tiny workload's decay recipe (alpha = sigmoid(N(2, 0.5))).
+
+Checked against the oracle on two heads:
+- the first 4096 tokens' outputs, from the zero initial state;
+- the last 4096 tokens' outputs and the final state, against the oracle run on
+  the last 5120 tokens from a zero state.  At these decay rates the state
+  forgets: even a channel five standard deviations slow (alpha ~ 0.989) keeps
+  e^-11 of what it held 1024 tokens earlier, far below the bf16 tolerance, so
+  the tail needs no input from the GPU's own earlier state."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from kda_testutil import TOL_BF16, gpu_or_skip, np64, oracle_on, per_seq_errors
+
+pytestmark = pytest.mark.gpu
+
+T, H, D = 1 << 20, 32, 128
+WIN, WARM = 4096, 1024
+HEADS = [0, H - 1]
+
+
+def _inputs(dev):
+    gen = torch.Generator(device=dev).manual_seed(2024)
+    q = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    g = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    step = 1 << 16
+    for s in range(0, T, step):
+        e = s + step
+        for dst in (q, k):
+            x = torch.randn((step, H, D), generator=gen, device=dev)
+            dst[s:e] = (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        v[s:e] = torch.randn((step, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        g[s:e] = torch.nn.functional.logsigmoid(
+            torch.randn((step, H, D), generator=gen, device=dev) * 0.5 + 2.0)
+    beta = torch.sigmoid(torch.randn((T, H), generator=gen, device=dev))
+    return q, k, v, g, beta
+
+
+def _window(q, k, v, g, beta, lo, hi):
+    cpu = lambda x: x[lo:hi][:, HEADS].cpu()
+    return workloads.RecurrenceInputs(cpu(q), cpu(k), cpu(v), cpu(g), cpu(beta),
+                                      torch.tensor([0, hi - lo], dtype=torch.int32), None,
+                                      "bf16", 64)
+
+
+def test_million_token_prefill():
+    gpu_or_skip()
+    import gated_delta_rule_99_amd as kda
+
+    kda.load()
+    dev = "cuda"
+    q, k, v, g, beta = _inputs(dev)
+    cu_h = torch.tensor([0, T], dtype=torch.int32)
+    o, S = kda.kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=cu_h.to(dev),
+                                   cu_seqlens_host=cu_h, chunk=64)
+    torch.cuda.synchronize()
+
+    head = _window(q, k, v, g, beta, 0, WIN)
+    o_ref, _ = oracle_on(head)
+    e_head, _ = per_seq_errors(np64(o[:WIN][:, HEADS].cpu()), o_ref, None, None,
+                               head.cu_seqlens)
+
+    tail = _window(q, k, v, g, beta, T - WIN - WARM, T)
+    o_ref, S_ref = oracle_on(tail)
+    e_tail, e_state = per_seq_errors(np64(o[T - WIN:][:, HEADS].cpu()), o_ref[WARM:],
+                                     np64(S[:, HEADS].cpu()), S_ref,
+                                     torch.tensor([0, WIN], dtype=torch.int32))
+    print(f"1M-token prefill, heads {HEADS}: first {WIN} o {e_head:.2e}, last {WIN} o "
+          f"{e_tail:.2e}, final state {e_state:.2e}")
+    del q, k, v, g, beta, o, S
+    torch.cuda.empty_cache()
+    assert np.isfinite(e_head) and np.isfinite(e_tail) and np.isfinite(e_state)
+    assert e_head <= TOL_BF16 and e_tail <= TOL_BF16 and e_state <= TOL_BF16
