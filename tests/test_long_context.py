@@ -1,4 +1,6 @@
-"""One sequence of 1 048 576 tokens, the 1M-token context that page "Ling-3.1-flash
+"""Sizes past 2^31 elements.
+
+One sequence of 1 048 576 tokens, the 1M-token context that page "Ling-3.1-flash
 and the 7:1 hybrid: how much KV cache does a 560B model need at 1M tokens?" is
 about, through the two-kernel prefill at H = 32, d = 128: q, k and v hold
 4.3e9 elements each, so element offsets pass 2^31 (the long packed workload
@@ -11,7 +13,10 @@ Checked against the oracle on two heads:
   the last 5120 tokens from a zero state.  At these decay rates the state
   forgets: even a channel five standard deviations slow (alpha ~ 0.989) keeps
   e^-11 of what it held 1024 tokens earlier, far below the bf16 tolerance, so
-  the tail needs no input from the GPU's own earlier state."""
+  the tail needs no input from the GPU's own earlier state.
+
+And a decode step into a state pool of 4096 slots at H = 64 (4.3e9 fp32
+elements), through a slot table reaching its end."""
 import numpy as np
 import pytest
 import torch
@@ -80,3 +85,32 @@ def test_million_token_prefill():
     torch.cuda.empty_cache()
     assert np.isfinite(e_head) and np.isfinite(e_tail) and np.isfinite(e_state)
     assert e_head <= TOL_BF16 and e_tail <= TOL_BF16 and e_state <= TOL_BF16
+
+
+def test_decode_large_state_pool():
+    """Decode through a slot table into a pool of 4096 states at H = 64, d = 128
+    (4.3e9 fp32 elements, 17 GB): slots near the end of the pool lie past 2^31
+    elements.  Outputs and the updated states match the oracle; a slot between
+    them that no sequence maps to is left untouched, bit for bit."""
+    gpu_or_skip()
+    import gated_delta_rule_99_amd as kda
+
+    kda.load()
+    n_slots, Hd, B = 4096, 64, 8
+    slots = torch.tensor([4095, 4000, 3000, 2048, 1, 0, 4093, 2047], dtype=torch.int32)
+    inp = workloads.recurrence_inputs([1] * B, H=Hd, d=D, dtype="bf16", s0_std=0.3, seed=91)
+    pool = torch.empty((n_slots, Hd, D, D), dtype=torch.float32, device="cuda")
+    pool[slots.long().cuda()] = inp.S0.cuda()
+    pool[4094].fill_(0.25)
+    dev = lambda x: x.cuda()
+    o = kda.kda_decode_step(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), pool,
+                            slot_idx=dev(slots))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = per_seq_errors(np64(o.cpu()), o_ref, np64(pool[slots.long().cuda()].cpu()), S_ref,
+                            inp.cu_seqlens)
+    untouched = bool(torch.all(pool[4094] == 0.25))
+    print(f"decode into a 4096-slot pool: o {eo:.2e} S {es:.2e}")
+    del pool
+    torch.cuda.empty_cache()
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and untouched
