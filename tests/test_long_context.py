@@ -15,8 +15,9 @@ Checked against the oracle on two heads:
   e^-11 of what it held 1024 tokens earlier, far below the bf16 tolerance, so
   the tail needs no input from the GPU's own earlier state.
 
-And a decode step into a state pool of 4096 slots at H = 64 (4.3e9 fp32
-elements), through a slot table reaching its end."""
+A decode step into a state pool of 4096 slots at H = 64 (4.3e9 fp32
+elements), through a slot table reaching its end; and the short conv over a
+1M-token stream of 8192 channels (8.6e9 elements)."""
 import numpy as np
 import pytest
 import torch
@@ -114,3 +115,36 @@ def test_decode_large_state_pool():
     del pool
     torch.cuda.empty_cache()
     assert eo <= TOL_BF16 and es <= TOL_BF16 and untouched
+
+
+def test_conv_million_tokens():
+    """The short conv with the per-head L2 norm over one 1 048 576-token stream of
+    8192 bf16 channels (8.6e9 elements): the last 64 rows, and the outgoing
+    tail, against the oracle run on those rows with the three rows before them
+    (inputs, not GPU results) as its incoming tail."""
+    gpu_or_skip()
+    import gated_delta_rule_99_amd as kda
+    import oracle
+
+    kda.load()
+    Tc, C, hd, n = 1 << 20, 8192, 128, 64
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    x = torch.empty((Tc, C), dtype=torch.bfloat16, device="cuda")
+    for s in range(0, Tc, 1 << 17):
+        x[s:s + (1 << 17)] = torch.randn((1 << 17, C), generator=gen, device="cuda").to(
+            torch.bfloat16)
+    w = torch.randn((C, 4), generator=gen, device="cuda") * 0.5
+    cu = torch.tensor([0, Tc], dtype=torch.int32)
+    tail_out = torch.empty((1, 3, C), dtype=torch.bfloat16, device="cuda")
+    y = kda.kda_short_conv_prefill(x, w, cu_seqlens=cu.cuda(), cu_seqlens_host=cu,
+                                   l2_head_dim=hd, conv_tail_out=tail_out)
+    torch.cuda.synchronize()
+    xs = np64(x[Tc - n - 3:].cpu())
+    y_ref, tail_ref = oracle.short_conv(xs[3:], np64(w.cpu()), tail=xs[None, :3])
+    y_ref = oracle.l2norm_heads(y_ref, hd, eps=1e-6)
+    err = float(np.linalg.norm(np64(y[Tc - n:].cpu()) - y_ref) / np.linalg.norm(y_ref))
+    tail_ok = bool(np.array_equal(np64(tail_out.cpu()), tail_ref))
+    print(f"conv over 1M tokens x {C} channels, last {n} rows: {err:.2e}")
+    del x, y
+    torch.cuda.empty_cache()
+    assert err <= 1e-2 and tail_ok
