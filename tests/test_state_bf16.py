@@ -60,7 +60,7 @@ def test_state_init_converts():
 
 
 @pytest.mark.parametrize("n_tok", [1, 4])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
 def test_decode_bf16_state_matches_rounded_oracle(d, n_tok):
     """One call of n_tok tokens on bf16 states, through a slot permutation: the
     outputs match the oracle run from the stored values, and every written
@@ -153,3 +153,55 @@ def test_decode_bf16_token_states():
         got = snaps[:, j].float().cpu().double().numpy()
         assert within_rounding(got, want)
         assert max(rel_fro(got[b], S_ref[b]) for b in range(B)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("n_tok", [1, 4])
+@pytest.mark.parametrize("gate", ["head", "proj"])
+def test_decode_bf16_state_gate_forms(gate, n_tok):
+    """bf16 states with the other decay inputs: one decay per head (g [.., H]
+    broadcast over the key channels), and the fused gate prologue (the decay
+    projection f, one log rate per head, beta logits; the oracle applies
+    oracle.gate_prologue to the same values).  Outputs match the oracle run
+    from the stored values, the written states its final state rounded to
+    bf16, and slots no sequence maps to stay zero."""
+    m = kda()
+    B, H, d, n_slots = 5, 3, 128, 8
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", s0_std=0.3,
+                                      seed=430 + n_tok, gate=gate if gate == "head" else "channel")
+    S0 = torch.from_numpy(oracle.round_bf16(inp.S0.double().numpy())).float()
+    if gate == "proj":
+        pr = workloads.gate_projections(inp.T, H, d, dtype="bf16", g_mu=2.0, g_sigma=0.5,
+                                        a_log_std=0.5, seed=430 + n_tok)
+        g, beta = oracle.gate_prologue(np64(pr.f), np64(pr.a_log), np64(pr.b))
+        g_in, b_in, a_log = pr.f, pr.b, dev(pr.a_log)
+        g, beta = torch.from_numpy(g), torch.from_numpy(beta)
+    else:
+        g_in, b_in, a_log = inp.g, inp.beta, None
+        g, beta = inp.g, inp.beta
+    pool = torch.zeros((n_slots, H, d, d))
+    slots = torch.tensor([6, 1, 3, 0, 7], dtype=torch.int32)
+    pool[slots.long()] = S0
+    state = dev(pool.to(torch.bfloat16))
+    if n_tok == 1:
+        o = m.kda_decode_step(dev(inp.q), dev(inp.k), dev(inp.v), dev(g_in), dev(b_in), state,
+                              slot_idx=dev(slots), a_log=a_log)
+    else:
+        t = lambda x: dev(x.reshape((B, n_tok) + tuple(x.shape[1:])))
+        o, _ = m.kda_decode_tokens(t(inp.q), t(inp.k), t(inp.v), t(g_in), t(b_in), state,
+                                   slot_idx=dev(slots), a_log=a_log)
+    torch.cuda.synchronize()
+    ref = workloads.RecurrenceInputs(inp.q, inp.k, inp.v, g, beta, inp.cu_seqlens, S0, "bf16",
+                                     inp.chunk)
+    o_ref, S_ref = oracle_on(ref)
+    S_gpu = state.float().cpu().double().numpy()[slots.long().numpy()]
+    S_want = oracle.round_bf16(S_ref)
+    eo, es = per_seq_errors(np64(o).reshape(B * n_tok, H, d), o_ref, S_gpu, S_ref,
+                            inp.cu_seqlens)
+    exact = float(np.mean(S_gpu == S_want))
+    print(f"bf16 state, {gate} gate, n_tok={n_tok}: o {eo:.2e} S {es:.2e}, "
+          f"state elements equal {exact:.5f}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert within_rounding(S_gpu, S_want)
+    assert exact >= 0.999
+    untouched = [s for s in range(n_slots) if s not in slots.tolist()]
+    assert not state[untouched].float().abs().sum().item()
