@@ -32,7 +32,8 @@ def run_tokens(m, inp, B, n_tok, state, slot_idx=None, token_states=None):
 
 
 @pytest.mark.parametrize("n_tok", [1, 4])
-@pytest.mark.parametrize("d,dtype", [(32, "f32"), (64, "bf16"), (128, "bf16")])
+@pytest.mark.parametrize("d,dtype", [(16, "f32"), (16, "bf16"), (32, "f32"), (64, "bf16"),
+                                     (128, "bf16"), (128, "f32")])
 def test_decode_tokens_matches_oracle(d, dtype, n_tok):
     """B sequences advanced by n_tok tokens through a slot permutation into a
     larger pool: outputs of every token and the final states match the oracle;
@@ -58,12 +59,14 @@ def test_decode_tokens_matches_oracle(d, dtype, n_tok):
     assert torch.equal(st[untouched], pool[untouched])
 
 
-def test_decode_tokens_snapshots_match_prefixes():
+@pytest.mark.parametrize("d,dtype", [(16, "f32"), (128, "bf16")])
+def test_decode_tokens_snapshots_match_prefixes(d, dtype):
     """token_states[b, j] is sequence b's state after token j: it matches the
     oracle run on the first j + 1 tokens, and the last one is the final state."""
     m = kda()
-    B, n_tok, H, d = 3, 4, 2, 128
-    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", s0_std=0.3, seed=71)
+    B, n_tok, H = 3, 4, 2
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype=dtype, s0_std=0.3,
+                                      seed=71 + d)
     state = dev(inp.S0)
     o, snaps = run_tokens(m, inp, B, n_tok, state, token_states=True)
     torch.cuda.synchronize()
@@ -74,11 +77,11 @@ def test_decode_tokens_snapshots_match_prefixes():
                                          inp.beta[rows],
                                          torch.arange(0, B * (j + 1) + 1, j + 1,
                                                       dtype=torch.int32),
-                                         inp.S0, "bf16", inp.chunk)
+                                         inp.S0, dtype, inp.chunk)
         _, S_ref = oracle_on(pre)
         err = max(rel_fro(np64(snaps[b, j]), S_ref[b]) for b in range(B))
-        print(f"snapshot after token {j}: {err:.2e}")
-        assert err <= TOL_BF16
+        print(f"d={d} {dtype}, snapshot after token {j}: {err:.2e}")
+        assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
     assert torch.equal(snaps[:, -1], state.cpu())
 
 
