@@ -93,3 +93,36 @@ def test_prefill_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(o, o_e), r
         assert torch.equal(S, S_e), r
+
+
+def test_decode_tokens_graph_replays():
+    """Multi-token decode (3 tokens per sequence, per-token snapshots, bf16
+    states through a slot table) recorded once: every replay equals the eager
+    call from the same starting states, outputs and snapshots included."""
+    m = kda()
+    B, n_tok, H, d, n_slots = 8, 3, 4, 128, 12
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype="bf16", s0_std=0.3, seed=81)
+    t = lambda x: dev(x.reshape((B, n_tok) + tuple(x.shape[1:])))
+    q, k, v, g, b = (t(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    slots = dev(torch.tensor([11, 0, 5, 3, 9, 1, 7, 2], dtype=torch.int32))
+    pool = torch.zeros((n_slots, H, d, d), dtype=torch.bfloat16, device="cuda")
+    pool[slots.long()] = dev(inp.S0).to(torch.bfloat16)
+    want = []
+    s_eager = pool.clone()
+    for _ in range(3):
+        o, snaps = m.kda_decode_tokens(q, k, v, g, b, s_eager, slot_idx=slots, token_states=True)
+        want.append((o.clone(), snaps.clone(), s_eager.clone()))
+    s_graph = pool.clone()
+    o_graph = torch.empty_like(want[0][0])
+    snap_graph = torch.empty_like(want[0][1])
+    graph = capture(lambda: m.kda_decode_tokens(q, k, v, g, b, s_graph, slot_idx=slots,
+                                                o=o_graph, token_states=snap_graph))
+    s_graph.copy_(pool)  # the warm-up call advanced it once
+    torch.cuda.synchronize()
+    for r in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph, want[r][0]), r
+        assert torch.equal(snap_graph, want[r][1]), r
+        assert torch.equal(s_graph, want[r][2]), r
+        _ = (v.float() * 2).sum().item()  # eager work between replays
