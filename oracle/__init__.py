@@ -41,12 +41,10 @@ SRC = os.path.join(HERE, "kda_oracle.c")
 LIB = os.path.join(HERE, "libkda_oracle.so")
 
 
-def build(out: str = LIB, mutant: int = 0) -> str:
-    """Compile the C oracle with gcc.  ``mutant`` plants a deliberate mistake
-    (pin tests only); the default build has none."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", SRC, "-o", out, "-lm"]
-    if mutant:
-        cmd.insert(1, f"-DKDA_ORACLE_MUTANT={int(mutant)}")
+def build(out: str = LIB, src: str = SRC) -> str:
+    """Compile the C oracle with gcc (``src``: this package's kda_oracle.c; the
+    pin tests pass patched copies of it)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -81,9 +79,7 @@ class Oracle:
         lib.kda_oracle_l2norm_heads_f64.restype = ctypes.c_int
         lib.kda_oracle_l2norm_heads_f64.argtypes = [_dp, ctypes.c_int64, ctypes.c_int,
                                                     ctypes.c_int, ctypes.c_double]
-        lib.kda_oracle_mutant.restype = ctypes.c_int
         self.lib = lib
-        self.mutant = lib.kda_oracle_mutant()
 
     # ------------------------------------------------------------------ recurrence
     def recurrence(self, q, k, v, g, beta, cu_seqlens=None, S0=None, precision="f64",

@@ -42,9 +42,9 @@
  * (sequence, head) pairs over threads; tokens are always processed in order.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC kda_oracle.c -o libkda_oracle.so -lm
- * Compiling with -DKDA_ORACLE_MUTANT=<n> plants one deliberate mistake (see
- * the MUTANT switch below); the pin tests use those builds to show that every
- * planted mistake is caught.  The default build has no mutant.
+ * (The pin tests also compile patched copies of this file, each with one
+ * planted mistake, to show that every such mistake fails a pin; the file itself
+ * holds no switch for them.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,16 +54,10 @@
 #include <omp.h>
 #endif
 
-#ifndef KDA_ORACLE_MUTANT
-#define KDA_ORACLE_MUTANT 0
-#endif
-
 /* Return codes. */
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARG 1
 #define ORACLE_NO_MEM 2
-
-int kda_oracle_mutant(void) { return KDA_ORACLE_MUTANT; }
 
 static int check_cu(const int32_t* cu, int n_seqs) {
     if (!cu || n_seqs < 0) return 0;
@@ -117,53 +111,23 @@ int kda_oracle_recurrence_##SUFFIX(const REAL* q, const REAL* k, const REAL* v, 
                     const REAL bt = beta[(size_t)t * H + h];                               \
                     REAL* ot = o + ((size_t)t * H + h) * dv;                               \
                     /* alpha_t = exp(g_t), one factor per key channel */                   \
-                    for (int i = 0; i < dk; ++i)                                           \
-                        alpha[i] = (KDA_ORACLE_MUTANT == 6) ? (REAL)EXPF(-gt[i])           \
-                                                            : (REAL)EXPF(gt[i]);           \
+                    for (int i = 0; i < dk; ++i) alpha[i] = (REAL)EXPF(gt[i]);             \
                     /* S' = Diag(alpha_t) S_{t-1}: row i (key channel i) scaled */         \
-                    if (KDA_ORACLE_MUTANT != 1) {                                          \
-                        for (int i = 0; i < dk; ++i)                                       \
-                            for (int j = 0; j < dv; ++j)                                   \
-                                S[(size_t)i * dv + j] *= (KDA_ORACLE_MUTANT == 3)          \
-                                    ? alpha[j % dk] : alpha[i];                            \
-                    }                                                                      \
+                    for (int i = 0; i < dk; ++i)                                           \
+                        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha[i];    \
                     /* y = S'^T k_t */                                                     \
                     for (int j = 0; j < dv; ++j) y[j] = 0;                                 \
                     for (int i = 0; i < dk; ++i)                                           \
-                        for (int j = 0; j < dv; ++j)                                       \
-                            y[j] += S[(size_t)i * dv + j] * kt[i];                         \
+                        for (int j = 0; j < dv; ++j) y[j] += S[(size_t)i * dv + j] * kt[i];\
                     /* u_t = beta_t (v_t - y) */                                           \
-                    for (int j = 0; j < dv; ++j) {                                         \
-                        if (KDA_ORACLE_MUTANT == 4) u[j] = bt * (vt[j] + y[j]);            \
-                        else if (KDA_ORACLE_MUTANT == 5) u[j] = bt * vt[j] - y[j];         \
-                        else u[j] = bt * (vt[j] - y[j]);                                   \
-                    }                                                                      \
-                    if (KDA_ORACLE_MUTANT == 2) {                                          \
-                        /* planted: read before the write */                               \
-                        for (int j = 0; j < dv; ++j) ot[j] = 0;                            \
-                        for (int i = 0; i < dk; ++i)                                       \
-                            for (int j = 0; j < dv; ++j)                                   \
-                                ot[j] += S[(size_t)i * dv + j] * qt[i];                    \
-                    }                                                                      \
+                    for (int j = 0; j < dv; ++j) u[j] = bt * (vt[j] - y[j]);               \
                     /* S_t = S' + k_t u_t^T */                                             \
                     for (int i = 0; i < dk; ++i)                                           \
-                        for (int j = 0; j < dv; ++j)                                       \
-                            S[(size_t)i * dv + j] +=                                       \
-                                ((KDA_ORACLE_MUTANT == 7) ? (REAL)1 : kt[i]) * u[j];       \
-                    if (KDA_ORACLE_MUTANT == 1) {                                          \
-                        /* planted: decay after the write instead of before */             \
-                        for (int i = 0; i < dk; ++i)                                       \
-                            for (int j = 0; j < dv; ++j)                                   \
-                                S[(size_t)i * dv + j] *= alpha[i];                         \
-                    }                                                                      \
+                        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += kt[i] * u[j];\
                     /* o_t = S_t^T q_t */                                                  \
-                    if (KDA_ORACLE_MUTANT != 2) {                                          \
-                        const REAL* rd = (KDA_ORACLE_MUTANT == 8) ? kt : qt;               \
-                        for (int j = 0; j < dv; ++j) ot[j] = 0;                            \
-                        for (int i = 0; i < dk; ++i)                                       \
-                            for (int j = 0; j < dv; ++j)                                   \
-                                ot[j] += S[(size_t)i * dv + j] * rd[i];                    \
-                    }                                                                      \
+                    for (int j = 0; j < dv; ++j) ot[j] = 0;                                \
+                    for (int i = 0; i < dk; ++i)                                           \
+                        for (int j = 0; j < dv; ++j) ot[j] += S[(size_t)i * dv + j] * qt[i];\
                 }                                                                          \
                 if (S_final) memcpy(S_final + sidx, S, sizeof(REAL) * (size_t)dk * dv);    \
             }                                                                              \

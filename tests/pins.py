@@ -295,4 +295,17 @@ def pin_l2norm(orc):
     assert np.allclose(cos, 1.0, rtol=1e-14)
 
 
-CONV_PINS = [pin_conv_identity_tap, pin_conv_numpy, pin_conv_handoff, pin_l2norm]
+def pin_l2norm_eps(orc):
+    """Where eps enters: inside the square root, x / sqrt(sum x^2 + eps).  Two
+    rows whose sum of squares is comparable to eps, with values fixed by hand:
+    (3, 4) with eps = 11 gives (3, 4) / sqrt(36) = (1/2, 2/3); four channels of
+    0.05 with eps = 0.01 (sum of squares 0.01) give 0.05 / sqrt(0.02) = 1/sqrt(8)
+    each.  eps added outside the root, or dropped, or squared, misses both."""
+    y = orc.l2norm_heads(np.array([[3.0, 4.0]]), 2, eps=11.0)
+    assert np.allclose(y, [[0.5, 2.0 / 3.0]], rtol=1e-15, atol=0), y
+    y = orc.l2norm_heads(np.full((1, 8), 0.05), 4, eps=0.01)
+    assert np.allclose(y, 1.0 / np.sqrt(8.0), rtol=1e-14, atol=0), y
+
+
+CONV_PINS = [pin_conv_identity_tap, pin_conv_numpy, pin_conv_handoff, pin_l2norm,
+             pin_l2norm_eps]
