@@ -104,6 +104,7 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
         case KDA_ERR_HIP: return "KDA_ERR_HIP";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -221,7 +222,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     const size_t ws_need = mfma ? kda::prefill_split_workspace_bytes(n_seqs, H) : 0;
     if (mfma && workspace) {
         if (workspace_bytes < ws_need)
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes, %zu needed", fn,
+            return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn,
                         workspace_bytes, ws_need);
         if (!aligned16(workspace))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned workspace", fn);

@@ -22,6 +22,7 @@
 #include <vector>
 
 #include "kda_state_pass.h"
+#include "kda_window_plan.h"
 
 namespace kda {
 namespace sp {
@@ -212,7 +213,11 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
 
 // ---------------------------------------------------------------- state pass
 // grid n_pairs * NS, n_pairs = (ranked sequences in the window) * H, the slices
-// of one head placed on one XCD; 8 waves: the chain waves form R, then
+// of one head placed on one XCD.  Ranks at or above n_prep have no tiles in
+// this window (prep_kernel ran for the first n_prep ranks only): they are
+// treated as having no chunks, whatever the device's cu_seqlens says, so a
+// device copy that disagrees with the host copy cannot send a tile access past
+// the ranks that own tiles; 8 waves: the chain waves form R, then
 // S <- G + Wb^T R and the next G; the output waves form Z = Qt G, then
 // O = Z + PT R; two barriers per chunk (R complete, next G complete).
 // Fragments come straight from the tiles into registers, two chunks ahead
@@ -220,7 +225,7 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
 __global__ void __launch_bounds__(512)
 state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
              const int32_t* __restrict__ order, int64_t T, int H,
-             int n_pairs, int w0, int win, const uint8_t* __restrict__ ws_tiles,
+             int n_pairs, int n_prep, int w0, int win, const uint8_t* __restrict__ ws_tiles,
              float* __restrict__ ws_state, const float* __restrict__ s0,
              float* __restrict__ s_final, bf16_t* __restrict__ o, Snapshots snap) {
     __shared__ __attribute__((aligned(16))) StateLds sm;
@@ -242,6 +247,7 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
     int64_t tb, te;
     int nc;
     seq_chunks(cu, n, T, tb, te, nc);
+    if (slot >= n_prep) nc = 0;
     const int c_beg = w0, c_end = min(nc, w0 + win);
     const bool first_window = w0 == 0, last_here = c_end == nc;
     const int tid = threadIdx.x, wave = tid >> 6, cw = wave & 3, lane = tid & 63;
@@ -438,7 +444,6 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gat
     std::vector<int> len(n_seqs);
     for (int n = 0; n < n_seqs; ++n) len[n] = (int)(((int64_t)cu_host[n + 1] - cu_host[n] + C - 1) / C);
     std::sort(len.begin(), len.end(), [](int a, int b) { return a > b; });
-    const int max_chunks = len[0];
     float* ws_state = reinterpret_cast<float*>(workspace);
     int32_t* order = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) +
                                                 (size_t)n_seqs * H * D * D * 4);
@@ -463,31 +468,20 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gat
     auto prep = g.mode == GATE_HEAD   ? prep_kernel<GATE_HEAD>
                 : g.mode == GATE_PROJ ? prep_kernel<GATE_PROJ>
                                       : prep_kernel<GATE_CH>;
-    int w0 = 0;
-    do {
-        // ranks still running at chunk w0; the first window also visits the
-        // empty sequences, whose final states are their initial ones
-        int active = 0;
-        while (active < n_seqs && len[active] > w0) ++active;
-        if (!ranked) active = n_seqs;  // identity order: every sequence takes part
-        const int visit = w0 == 0 ? n_seqs : active;
-        size_t w = active ? tbytes / ((size_t)active * H * TILE) : 1;
-        const int win = w < 1 ? 1 : (w > (size_t)MAX_WIN ? MAX_WIN : (int)w);
-        const int rows = max_chunks - w0 < win ? max_chunks - w0 : win;
-        if (rows > 0 && active > 0) {
-            hipLaunchKernelGGL(prep, dim3((unsigned)(active * H), (unsigned)rows), dim3(256), 0,
-                               stream, (const bf16_t*)q, (const bf16_t*)k, g, beta, cu, order, T,
-                               H, w0, win, tiles);
+    for (const Window& wd : plan_windows(len, ranked, H, tbytes, TILE, MAX_WIN)) {
+        if (wd.rows > 0 && wd.active > 0) {
+            hipLaunchKernelGGL(prep, dim3((unsigned)(wd.active * H), (unsigned)wd.rows),
+                               dim3(256), 0, stream, (const bf16_t*)q, (const bf16_t*)k, g, beta,
+                               cu, order, T, H, wd.w0, wd.win, tiles);
             err = hipGetLastError();
             if (err != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(state_kernel, dim3((unsigned)((int64_t)visit * H * NS)), dim3(512), 0,
-                           stream, (const bf16_t*)v, cu, order, T, H, visit * H, w0, win, tiles,
-                           ws_state, s0, s_final, (bf16_t*)o, snap);
+        hipLaunchKernelGGL(state_kernel, dim3((unsigned)((int64_t)wd.visit * H * NS)), dim3(512),
+                           0, stream, (const bf16_t*)v, cu, order, T, H, wd.visit * H, wd.active,
+                           wd.w0, wd.win, tiles, ws_state, s0, s_final, (bf16_t*)o, snap);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
-        w0 += win;
-    } while (w0 < max_chunks);
+    }
     return hipSuccess;
 }
 

@@ -66,7 +66,8 @@ typedef enum kda_status KDA_ENUM_BASE {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad cu_seqlens */
     KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k != d_v) */
-    KDA_ERR_HIP = 3               /* a HIP runtime call failed; see kda_last_error_detail */
+    KDA_ERR_HIP = 3,              /* a HIP runtime call failed; see kda_last_error_detail */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 4 /* a workspace below the size its query returns */
 } kda_status;
 
 typedef enum kda_dtype KDA_ENUM_BASE {
@@ -187,10 +188,9 @@ kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, i
  * dimension).  Every other case runs the fp32 vector kernel and ignores the
  * workspace.  T = 0 or n_seqs = 0 is valid: final states of empty sequences
  * equal their initial states.
- * Numerical range: the per-chunk sum of g on any channel must stay above about
- * -80 (exp of its negative must be finite in fp32).
- * Errors: KDA_ERR_INVALID_ARGUMENT also for a non-NULL workspace smaller than
- * kda_prefill_workspace_bytes or overlapping another argument.
+ * Errors: KDA_ERR_WORKSPACE_TOO_SMALL for a non-NULL workspace smaller than
+ * kda_prefill_workspace_bytes; KDA_ERR_INVALID_ARGUMENT for a misaligned one
+ * or one that overlaps another argument.
  */
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
                                const void* g, const float* beta, kda_dtype dtype, kda_gate gate,

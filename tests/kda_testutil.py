@@ -1,10 +1,23 @@
 """Helpers shared by the GPU parity tests: device plumbing, oracle calls on the
-exact inputs the GPU sees, and the error measure.
+exact inputs the GPU sees, and the error measures.
 
-Error measure: for each sequence n, separately for the outputs o and for the
-final state, the relative Frobenius error ||X_gpu - X_ref||_F / ||X_ref||_F; a
-case passes when the largest of these is within the tolerance (1e-4 for fp32
-inputs, 2e-2 for bf16 inputs with fp32 state).
+The reference is the oracle's fp64 build run on exactly the values the GPU
+reads (bf16 inputs widened exactly).  That is a stricter reading of "the fp32
+CPU recurrence" than the fp32 build itself: the fp32 build is pinned to lie
+within 1e-5 of the fp64 one (``pins.pin_f32_close_to_f64``), far inside every
+tolerance below, so the GPU's error is measured against the exact recurrence
+rather than against another rounding of it.
+
+Error measures (``assert_parity``), all against one tolerance tol (1e-4 for
+fp32 inputs, 2e-2 for bf16 inputs with fp32 state):
+  * per sequence n, separately for o and the final state S:
+    ||X_gpu - X_ref||_F / ||X_ref||_F  (the headline measure);
+  * per (sequence, head), the same ratio for o and for S, so that one wrong
+    head cannot hide among many right ones;
+  * per row: every (token, head) row of o and every (sequence, head, key
+    channel) row of S must satisfy ||x_gpu - x_ref|| <= tol * max(||x_ref||,
+    median row norm of the case), so that one wrong token or chunk cannot hide
+    in a long sequence.
 """
 from __future__ import annotations
 
@@ -39,16 +52,53 @@ def rel_fro(a, ref):
     return float(num / den)
 
 
-def per_seq_errors(o_gpu, o_ref, S_gpu, S_ref, cu):
-    """Max over sequences of the relative Frobenius errors of o and of S."""
+def _row_ratio(x, ref):
+    """max over rows (last axis) of ||x - ref|| / max(||ref||, median ||ref||)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rn = np.linalg.norm(ref.reshape(-1, ref.shape[-1]), axis=-1)
+    en = np.linalg.norm((x - ref).reshape(-1, ref.shape[-1]), axis=-1)
+    floor = float(np.median(rn))
+    scale = np.maximum(rn, floor)
+    if floor == 0.0:
+        scale = np.where(scale == 0.0, 1.0, scale)
+    return float(np.max(en / scale))
+
+
+def parity_stats(o_gpu, o_ref, S_gpu, S_ref, cu):
+    """Error measures of a case: o [T, H, dv] and S [n, H, dk, dv] (either
+    reference may be None: not compared), cu the n + 1 sequence offsets.  Returns the maxima over sequences, over
+    (sequence, head) pairs and over rows (see the module docstring)."""
     cu = [int(c) for c in cu]
-    eo, es = 0.0, 0.0
+    st = {"seq_o": 0.0, "seq_S": 0.0, "head_o": 0.0, "head_S": 0.0}
+    if o_ref is not None:
+        o_gpu = np.asarray(o_gpu, dtype=np.float64)
+        o_ref = np.asarray(o_ref, dtype=np.float64)
+        H = o_ref.shape[1]
     for n in range(len(cu) - 1):
-        if cu[n + 1] > cu[n]:
-            eo = max(eo, rel_fro(o_gpu[cu[n]:cu[n + 1]], o_ref[cu[n]:cu[n + 1]]))
+        a, b = cu[n], cu[n + 1]
+        if b > a and o_ref is not None:
+            st["seq_o"] = max(st["seq_o"], rel_fro(o_gpu[a:b], o_ref[a:b]))
+            for h in range(H):
+                st["head_o"] = max(st["head_o"], rel_fro(o_gpu[a:b, h], o_ref[a:b, h]))
         if S_ref is not None:
-            es = max(es, rel_fro(S_gpu[n], S_ref[n]))
-    return eo, es
+            st["seq_S"] = max(st["seq_S"], rel_fro(S_gpu[n], S_ref[n]))
+            for h in range(S_ref.shape[1]):
+                st["head_S"] = max(st["head_S"], rel_fro(S_gpu[n, h], S_ref[n, h]))
+    st["row_o"] = _row_ratio(o_gpu, o_ref) if o_ref is not None else 0.0
+    st["row_S"] = _row_ratio(S_gpu, S_ref) if S_ref is not None else 0.0
+    return st
+
+
+def assert_parity(o_gpu, o_ref, S_gpu, S_ref, cu, tol, label=""):
+    """Assert every measure of ``parity_stats`` within tol; print them."""
+    st = parity_stats(o_gpu, o_ref, S_gpu, S_ref, cu)
+    print(f"{label}: " + " ".join(f"{k} {v:.2e}" for k, v in st.items()))
+    bad = {k: v for k, v in st.items() if not v <= tol}
+    assert not bad, f"{label}: above {tol:g}: {bad}"
+    return st
 
 
 def oracle_on(inp, heads=None, precision="f64"):

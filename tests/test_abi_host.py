@@ -10,7 +10,7 @@ import pytest
 
 import gated_delta_rule_99_amd as kda_pkg
 from gated_delta_rule_99_amd.kda import (KDA_BF16, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED,
-                                          KDA_F32)
+                                          KDA_ERR_WORKSPACE_TOO_SMALL, KDA_F32)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -49,6 +49,7 @@ def test_state_bytes(lib):
     assert lib.kda_state_bytes(64, 128, 128, 7) == 0
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(4) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
 
 
 def cu_arr(vals):
@@ -89,7 +90,7 @@ def prefill(lib, **kw):
     (dict(o=A + 64), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(s0=0x7000000, sf=0x7000040), KDA_ERR_INVALID_ARGUMENT, "overlap"),
     (dict(sf=A), KDA_ERR_INVALID_ARGUMENT, "overlap"),
-    (dict(ws=0x9000000, ws_bytes=1024), KDA_ERR_INVALID_ARGUMENT, "needed"),
+    (dict(ws=0x9000000, ws_bytes=1024), KDA_ERR_WORKSPACE_TOO_SMALL, "needed"),
     (dict(ws=0x9000008, ws_bytes=1 << 30), KDA_ERR_INVALID_ARGUMENT, "misaligned workspace"),
     (dict(ws=A - 4096, ws_bytes=1 << 30), KDA_ERR_INVALID_ARGUMENT, "workspace overlaps"),
     (dict(snaps=Hp, snap_interval=48, snap_capacity=1), KDA_ERR_INVALID_ARGUMENT,
@@ -261,10 +262,110 @@ def test_conv_decode_rejects(lib):
         KDA_ERR_INVALID_ARGUMENT
 
 
-def test_python_binding_raises_on_error():
-    """The binding turns a non-OK status into KdaError (no fallback)."""
-    import torch
-    q = torch.zeros((4, 2, 96))
+def test_python_binding_raises_on_error(lib):
+    """The binding turns a non-OK status into KdaError with the library's detail
+    (no fallback)."""
+    from gated_delta_rule_99_amd import kda as binding
+    assert prefill(lib, dk=96, dv=96) == KDA_ERR_UNSUPPORTED
     with pytest.raises(kda_pkg.KdaError) as ei:
-        kda_pkg.kda_prefill_chunked(q, q, q, q, torch.zeros((4, 2)), chunk=64, stream=0)
-    assert ei.value.status == KDA_ERR_UNSUPPORTED
+        binding._check(KDA_ERR_UNSUPPORTED)
+    assert ei.value.status == KDA_ERR_UNSUPPORTED and "head dim" in ei.value.detail
+
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.float32)
+
+
+def _prefill_args(T=8, H=2, d=128, n=1, bf16=True):
+    import torch
+    dt = torch.bfloat16 if bf16 else torch.float32
+    cu = torch.tensor([0, T] if n == 1 else [0, T // 2, T], dtype=torch.int32)
+    return dict(q=_t(T, H, d, dtype=dt), k=_t(T, H, d, dtype=dt), v=_t(T, H, d, dtype=dt),
+                g=_t(T, H, d), beta=_t(T, H), cu_seqlens=cu)
+
+
+def _call_prefill(args, **kw):
+    a = dict(args)
+    a.update(kw)
+    return kda_pkg.kda_prefill_chunked(a.pop("q"), a.pop("k"), a.pop("v"), a.pop("g"),
+                                       a.pop("beta"), **a)
+
+
+@pytest.mark.parametrize("change,err,needle", [
+    # the host cu_seqlens must end at the tokens the tensors hold
+    (dict(cu_seqlens="long"), ValueError, "cu_seqlens ends at"),
+    (dict(k="f32"), TypeError, "k has dtype"),
+    (dict(v="short"), ValueError, "v must be"),
+    (dict(g="bf16"), TypeError, "g has dtype"),
+    (dict(g="wide"), ValueError, "g has shape"),
+    (dict(beta="bf16"), TypeError, "beta has dtype"),
+    (dict(beta="short"), ValueError, "beta has shape"),
+    (dict(o="f32"), TypeError, "o has dtype"),
+    (dict(final_state="short"), ValueError, "final_state has shape"),
+    (dict(initial_state="bf16"), TypeError, "initial_state has dtype"),
+    (dict(a_log="f32 g"), TypeError, "g has dtype"),
+    (dict(), ValueError, "runs on a GPU"),
+])
+def test_binding_checks_prefill_arguments(change, err, needle):
+    """What the C ABI cannot see from raw pointers (sizes, dtypes, devices) is
+    checked by the binding before any call: each mismatch raises, none reaches
+    a kernel.  CPU tensors stop at the device check, which runs last."""
+    import torch
+    a = _prefill_args()
+    T, H, d = a["q"].shape
+    if change.get("cu_seqlens") == "long":
+        a["cu_seqlens"] = torch.tensor([0, T + 8], dtype=torch.int32)
+    if change.get("k") == "f32":
+        a["k"] = a["k"].float()
+    if change.get("v") == "short":
+        a["v"] = _t(T - 1, H, d, dtype=torch.bfloat16)
+    if change.get("g") == "bf16":
+        a["g"] = a["g"].bfloat16()
+    if change.get("g") == "wide":
+        a["g"] = _t(T, H, 2 * d)
+    if change.get("beta") == "bf16":
+        a["beta"] = a["beta"].bfloat16()
+    if change.get("beta") == "short":
+        a["beta"] = _t(T, H - 1)
+    if change.get("o") == "f32":
+        a["o"] = _t(T, H, d)
+    if change.get("final_state") == "short":
+        a["final_state"] = _t(1, H, d, d // 2)
+    if change.get("initial_state") == "bf16":
+        a["initial_state"] = _t(1, H, d, d, dtype=torch.bfloat16)
+    if change.get("a_log") == "f32 g":
+        a["a_log"] = _t(H)  # then g must be the bf16 projection, not fp32
+    with pytest.raises(err) as ei:
+        _call_prefill(a, workspace=None)
+    assert needle in str(ei.value)
+
+
+@pytest.mark.parametrize("change,err,needle", [
+    (dict(slot_idx="int64"), TypeError, "slot_idx has dtype"),
+    (dict(slot_idx="short"), ValueError, "slot_idx has shape"),
+    (dict(state="bad"), ValueError, "state must be"),
+    (dict(v="bad"), ValueError, "v must be"),
+    (dict(), ValueError, "runs on a GPU"),
+])
+def test_binding_checks_decode_arguments(change, err, needle):
+    import torch
+    B, H, d = 3, 2, 64
+    bf = torch.bfloat16
+    a = dict(q=_t(B, H, d, dtype=bf), k=_t(B, H, d, dtype=bf), v=_t(B, H, d, dtype=bf),
+             g=_t(B, H, d), beta=_t(B, H), state=_t(5, H, d, d),
+             slot_idx=torch.zeros(B, dtype=torch.int32))
+    if change.get("slot_idx") == "int64":
+        a["slot_idx"] = torch.zeros(B, dtype=torch.int64)
+    if change.get("slot_idx") == "short":
+        a["slot_idx"] = torch.zeros(B - 1, dtype=torch.int32)
+    if change.get("state") == "bad":
+        a["state"] = _t(5, H, d, d + 1)
+    if change.get("v") == "bad":
+        a["v"] = _t(B + 1, H, d, dtype=bf)
+    with pytest.raises(err) as ei:
+        kda_pkg.kda_decode_step(**a)
+    assert needle in str(ei.value)
+    tok = {k_: (v_.unsqueeze(1) if k_ not in ("state", "slot_idx") else v_) for k_, v_ in a.items()}
+    with pytest.raises(err):
+        kda_pkg.kda_decode_tokens(**tok)

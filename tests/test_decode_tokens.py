@@ -7,8 +7,8 @@ import pytest
 import torch
 
 import workloads
-from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, np64, oracle_on, per_seq_errors,
-                          rel_fro)
+from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, np64, oracle_on,
+                          assert_parity, rel_fro)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,11 +50,9 @@ def test_decode_tokens_matches_oracle(d, dtype, n_tok):
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_on(inp)
     st = state.cpu()
-    eo, es = per_seq_errors(np64(o).reshape(B * n_tok, H, d), o_ref, np64(st[slots.long()]),
-                            S_ref, inp.cu_seqlens)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    print(f"decode_tokens d={d} {dtype} n_tok={n_tok}: o {eo:.2e} S {es:.2e}")
-    assert eo <= tol and es <= tol
+    assert_parity(np64(o).reshape(B * n_tok, H, d), o_ref, np64(st[slots.long()]), S_ref,
+                  inp.cu_seqlens, tol, f"decode_tokens d={d} {dtype} n_tok={n_tok}")
     untouched = [s for s in range(n_slots) if s not in slots.tolist()]
     assert torch.equal(st[untouched], pool[untouched])
 
@@ -79,9 +77,9 @@ def test_decode_tokens_snapshots_match_prefixes(d, dtype):
                                                       dtype=torch.int32),
                                          inp.S0, dtype, inp.chunk)
         _, S_ref = oracle_on(pre)
-        err = max(rel_fro(np64(snaps[b, j]), S_ref[b]) for b in range(B))
-        print(f"d={d} {dtype}, snapshot after token {j}: {err:.2e}")
-        assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+        assert_parity(None, None, np64(snaps[:, j]), S_ref, range(B + 1),
+                      TOL_F32 if dtype == "f32" else TOL_BF16,
+                      f"d={d} {dtype}, snapshot after token {j}")
     assert torch.equal(snaps[:, -1], state.cpu())
 
 

@@ -7,7 +7,7 @@ import torch
 
 import workloads
 from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, gpu_prefill, np64, oracle_on,
-                          per_seq_errors)
+                          assert_parity)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,10 +41,9 @@ def test_prefill_head_gate(d, dtype, chunk, ws):
                                       g_sigma=1.0, s0_std=0.3, seed=300 + d + chunk, gate="head")
     o, S = gpu_prefill(inp, workspace=ws)
     o_ref, S_ref = oracle_on(inp)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    print(f"head gate d={d} {dtype} C={chunk} ws={ws}: o {eo:.2e} S {es:.2e}")
-    assert eo <= tol and es <= tol
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, tol,
+                  f"head gate d={d} {dtype} C={chunk} ws={ws}")
     # the per-channel path on the broadcast decay gives the same bits
     o2, S2 = gpu_prefill(broadcast(inp), workspace=ws)
     assert torch.equal(o, o2) and torch.equal(S, S2)
@@ -61,11 +60,10 @@ def test_decode_head_gate(d, dtype):
     o, _ = m.kda_decode_tokens(t(inp.q), t(inp.k), t(inp.v), t(inp.g), t(inp.beta), state)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_on(inp)
-    eo, es = per_seq_errors(np64(o).reshape(B * n_tok, H, d), o_ref, np64(state), S_ref,
-                            inp.cu_seqlens)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    print(f"head gate decode d={d} {dtype}: o {eo:.2e} S {es:.2e}")
-    assert eo <= tol and es <= tol
+    assert_parity(np64(o).reshape(B * n_tok, H, d), o_ref, np64(state), S_ref,
+                            inp.cu_seqlens, tol,
+                  f"head gate decode d={d} {dtype}")
     # single-token step, per-head vs broadcast per-channel decay: same bits
     rows = torch.arange(B) * n_tok
     b = broadcast(inp)

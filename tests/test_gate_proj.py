@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, np64, oracle_on,
-                          per_seq_errors)
+                          assert_parity)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,10 +61,9 @@ def test_prefill_gate_proj(name):
                                  a_log=dev(pr.a_log))
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_on(ref)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    print(f"  o {eo:.2e} S {es:.2e}")
-    assert eo <= tol and es <= tol
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, tol,
+                  f" ")
 
 
 def test_prefill_gate_proj_ling_layer():
@@ -80,9 +79,8 @@ def test_prefill_gate_proj_ling_layer():
                                  chunk=64, a_log=dev(pr.a_log))
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_on(ref)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
-    print(f"gate proj ling layer: o {eo:.2e} S {es:.2e}")
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, TOL_BF16,
+                  f"gate proj ling layer")
 
 
 @pytest.mark.parametrize("dtype,d,n_tok", [("bf16", 128, 1), ("f32", 64, 4)])
@@ -107,10 +105,9 @@ def test_decode_gate_proj(dtype, d, n_tok):
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_on(ref)
     S_gpu = np64(state)[slots.long().numpy()]
-    eo, es = per_seq_errors(np64(o), o_ref, S_gpu, S_ref, inp.cu_seqlens)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    print(f"gate proj decode {dtype} d={d} n_tok={n_tok}: o {eo:.2e} S {es:.2e}")
-    assert eo <= tol and es <= tol
+    assert_parity(np64(o), o_ref, S_gpu, S_ref, inp.cu_seqlens, tol,
+                  f"gate proj decode {dtype} d={d} n_tok={n_tok}")
     untouched = [s for s in range(n_slots) if s not in slots.tolist()]
     assert not state[untouched].abs().sum().item()
 
@@ -119,6 +116,6 @@ def test_gate_proj_rejects_mismatched_projection():
     """The binding takes the projection in q's shape and dtype only."""
     m = kda()
     q = torch.zeros((4, 2, 64), device="cuda")
-    with pytest.raises(ValueError):
+    with pytest.raises(TypeError):
         m.kda_prefill_chunked(q, q, q, q.to(torch.bfloat16), torch.zeros((4, 2), device="cuda"),
                               a_log=torch.zeros(2, device="cuda"))

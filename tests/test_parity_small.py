@@ -8,7 +8,7 @@ import torch
 import oracle
 import workloads
 from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, gpu_prefill, np64, oracle_on,
-                          per_seq_errors, rel_fro)
+                          assert_parity, rel_fro)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,9 +26,8 @@ def test_tiny_f32_prefill():
     inp = workloads.tiny_f32()
     o, S = gpu_prefill(inp)
     o_ref, S_ref = oracle_on(inp)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
-    print(f"tiny f32 prefill: o {eo:.2e} S {es:.2e}")
-    assert eo <= TOL_F32 and es <= TOL_F32
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, TOL_F32,
+                  f"tiny f32 prefill")
 
 
 def test_tiny_f32_as_decode_steps():
@@ -45,9 +44,8 @@ def test_tiny_f32_as_decode_steps():
     torch.cuda.synchronize()
     o = torch.cat(outs)
     o_ref, S_ref = oracle_on(inp)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(state), S_ref, inp.cu_seqlens)
-    print(f"tiny f32 decode steps: o {eo:.2e} S {es:.2e}")
-    assert eo <= TOL_F32 and es <= TOL_F32
+    assert_parity(np64(o), o_ref, np64(state), S_ref, inp.cu_seqlens, TOL_F32,
+                  f"tiny f32 decode steps")
 
 
 RAGGED = [37, 0, 100, 1, 64, 129]
@@ -63,10 +61,8 @@ def test_prefill_ragged(d, chunk, dtype):
                                       g_sigma=0.5, s0_std=0.5, seed=7 + d + chunk)
     o, S = gpu_prefill(inp)
     o_ref, S_ref = oracle_on(inp)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    print(f"d={d} C={chunk} {dtype}: o {eo:.2e} S {es:.2e}")
-    assert eo <= tol and es <= tol
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, tol, f"d={d} C={chunk} {dtype}")
 
 
 # workspace argument of the binding: "auto" runs the two-kernel matrix-core path
@@ -84,9 +80,8 @@ def test_mfma_prefill_multichunk(H, path):
                                       chunk=64, g_mu=3.0, g_sigma=1.0, s0_std=0.5, seed=99 + H)
     o, S = gpu_prefill(inp, workspace=PATHS[path])
     o_ref, S_ref = oracle_on(inp)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
-    print(f"mfma {path} H={H}: o {eo:.2e} S {es:.2e}")
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, TOL_BF16,
+                  f"mfma {path} H={H}")
 
 
 @pytest.mark.parametrize("path", list(PATHS))
@@ -98,9 +93,8 @@ def test_mfma_prefill_multiwindow(path):
                                       chunk=64, g_mu=3.0, g_sigma=1.0, s0_std=0.5, seed=123)
     o, S = gpu_prefill(inp, workspace=PATHS[path])
     o_ref, S_ref = oracle_on(inp)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
-    print(f"mfma {path} multiwindow: o {eo:.2e} S {es:.2e}")
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, TOL_BF16,
+                  f"mfma {path} multiwindow")
 
 
 @pytest.mark.parametrize("path", list(PATHS))
@@ -114,9 +108,8 @@ def test_mfma_prefill_many_short_sequences(path):
                                       g_sigma=1.0, s0_std=0.3, seed=125)
     o, S = gpu_prefill(inp, workspace=PATHS[path])
     o_ref, S_ref = oracle_on(inp)
-    eo, es = per_seq_errors(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens)
-    print(f"mfma {path} 600 sequences: o {eo:.2e} S {es:.2e}")
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, TOL_BF16,
+                  f"mfma {path} 600 sequences")
 
 
 @pytest.mark.parametrize("path", list(PATHS))
@@ -168,10 +161,9 @@ def test_decode_slots(d, dtype):
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_on(inp)
     st = state.cpu()
-    eo, es = per_seq_errors(np64(o), o_ref, np64(st[slots.long()]), S_ref, inp.cu_seqlens)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    print(f"decode d={d} {dtype}: o {eo:.2e} S {es:.2e}")
-    assert eo <= tol and es <= tol
+    assert_parity(np64(o), o_ref, np64(st[slots.long()]), S_ref, inp.cu_seqlens, tol,
+                  f"decode d={d} {dtype}")
     untouched = [s for s in range(n_slots) if s not in slots.tolist()]
     assert torch.equal(st[untouched], pool[untouched])
 

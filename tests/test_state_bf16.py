@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from kda_testutil import TOL_BF16, dev, gpu_or_skip, np64, oracle_on, per_seq_errors, rel_fro
+from kda_testutil import TOL_BF16, assert_parity, dev, gpu_or_skip, np64, oracle_on, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -85,11 +85,11 @@ def test_decode_bf16_state_matches_rounded_oracle(d, n_tok):
     o_ref, S_ref = oracle_on(ref)
     S_gpu = state.float().cpu().double().numpy()[slots.long().numpy()]
     S_want = oracle.round_bf16(S_ref)
-    eo, _ = per_seq_errors(np64(o).reshape(B * n_tok, H, d), o_ref, None, None, inp.cu_seqlens)
+    assert_parity(np64(o).reshape(B * n_tok, H, d), o_ref, S_gpu, S_ref, inp.cu_seqlens,
+                  TOL_BF16, f"bf16 state d={d} n_tok={n_tok}")
     diff = np.abs(S_gpu - S_want)
     exact = float(np.mean(diff == 0))
-    print(f"bf16 state d={d} n_tok={n_tok}: o {eo:.2e}, state elements equal {exact:.5f}")
-    assert eo <= TOL_BF16
+    print(f"state elements equal to the rounded oracle: {exact:.5f}")
     assert within_rounding(S_gpu, S_want)
     assert exact >= 0.999
     untouched = [s for s in range(n_slots) if s not in slots.tolist()]
@@ -119,10 +119,9 @@ def test_bf16_state_error_over_many_steps():
                                           dev(inp.g[rows]), dev(inp.beta[rows]), state))
         torch.cuda.synchronize()
         o = torch.stack(outs, dim=1).reshape(B * n, H, d)
-        eo, es = per_seq_errors(np64(o), o_ref, state.float().cpu().double().numpy(), S_ref,
-                                inp.cu_seqlens)
-        res[name] = (eo, es)
-        print(f"{name} state, {n} steps: o {eo:.2e}  final state {es:.2e}")
+        st = assert_parity(np64(o), o_ref, state.float().cpu().double().numpy(), S_ref,
+                           inp.cu_seqlens, TOL_BF16, f"{name} state, {n} steps")
+        res[name] = (st["seq_o"], st["seq_S"])
     assert res["fp32"][1] <= 1e-4
     assert res["bf16"][1] <= TOL_BF16 and res["bf16"][0] <= TOL_BF16
     assert res["bf16"][1] > 10 * res["fp32"][1]
@@ -195,12 +194,10 @@ def test_decode_bf16_state_gate_forms(gate, n_tok):
     o_ref, S_ref = oracle_on(ref)
     S_gpu = state.float().cpu().double().numpy()[slots.long().numpy()]
     S_want = oracle.round_bf16(S_ref)
-    eo, es = per_seq_errors(np64(o).reshape(B * n_tok, H, d), o_ref, S_gpu, S_ref,
-                            inp.cu_seqlens)
+    assert_parity(np64(o).reshape(B * n_tok, H, d), o_ref, S_gpu, S_ref, inp.cu_seqlens,
+                  TOL_BF16, f"bf16 state, {gate} gate, n_tok={n_tok}")
     exact = float(np.mean(S_gpu == S_want))
-    print(f"bf16 state, {gate} gate, n_tok={n_tok}: o {eo:.2e} S {es:.2e}, "
-          f"state elements equal {exact:.5f}")
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    print(f"state elements equal to the rounded oracle: {exact:.5f}")
     assert within_rounding(S_gpu, S_want)
     assert exact >= 0.999
     untouched = [s for s in range(n_slots) if s not in slots.tolist()]
