@@ -20,6 +20,9 @@ Contents
   outputs (numpy fp64): g = -exp(a_log) softplus(f), beta = sigmoid(b).  The
   same page names f_proj and A_log behind the per-channel decay and b_proj
   behind beta but prints no formula; this is the reading the library adopts.
+* ``output_gate``   -- the output gate applied to the recurrence's outputs
+  (numpy fp64): o * sigmoid(z), z the gate projection per (token, head, value
+  channel).
 
 Where each step comes from is stated in ``kda_oracle.c``'s header: page
 "Ling-3.1-flash: a 560B hybrid-attention MoE, counted from its safetensors
@@ -260,3 +263,24 @@ def gate_prologue(f, a_log, b):
     beta = 1.0 / (1.0 + np.exp(-b))
     return g, beta
 
+
+
+def output_gate(o, z):
+    """The output gate on the recurrence's outputs, in fp64: o * sigmoid(z).
+
+    o: [..., H, d_v] outputs o_t = S_t^T q_t; z: the same shape, the gate
+    projection's output.  Page "Ling-3.1-flash: a 560B hybrid-attention MoE,
+    counted from its safetensors headers", section "How KDA and MLA split the
+    work", lists a gate projection among each KDA layer's full-rank 4096 -> 8192
+    matrices (one value per head and value channel) beside the output
+    projection that follows it, without its activation; the same section's
+    gated MLA scales its result by a sigmoid gate.  Taken here: the elementwise
+    sigmoid gate, with no normalisation before it (the pages name none).
+    sigmoid(z) = 1 / (1 + e^{-z}) is evaluated without overflow for any finite
+    z (numpy's exp of a large -z gives inf, and 1 / inf = 0)."""
+    o = np.asarray(o, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    if o.shape != z.shape:
+        raise ValueError("oracle: output gate shape")
+    with np.errstate(over="ignore"):
+        return o / (1.0 + np.exp(-z))

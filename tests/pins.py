@@ -309,3 +309,26 @@ def pin_l2norm_eps(orc):
 
 CONV_PINS = [pin_conv_identity_tap, pin_conv_numpy, pin_conv_handoff, pin_l2norm,
              pin_l2norm_eps]
+
+
+# --------------------------------------------------------------------------- output gate
+
+def pin_output_gate(gate):
+    """The output gate o * sigmoid(z) at values fixed by hand: sigmoid(0) = 1/2,
+    sigmoid(ln 3) = 1 / (1 + 1/3) = 3/4, sigmoid(-ln 3) = 1/4; far positive z
+    passes o through, far negative z closes the gate; gate(o, z) + gate(o, -z)
+    = o (sigmoid(z) + sigmoid(-z) = 1); elementwise, so each (token, head,
+    channel) uses its own z."""
+    o = np.array([[[2.0, -8.0, 4.0, 1.0]]])
+    z = np.array([[[0.0, np.log(3.0), -np.log(3.0), 60.0]]])
+    y = gate(o, z)
+    assert np.allclose(y, [[[1.0, -6.0, 1.0, 1.0]]], rtol=1e-15, atol=0), y
+    assert abs(gate(np.array([5.0]), np.array([-60.0]))[0]) < 1e-24
+    assert gate(np.array([3.0]), np.array([-1000.0]))[0] == 0.0
+    rng = np.random.default_rng(35)
+    o = rng.standard_normal((7, 3, 16))
+    z = rng.standard_normal((7, 3, 16)) * 4
+    assert np.allclose(gate(o, z) + gate(o, -z), o, rtol=1e-14, atol=1e-14)
+    # each element gated by its own z: permuting both the same way commutes
+    perm = rng.permutation(16)
+    assert np.array_equal(gate(o[..., perm], z[..., perm]), gate(o, z)[..., perm])

@@ -118,3 +118,27 @@ def test_gate_prologue_closed_forms():
     alpha = np.exp(oracle.gate_prologue(rng.standard_normal((9, 3, 5)) * 20, a_log,
                                         np.zeros((9, 3)))[0])
     assert np.all((alpha > 0) & (alpha <= 1))
+
+
+def test_output_gate_pin():
+    from pins import pin_output_gate
+    pin_output_gate(oracle.output_gate)
+
+
+# plausible mistakes in an output gate, each of which the pin must reject
+WRONG_GATES = {
+    "gate_sign_flipped": lambda o, z: o / (1.0 + np.exp(z)),
+    "raw_multiply": lambda o, z: o * z,
+    "tanh_gate": lambda o, z: o * np.tanh(z),
+    "additive": lambda o, z: o + 1.0 / (1.0 + np.exp(-z)),
+    "swish_gate": lambda o, z: o * z / (1.0 + np.exp(-z)),
+    "gate_per_head": lambda o, z: o / (1.0 + np.exp(-z.mean(axis=-1, keepdims=True))),
+}
+
+
+@pytest.mark.parametrize("name", list(WRONG_GATES))
+def test_output_gate_pin_catches(name):
+    from pins import pin_output_gate
+    with np.errstate(over="ignore", invalid="ignore"):
+        with pytest.raises(AssertionError):
+            pin_output_gate(WRONG_GATES[name])
