@@ -145,7 +145,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                                const float* beta, kda_dtype dtype, kda_gate gate,
                                const float* a_log, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
-                               const float* initial_state, float* final_state, void* o,
+                               const float* initial_state, float* final_state,
+                               const void* out_gate, void* o,
                                float* snapshots, int snap_interval, int snap_capacity,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const char* fn = "kda_prefill_chunked";
@@ -176,12 +177,19 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
             ((uintptr_t)beta & 3u))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
+        if (!aligned16(out_gate))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned out_gate", fn);
         if (overlaps(o, n_qk * es, q, n_qk * es) || overlaps(o, n_qk * es, k, n_qk * es) ||
             overlaps(o, n_qk * es, v, n_qk * es) || overlaps(o, n_qk * es, g, gb) ||
             overlaps(o, n_qk * es, beta, n_bt * 4) || overlaps(o, n_qk * es, a_log, ab) ||
             overlaps(o, n_qk * es, final_state, sbytes) ||
-            overlaps(o, n_qk * es, initial_state, sbytes))
+            overlaps(o, n_qk * es, initial_state, sbytes) ||
+            overlaps(o, n_qk * es, out_gate, n_qk * es))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o overlaps another argument", fn);
+        if (final_state && overlaps(final_state, sbytes, out_gate, n_qk * es))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state overlaps out_gate", fn);
+    } else {
+        out_gate = nullptr;
     }
     if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned state pointer", fn);
@@ -212,6 +220,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
             overlaps(snapshots, snb, beta, n_bt * 4) || overlaps(snapshots, snb, o, n_qk * es) ||
             overlaps(snapshots, snb, initial_state, sbytes) ||
             overlaps(snapshots, snb, final_state, sbytes) ||
+            overlaps(snapshots, snb, out_gate, n_qk * es) ||
             overlaps(snapshots, snb, workspace, workspace ? workspace_bytes : 0))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: snapshots overlap another argument", fn);
         if (snap_capacity == 0) snapshots = nullptr;
@@ -231,7 +240,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
             overlaps(workspace, workspace_bytes, a_log, ab) ||
             overlaps(workspace, workspace_bytes, beta, n_bt * 4) || overlaps(workspace, workspace_bytes, o, n_qk * es) ||
             overlaps(workspace, workspace_bytes, initial_state, sbytes) ||
-            overlaps(workspace, workspace_bytes, final_state, sbytes))
+            overlaps(workspace, workspace_bytes, final_state, sbytes) ||
+            overlaps(workspace, workspace_bytes, out_gate, n_qk * es))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps another argument", fn);
     }
 
@@ -239,14 +249,15 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     hipError_t err;
     if (mfma && workspace) {
         err = kda::launch_prefill_split(q, k, v, gt, beta, cu_seqlens_dev, cu_seqlens_host,
-                                        n_seqs, T, H, initial_state, final_state, o, snap,
-                                        workspace, workspace_bytes, stream);
+                                        n_seqs, T, H, initial_state, final_state, out_gate, o,
+                                        snap, workspace, workspace_bytes, stream);
     } else if (mfma)
-        err = kda::launch_prefill_fused(q, k, v, gt, beta, cu_seqlens_dev,
-                                        n_seqs, T, H, initial_state, final_state, o, snap, stream);
+        err = kda::launch_prefill_fused(q, k, v, gt, beta, cu_seqlens_dev, n_seqs, T, H,
+                                        initial_state, final_state, out_gate, o, snap, stream);
     else
-        err = kda::launch_prefill_vector(q, k, v, gt, beta, dtype, cu_seqlens_dev, n_seqs, T, H, d, chunk, initial_state,
-                                         final_state, o, snap, stream);
+        err = kda::launch_prefill_vector(q, k, v, gt, beta, dtype, cu_seqlens_dev, n_seqs, T, H,
+                                         d, chunk, initial_state, final_state, out_gate, o, snap,
+                                         stream);
     return hip_status(err, "kda_prefill_chunked launch");
 }
 
@@ -272,7 +283,8 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
                                 const float* a_log, void* state, kda_dtype state_dtype,
                                 int64_t n_slots,
                                 const int32_t* slot_idx, int B, int n_tok, int H, int dk, int dv,
-                                void* o, void* token_states, hipStream_t stream) {
+                                const void* out_gate, void* o, void* token_states,
+                                hipStream_t stream) {
     g_detail[0] = 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
@@ -296,7 +308,7 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
     const size_t es = elem_size(dtype);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
         !aligned16(state) || ((uintptr_t)beta & 3u) || ((uintptr_t)slot_idx & 3u) ||
-        !aligned16(token_states))
+        !aligned16(token_states) || !aligned16(out_gate))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: misaligned tensor pointer", fn);
     const size_t nv = (size_t)B * n_tok * H * dk, nb = (size_t)B * n_tok * H * 4;
     const size_t gb = gate_bytes(gate, (size_t)B * n_tok, H, dk, dtype);
@@ -309,17 +321,19 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
         overlaps(o, nv * es, state, sbytes) || overlaps(state, sbytes, q, nv * es) ||
         overlaps(state, sbytes, k, nv * es) || overlaps(state, sbytes, v, nv * es) ||
         overlaps(state, sbytes, g, gb) || overlaps(state, sbytes, beta, nb) ||
-        overlaps(state, sbytes, a_log, ab))
+        overlaps(state, sbytes, a_log, ab) || overlaps(o, nv * es, out_gate, nv * es) ||
+        overlaps(state, sbytes, out_gate, nv * es))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state or o overlaps another argument", fn);
     if (token_states &&
         (overlaps(token_states, tbytes, state, sbytes) || overlaps(token_states, tbytes, o, nv * es) ||
          overlaps(token_states, tbytes, q, nv * es) || overlaps(token_states, tbytes, k, nv * es) ||
          overlaps(token_states, tbytes, v, nv * es) || overlaps(token_states, tbytes, g, gb) ||
-         overlaps(token_states, tbytes, beta, nb) || overlaps(token_states, tbytes, a_log, ab)))
+         overlaps(token_states, tbytes, beta, nb) || overlaps(token_states, tbytes, a_log, ab) ||
+         overlaps(token_states, tbytes, out_gate, nv * es)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: token_states overlaps another argument", fn);
     return hip_status(kda::launch_decode(q, k, v, make_gate(g, a_log, gate), beta, dtype, state,
                                          state_dtype, n_slots, slot_idx, B, n_tok, H, dk,
-                                         token_states, o, stream),
+                                         token_states, out_gate, o, stream),
                       "decode launch");
 }
 
@@ -327,21 +341,22 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            const float* beta, kda_dtype dtype, kda_gate gate,
                            const float* a_log, void* state,
                            kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
-                           int B, int H, int dk, int dv, void* o, hipStream_t stream) {
+                           int B, int H, int dk, int dv, const void* out_gate, void* o,
+                           hipStream_t stream) {
     return decode_common("kda_decode_step", q, k, v, g, beta, dtype, gate, a_log, state,
-                         state_dtype,
-                         n_slots, slot_idx, B, 1, H, dk, dv, o, nullptr, stream);
+                         state_dtype, n_slots, slot_idx, B, 1, H, dk, dv, out_gate, o, nullptr,
+                         stream);
 }
 
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const void* g,
                              const float* beta, kda_dtype dtype, kda_gate gate,
                              const float* a_log, void* state,
                              kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
-                             int B, int n_tok, int H, int dk, int dv, void* o,
-                             void* token_states, hipStream_t stream) {
+                             int B, int n_tok, int H, int dk, int dv, const void* out_gate,
+                             void* o, void* token_states, hipStream_t stream) {
     return decode_common("kda_decode_tokens", q, k, v, g, beta, dtype, gate, a_log, state,
-                         state_dtype,
-                         n_slots, slot_idx, B, n_tok, H, dk, dv, o, token_states, stream);
+                         state_dtype, n_slots, slot_idx, B, n_tok, H, dk, dv, out_gate, o,
+                         token_states, stream);
 }
 
 static kda_status check_conv_common(const char* fn, const float* w, kda_dtype dtype,

@@ -199,7 +199,7 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
               const float* __restrict__ g, const float* __restrict__ a_log,
               const float* __restrict__ beta, int g_head, TS* __restrict__ state, int64_t n_slots,
               const int32_t* __restrict__ slot_idx, int H, int n_tok,
-              TS* __restrict__ token_states, Tin* __restrict__ o) {
+              TS* __restrict__ token_states, const Tin* __restrict__ zg, Tin* __restrict__ o) {
     constexpr int VEC = decode_vec<D, TS>();
     using S = DecodeShape<D, VEC, MULTI>;
     constexpr int NT = S::NT, CG = S::CG, RG = S::RG, RPT = S::RPT;
@@ -355,6 +355,12 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
             float ov[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) ov[e] = Yq[e] + qk * u[e];
+            if (zg) {  // output gate: o * sigmoid(z)
+                float zv[VEC];
+                in_load<Tin, VEC>(zg + vec + c0, zv);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) ov[e] *= sigmoid_f(zv[e]);
+            }
             in_store<Tin, VEC>(o + vec + c0, ov);
         }
 
@@ -379,7 +385,8 @@ template <int D, typename Tin, typename TS>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, Gate g,
                                   const float* beta, void* state, int64_t n_slots,
                                   const int32_t* slot_idx, int B, int n_tok, int H,
-                                  void* token_states, void* o, hipStream_t stream) {
+                                  void* token_states, const void* zg, void* o,
+                                  hipStream_t stream) {
     const int64_t blocks = (int64_t)B * H;
     if (blocks == 0 || n_tok == 0) return hipSuccess;
     const bool proj = g.mode == GATE_PROJ;
@@ -393,7 +400,7 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, G
                        0, stream, (const Tin*)q, (const Tin*)k, (const Tin*)v,
                        static_cast<const float*>(g.g), g.a_log, beta, (int)(g.mode == GATE_HEAD),
                        (TS*)state, n_slots, slot_idx, H, n_tok, (TS*)token_states,
-                       (Tin*)o);
+                       (const Tin*)zg, (Tin*)o);
     return hipGetLastError();
 }
 
@@ -402,27 +409,29 @@ static hipError_t launch_decode_s(const void* q, const void* k, const void* v, G
                                   const float* beta, void* state,
                                   kda_dtype state_dtype, int64_t n_slots,
                                   const int32_t* slot_idx, int B, int n_tok, int H,
-                                  void* token_states, void* o, hipStream_t stream) {
+                                  void* token_states, const void* zg, void* o,
+                                  hipStream_t stream) {
     if (state_dtype == KDA_BF16)
         return launch_decode_t<D, Tin, bf16_t>(q, k, v, g, beta, state, n_slots, slot_idx,
-                                               B, n_tok, H, token_states, o, stream);
+                                               B, n_tok, H, token_states, zg, o, stream);
     return launch_decode_t<D, Tin, float>(q, k, v, g, beta, state, n_slots, slot_idx, B,
-                                          n_tok, H, token_states, o, stream);
+                                          n_tok, H, token_states, zg, o, stream);
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, Gate g,
                          const float* beta, kda_dtype dtype, void* state,
                          kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx, int B,
-                         int n_tok, int H, int d, void* token_states, void* o,
-                         hipStream_t stream) {
+                         int n_tok, int H, int d, void* token_states, const void* out_gate,
+                         void* o, hipStream_t stream) {
 #define KDA_DEC(D)                                                                           \
     if (d == D) {                                                                            \
         if (dtype == KDA_BF16)                                                               \
             return launch_decode_s<D, bf16_t>(q, k, v, g, beta, state, state_dtype,  \
-                                              n_slots, slot_idx, B, n_tok, H, token_states, o, \
-                                              stream);                                       \
+                                              n_slots, slot_idx, B, n_tok, H, token_states,  \
+                                              out_gate, o, stream);                          \
         return launch_decode_s<D, float>(q, k, v, g, beta, state, state_dtype, n_slots, \
-                                         slot_idx, B, n_tok, H, token_states, o, stream);    \
+                                         slot_idx, B, n_tok, H, token_states, out_gate, o,   \
+                                         stream);                                            \
     }
     KDA_DEC(16)
     KDA_DEC(32)

@@ -128,29 +128,32 @@ __device__ __forceinline__ float sigmoid_f(float x) {
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already checked.
+// out_gate, where taken: the output gate's projection z in o's layout and dtype,
+// or NULL; with it every output is multiplied by sigmoid(z) before it is stored.
 // n_elems elements of state_dtype: zeros (src NULL) or src converted.
 hipError_t launch_state_init(void* state, kda_dtype state_dtype, int64_t n_elems, const void* src,
                              kda_dtype src_dtype, hipStream_t stream);
 
 // n_tok consecutive tokens per sequence; token_states may be NULL; state and
 // token_states hold state_dtype elements.
+// out_gate (o's layout and dtype) or NULL: o is multiplied by sigmoid(out_gate).
 hipError_t launch_decode(const void* q, const void* k, const void* v, Gate gate,
                          const float* beta, kda_dtype dtype, void* state,
                          kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx, int B,
-                         int n_tok, int H, int d, void* token_states, void* o,
-                         hipStream_t stream);
+                         int n_tok, int H, int d, void* token_states, const void* out_gate,
+                         void* o, hipStream_t stream);
 
 hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, Gate gate,
                                  const float* beta, kda_dtype dtype, const int32_t* cu,
                                  int n_seqs, int64_t T, int H, int d, int chunk,
-                                 const float* s0, float* s_final, void* o, Snapshots snap,
-                                 hipStream_t stream);
+                                 const float* s0, float* s_final, const void* out_gate, void* o,
+                                 Snapshots snap, hipStream_t stream);
 
 // bf16, d = 128, chunk = 64, one fused kernel (no workspace).
 hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, Gate gate,
                                 const float* beta, const int32_t* cu, int n_seqs,
-                                int64_t T, int H, const float* s0, float* s_final, void* o,
-                                Snapshots snap, hipStream_t stream);
+                                int64_t T, int H, const float* s0, float* s_final,
+                                const void* out_gate, void* o, Snapshots snap, hipStream_t stream);
 
 // bf16, d = 128, chunk = 64, two kernels through a caller workspace of
 // prefill_split_workspace_bytes(n_seqs, H) bytes; cu_host: the validated host
@@ -160,8 +163,8 @@ size_t prefill_split_workspace_bytes_batch(const int32_t* cu_host, int n_seqs, i
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gate gate,
                                 const float* beta, const int32_t* cu, const int32_t* cu_host,
                                 int n_seqs, int64_t T, int H, const float* s0, float* s_final,
-                                void* o, Snapshots snap, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream);
+                                const void* out_gate, void* o, Snapshots snap, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 hipError_t launch_short_conv_prefill(const void* x, const float* w, kda_dtype dtype,
                                      const int32_t* cu, int n_seqs, int64_t T, int channels,

@@ -44,10 +44,12 @@ struct FusedLds {
 using namespace fu;
 
 // GM: the decay inputs' GateMode (per channel, per head, or the projection).
-template <int GM>
+// OG: the outputs are gated, O * sigmoid(z), z the gate projection zg (o's
+// layout), read one chunk ahead by the output waves.
+template <int GM, bool OG>
 __global__ void __launch_bounds__(768)
 prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                     const bf16_t* __restrict__ v, Gate g,
+                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ zg, Gate g,
                      const float* __restrict__ beta, const int32_t* __restrict__ cu,
                      int64_t T, int H, int n_pairs, const float* __restrict__ s0,
                      float* __restrict__ s_final, bf16_t* __restrict__ o, Snapshots snap) {
@@ -221,6 +223,15 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) cur.P[kk] = ld8(sm.ck.P + (16 * cw + r) * LDT + 32 * kk + 8 * q4);
         };
+        auto load_z = [&](int c) {
+            uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (OG) {
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vo_rsrc(zg, c), xoff, 0, 0);
+                z = make_uint4(x[0], x[1], x[2], x[3]);
+            }
+            return z;
+        };
+        uint4 znext = load_z(0);
         __syncthreads();  // P1
         __syncthreads();  // P2
         __syncthreads();  // P3
@@ -228,14 +239,16 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         __syncthreads();  // P4
         for (int s = 0; s < nc; ++s) {
             const bool next = s + 1 < nc;
+            const uint4 zc = znext;
+            znext = load_z(s + 1);
             // ---- [A] Z = Qt G
             f32x4 Zc[2];
             out_z(sm.st, cur, Zc, lane);
             __syncthreads();  // B1
             __syncthreads();  // B2
-            // ---- [C] O = Z + P U, staged through this wave's rows, one 16-byte store
-            __builtin_amdgcn_raw_buffer_store_b128(out_o(sm.st, cur, Zc, cw, lane, xrow, xcol),
-                                                   vo_rsrc(o, s), xoff, 0, 0);
+            // ---- [C] O = Z + P U (gated), staged through this wave's rows, one 16-byte store
+            __builtin_amdgcn_raw_buffer_store_b128(
+                out_o<OG>(sm.st, cur, Zc, zc, cw, lane, xrow, xcol), vo_rsrc(o, s), xoff, 0, 0);
             __syncthreads();  // B3
             // ---- [D] fragments of chunk s + 1
             if (next) copy_in();
@@ -244,19 +257,32 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
 }
 
+template <bool OG>
+static hipError_t launch_fused_og(const void* q, const void* k, const void* v, Gate g,
+                                  const float* beta, const int32_t* cu, int64_t n_pairs,
+                                  int64_t T, int H, const float* s0, float* s_final,
+                                  const void* out_gate, void* o, Snapshots snap,
+                                  hipStream_t stream) {
+    auto kern = g.mode == GATE_HEAD   ? prefill_fused_kernel<GATE_HEAD, OG>
+                : g.mode == GATE_PROJ ? prefill_fused_kernel<GATE_PROJ, OG>
+                                      : prefill_fused_kernel<GATE_CH, OG>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(n_pairs * NS)), dim3(768), 0, stream, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)out_gate, g, beta, cu,
+                       T, H, (int)n_pairs, s0, s_final, (bf16_t*)o, snap);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, Gate g,
                                 const float* beta, const int32_t* cu, int n_seqs,
-                                int64_t T, int H, const float* s0, float* s_final, void* o,
-                                Snapshots snap, hipStream_t stream) {
+                                int64_t T, int H, const float* s0, float* s_final,
+                                const void* out_gate, void* o, Snapshots snap, hipStream_t stream) {
     const int64_t n_pairs = (int64_t)n_seqs * H;
     if (n_pairs == 0) return hipSuccess;
-    hipLaunchKernelGGL(g.mode == GATE_HEAD   ? prefill_fused_kernel<GATE_HEAD>
-                       : g.mode == GATE_PROJ ? prefill_fused_kernel<GATE_PROJ>
-                                             : prefill_fused_kernel<GATE_CH>,
-                       dim3((unsigned)(n_pairs * NS)), dim3(768), 0, stream, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, g, beta, cu, T, H, (int)n_pairs, s0,
-                       s_final, (bf16_t*)o, snap);
-    return hipGetLastError();
+    if (out_gate)
+        return launch_fused_og<true>(q, k, v, g, beta, cu, n_pairs, T, H, s0, s_final, out_gate, o,
+                                     snap, stream);
+    return launch_fused_og<false>(q, k, v, g, beta, cu, n_pairs, T, H, s0, s_final, nullptr, o,
+                                  snap, stream);
 }
 
 }  // namespace kda

@@ -221,9 +221,13 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
 // S <- G + Wb^T R and the next G; the output waves form Z = Qt G, then
 // O = Z + PT R; two barriers per chunk (R complete, next G complete).
 // Fragments come straight from the tiles into registers, two chunks ahead
-// (three register sets in rotation), spread over the step's segments.
+// (three register sets in rotation), spread over the step's segments.  OG: the
+// outputs are gated, O * sigmoid(z) with z the gate projection zg (o's layout),
+// read by the output waves with their fragments.
+template <bool OG>
 __global__ void __launch_bounds__(512)
-state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
+state_kernel(const bf16_t* __restrict__ v, const bf16_t* __restrict__ zg,
+             const int32_t* __restrict__ cu,
              const int32_t* __restrict__ order, int64_t T, int H,
              int n_pairs, int n_prep, int w0, int win, const uint8_t* __restrict__ ws_tiles,
              float* __restrict__ ws_state, const float* __restrict__ s0,
@@ -350,7 +354,10 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
     } else {
         // ============================================================ output
         auto load_a = [&](int c, OutFrags& f) { outw_load_a(f, tile_rsrc(c), cw, lane); };
-        auto load_b = [&](int c, OutFrags& f) { outw_load_b(f, tile_rsrc(c), cw, lane); };
+        auto load_b = [&](int c, OutFrags& f) {
+            outw_load_b(f, tile_rsrc(c), cw, lane);
+            if constexpr (OG) out_load_z(f, vo_rsrc(zg, c), xoff);
+        };
         OutFrags F0, F1, F2;
         load_a(c_beg, F0);
         load_b(c_beg, F0);
@@ -361,8 +368,8 @@ state_kernel(const bf16_t* __restrict__ v, const int32_t* __restrict__ cu,
             f32x4 Zc[2];
             out_z(sm, cur, Zc, lane);
             __syncthreads();
-            __builtin_amdgcn_raw_buffer_store_b128(outw_o(sm, cur, Zc, cw, lane, xrow, xcol),
-                                                   vo_rsrc(o, c), xoff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                outw_o<OG>(sm, cur, Zc, cur.z, cw, lane, xrow, xcol), vo_rsrc(o, c), xoff, 0, 0);
             load_a(c + 2, later);
             load_b(c + 2, later);
             __syncthreads();
@@ -437,8 +444,8 @@ size_t prefill_split_workspace_bytes_batch(const int32_t* cu_host, int n_seqs, i
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gate g,
                                 const float* beta, const int32_t* cu, const int32_t* cu_host,
                                 int n_seqs, int64_t T, int H, const float* s0, float* s_final,
-                                void* o, Snapshots snap, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                const void* out_gate, void* o, Snapshots snap, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
     if ((int64_t)n_seqs * H == 0) return hipSuccess;
     // chunk counts, longest first: the ranks' lengths
     std::vector<int> len(n_seqs);
@@ -476,8 +483,10 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gat
             err = hipGetLastError();
             if (err != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(state_kernel, dim3((unsigned)((int64_t)wd.visit * H * NS)), dim3(512),
-                           0, stream, (const bf16_t*)v, cu, order, T, H, wd.visit * H, wd.active,
+        hipLaunchKernelGGL(out_gate ? state_kernel<true> : state_kernel<false>,
+                           dim3((unsigned)((int64_t)wd.visit * H * NS)), dim3(512), 0, stream,
+                           (const bf16_t*)v, (const bf16_t*)out_gate, cu, order, T, H,
+                           wd.visit * H, wd.active,
                            wd.w0, wd.win, tiles, ws_state, s0, s_final, (bf16_t*)o, snap);
         err = hipGetLastError();
         if (err != hipSuccess) return err;

@@ -39,7 +39,8 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                       const Tin* __restrict__ v, Gate gate,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu,
                       int64_t T, int H, const float* __restrict__ s0,
-                      float* __restrict__ s_final, Tin* __restrict__ o, Snapshots snap) {
+                      float* __restrict__ s_final, const Tin* __restrict__ zg,
+                      Tin* __restrict__ o, Snapshots snap) {
     using SH = VecShape<D, C>;
     constexpr int DVS = SH::DVS, NS = SH::NS, LD = SH::LD, NT = SH::NT;
     extern __shared__ float smem[];
@@ -157,7 +158,9 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
             float acc = 0.f;
             for (int i = 0; i < D; ++i) acc += sQt[t * LD + i] * sS[i * DVS + j];
             for (int s = 0; s <= t; ++s) acc += sNP[t * C + s] * sU[s * DVS + j];
-            In<Tin>::store1(o + (size_t)(c0 + t) * rowk + (size_t)h * D + j0 + j, acc);
+            const size_t oat = (size_t)(c0 + t) * rowk + (size_t)h * D + j0 + j;
+            if (zg) acc *= sigmoid_f(In<Tin>::load1(zg + oat));  // output gate
+            In<Tin>::store1(o + oat, acc);
         }
         __syncthreads();
         // S <- Gam * S + (Kh * Gam)^T U (and the snapshot when one falls here)
@@ -183,8 +186,8 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
 template <int D, int C, typename Tin>
 static hipError_t launch_vec_t(const void* q, const void* k, const void* v, Gate g,
                                const float* beta, const int32_t* cu, int n_seqs,
-                               int64_t T, int H, const float* s0, float* s_final, void* o,
-                               Snapshots snap, hipStream_t stream) {
+                               int64_t T, int H, const float* s0, float* s_final,
+                               const void* zg, void* o, Snapshots snap, hipStream_t stream) {
     using SH = VecShape<D, C>;
     const int64_t blocks = (int64_t)n_seqs * H * SH::NS;
     if (blocks == 0) return hipSuccess;
@@ -195,7 +198,7 @@ static hipError_t launch_vec_t(const void* q, const void* k, const void* v, Gate
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(SH::NT), SH::BYTES, stream,
                        (const Tin*)q, (const Tin*)k, (const Tin*)v, g, beta, cu, T, H,
-                       s0, s_final, (Tin*)o, snap);
+                       s0, s_final, (const Tin*)zg, (Tin*)o, snap);
     return hipGetLastError();
 }
 
@@ -203,11 +206,11 @@ template <int D, typename Tin>
 static hipError_t launch_vec_c(int chunk, const void* q, const void* k, const void* v,
                                Gate g, const float* beta, const int32_t* cu,
                                int n_seqs, int64_t T, int H, const float* s0, float* s_final,
-                               void* o, Snapshots snap, hipStream_t stream) {
+                               const void* zg, void* o, Snapshots snap, hipStream_t stream) {
     switch (chunk) {
-        case 16: return launch_vec_t<D, 16, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
-        case 32: return launch_vec_t<D, 32, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
-        case 64: return launch_vec_t<D, 64, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, o, snap, stream);
+        case 16: return launch_vec_t<D, 16, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, zg, o, snap, stream);
+        case 32: return launch_vec_t<D, 32, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, zg, o, snap, stream);
+        case 64: return launch_vec_t<D, 64, Tin>(q, k, v, g, beta, cu, n_seqs, T, H, s0, s_final, zg, o, snap, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -215,15 +218,15 @@ static hipError_t launch_vec_c(int chunk, const void* q, const void* k, const vo
 hipError_t launch_prefill_vector(const void* q, const void* k, const void* v, Gate g,
                                  const float* beta, kda_dtype dtype, const int32_t* cu,
                                  int n_seqs, int64_t T, int H, int d, int chunk,
-                                 const float* s0, float* s_final, void* o, Snapshots snap,
-                                 hipStream_t stream) {
+                                 const float* s0, float* s_final, const void* out_gate, void* o,
+                                 Snapshots snap, hipStream_t stream) {
 #define KDA_VEC(D)                                                                            \
     if (d == D) {                                                                             \
         if (dtype == KDA_BF16)                                                                \
             return launch_vec_c<D, bf16_t>(chunk, q, k, v, g, beta, cu, n_seqs, T, H, \
-                                           s0, s_final, o, snap, stream);                     \
+                                           s0, s_final, out_gate, o, snap, stream);           \
         return launch_vec_c<D, float>(chunk, q, k, v, g, beta, cu, n_seqs, T, H, s0,  \
-                                      s_final, o, snap, stream);                              \
+                                      s_final, out_gate, o, snap, stream);                    \
     }
     KDA_VEC(16)
     KDA_VEC(32)

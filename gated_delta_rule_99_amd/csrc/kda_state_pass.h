@@ -77,6 +77,7 @@ struct ChainFrags {
 };
 struct OutFrags {
     bf16x8 Q[4], P[2];
+    uint4 z;  // output gate: this lane's 16-byte piece of the gate projection
 };
 
 __device__ __forceinline__ bf16x8 ld_frag(__amdgpu_buffer_rsrc_t rt, int off) {
@@ -184,22 +185,53 @@ __device__ __forceinline__ void out_z(StateLds& sm, const OutFrags& cur, f32x4 (
     }
 }
 
-// [C] O = Z + P U, staged through this wave's rows; returns this lane's
-// 16-byte piece (row xrow, columns xcol ..) for one store.
-__device__ __forceinline__ u32x4 out_o(StateLds& sm, const OutFrags& cur, const f32x4 (&Zc)[2],
-                                       int cw, int lane, int xrow, int xcol) {
+// This wave's 16 output rows, fp32 in the accumulator layout (acc[jb][e]: row
+// 16cw + 4q4 + e, column 16jb + r), to this lane's 16-byte piece of them (row
+// xrow, columns xcol ..) in bf16, through the wave's rows of the staging tile.
+// GATED: each output is first multiplied by sigmoid(z), the output gate, with z
+// this lane's 16-byte piece of the gate projection (same rows and columns): z
+// takes the same way through the staging rows into the accumulator layout, so
+// that the gated value is rounded to bf16 once.  Only the wave itself touches
+// these rows, and a wave's LDS accesses complete in order.
+template <bool GATED>
+__device__ __forceinline__ u32x4 stage_out(StateLds& sm, f32x4 (&acc)[2], const uint4& z, int cw,
+                                           int lane, int xrow, int xcol) {
     const int r = lane & 15, q4 = lane >> 4;
+    if constexpr (GATED) {
+        *reinterpret_cast<uint4*>(sm.O + xrow * LDX + xcol) = z;
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-        f32x4 acc = mma32(cur.P[0], ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
-        if (cw >= 2) acc = mma32(cur.P[1], ld8(sm.Ut + (16 * jb + r) * LDT + 32 + 8 * q4), acc);
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[jb][e] *= sigmoid_f(
+                    bf16_bits_to_f32(sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r]));
+        __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[e]);
-    }
+            sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[jb][e]);
     __builtin_amdgcn_wave_barrier();
     const uint4 x = *reinterpret_cast<const uint4*>(sm.O + xrow * LDX + xcol);
     return u32x4{x.x, x.y, x.z, x.w};
+}
+
+// [C] O = Z + P U (gated by sigmoid(z) with GATED), staged through this wave's
+// rows; returns this lane's 16-byte piece (row xrow, columns xcol ..) for one
+// store.
+template <bool GATED>
+__device__ __forceinline__ u32x4 out_o(StateLds& sm, const OutFrags& cur, const f32x4 (&Zc)[2],
+                                       const uint4& z, int cw, int lane, int xrow, int xcol) {
+    const int r = lane & 15, q4 = lane >> 4;
+    f32x4 acc[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+        acc[jb] = mma32(cur.P[0], ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
+        if (cw >= 2) acc[jb] = mma32(cur.P[1], ld8(sm.Ut + (16 * jb + r) * LDT + 32 + 8 * q4), acc[jb]);
+    }
+    return stage_out<GATED>(sm, acc, z, cw, lane, xrow, xcol);
 }
 
 // ------------------------------------------------ two-kernel path, T folded in
@@ -242,6 +274,12 @@ __device__ __forceinline__ void outw_load_b(OutFrags& f, __amdgpu_buffer_rsrc_t 
     f.P[0] = ld_frag(rt, OFF_PT + (cw * 2 * 64 + lane) * 16);
     if (cw >= 2) f.P[1] = ld_frag(rt, OFF_PT + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
 }
+// This lane's 16-byte piece of the chunk's gate projection (row xrow, columns
+// xcol ..; a window of zero rows past the chunk).
+__device__ __forceinline__ void out_load_z(OutFrags& f, __amdgpu_buffer_rsrc_t rz, int xoff) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rz, xoff, 0, 0);
+    f.z = make_uint4(x[0], x[1], x[2], x[3]);
+}
 
 // [C] S <- G + Wb^T R (R from Rt); the raw S to snp (a snapshot) when snp is
 // set; with more, the next G = Gam' S into Gt.
@@ -271,22 +309,20 @@ __device__ __forceinline__ void chainw_s(StateLds& sm, const ChainFragsW& cur,
     }
 }
 
-// [C] O = Z + PT R, staged through this wave's rows; returns this lane's
-// 16-byte piece (row xrow, columns xcol ..) for one store.
+// [C] O = Z + PT R (gated by sigmoid(z) with GATED), staged through this
+// wave's rows; returns this lane's 16-byte piece (row xrow, columns xcol ..)
+// for one store.
+template <bool GATED>
 __device__ __forceinline__ u32x4 outw_o(StateLds& sm, const OutFrags& cur, const f32x4 (&Zc)[2],
-                                        int cw, int lane, int xrow, int xcol) {
+                                        const uint4& z, int cw, int lane, int xrow, int xcol) {
     const int r = lane & 15, q4 = lane >> 4;
+    f32x4 acc[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
-        f32x4 acc = mma32(cur.P[0], ld8(sm.Rt + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
-        if (cw >= 2) acc = mma32(cur.P[1], ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4), acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[e]);
+        acc[jb] = mma32(cur.P[0], ld8(sm.Rt + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
+        if (cw >= 2) acc[jb] = mma32(cur.P[1], ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4), acc[jb]);
     }
-    __builtin_amdgcn_wave_barrier();
-    const uint4 x = *reinterpret_cast<const uint4*>(sm.O + xrow * LDX + xcol);
-    return u32x4{x.x, x.y, x.z, x.w};
+    return stage_out<GATED>(sm, acc, z, cw, lane, xrow, xcol);
 }
 
 }  // namespace co

@@ -40,15 +40,15 @@ _SIGNATURES = {
     "kda_state_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
     "kda_state_init": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _i32, _vp]),
     "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32,
-                                   _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
-                                   ctypes.c_size_t, _vp]),
+                                   _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                   _vp, ctypes.c_size_t, _vp]),
     "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "kda_prefill_workspace_bytes_batch": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32, _i32,
                                                             _i32]),
     "kda_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp,
-                               _i32, _i32, _i32, _i32, _vp, _vp]),
+                               _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "kda_decode_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp,
-                                 _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+                                 _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "kda_short_conv_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32, _vp,
                                       _vp, _vp, _vp]),
     "kda_short_conv_decode": (_i32, [_vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _f32,
@@ -274,11 +274,13 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
                         initial_state=None, final_state=None, o=None,
                         output_final_state: bool = True, cu_seqlens_host=None,
                         workspace="auto", snapshots=None, snap_interval: int = 0,
-                        a_log=None, stream=None):
+                        a_log=None, out_gate=None, stream=None):
     """Chunked prefill over packed sequences.  q, k: [T, H, dk]; v: [T, H, dv];
     g: [T, H, dk] (per-channel decay) or [T, H] (per-head decay); beta: [T, H].
     With a_log ([H] fp32), g is the decay projection f (q's dtype) and beta the
     write-strength logits: log alpha = -exp(a_log) softplus(f), beta = sigmoid.
+    out_gate: None, or the output gate's projection z [T, H, dv] in q's dtype:
+    o is then o * sigmoid(z).
     Returns (o, final_state or None), or (o, final_state, snapshots) when
     snapshots is given.
 
@@ -308,6 +310,9 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     if o is not None:
         _shape("o", o, (T, H, dv))
         _dtype("o", o, q.dtype)
+    if out_gate is not None:
+        _shape("out_gate", out_gate, (T, H, dv))
+        _dtype("out_gate", out_gate, q.dtype)
     if isinstance(snapshots, torch.Tensor):
         _need(snapshots.dim() == 5 and tuple(snapshots.shape[:1]) == (n_seqs,) and
               tuple(snapshots.shape[2:]) == (H, dk, dv),
@@ -316,7 +321,7 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     if isinstance(workspace, torch.Tensor):
         _dtype("workspace", workspace, torch.uint8)
     _same_device(q, k=k, v=v, g=g, beta=beta, a_log=a_log, initial_state=initial_state,
-                 final_state=final_state, o=o,
+                 final_state=final_state, o=o, out_gate=out_gate,
                  snapshots=snapshots if isinstance(snapshots, torch.Tensor) else None,
                  workspace=workspace if isinstance(workspace, torch.Tensor) else None)
     handle, st = _stream(stream, q.device)
@@ -343,14 +348,14 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     _check(load().kda_prefill_chunked(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q),
         _gate_code(g, q, a_log), _ptr(a_log), _ptr(cu_dev), cu_host.data_ptr(), n_seqs, H, dk,
-        dv, int(chunk), _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(snapshots),
-        int(snap_interval), snap_cap, _ptr(workspace), ws_bytes, handle))
+        dv, int(chunk), _ptr(initial_state), _ptr(final_state), _ptr(out_gate), _ptr(o),
+        _ptr(snapshots), int(snap_interval), snap_cap, _ptr(workspace), ws_bytes, handle))
     if want_snaps:
         return o, final_state, snapshots
     return o, final_state
 
 
-def _decode_checks(q, k, v, g, beta, state, slot_idx, o, a_log, lead):
+def _decode_checks(q, k, v, g, beta, state, slot_idx, o, a_log, lead, out_gate=None):
     """Shapes, dtypes and devices of a decode call; lead = (B,) or (B, n_tok)."""
     _dtype("q", q, (torch.float32, torch.bfloat16))
     _shape("k", k, q.shape)
@@ -369,41 +374,47 @@ def _decode_checks(q, k, v, g, beta, state, slot_idx, o, a_log, lead):
     if slot_idx is not None:
         _shape("slot_idx", slot_idx, (lead[0],))
         _dtype("slot_idx", slot_idx, torch.int32)
-    if o is not None:
-        _shape("o", o, tuple(lead) + (H, dv))
-        _dtype("o", o, q.dtype)
-    _same_device(q, k=k, v=v, g=g, beta=beta, a_log=a_log, state=state, slot_idx=slot_idx, o=o)
+    for name, t in (("o", o), ("out_gate", out_gate)):
+        if t is not None:
+            _shape(name, t, tuple(lead) + (H, dv))
+            _dtype(name, t, q.dtype)
+    _same_device(q, k=k, v=v, g=g, beta=beta, a_log=a_log, state=state, slot_idx=slot_idx, o=o,
+                 out_gate=out_gate)
     return H, dk, dv
 
 
-def kda_decode_step(q, k, v, g, beta, state, slot_idx=None, o=None, a_log=None, stream=None):
+def kda_decode_step(q, k, v, g, beta, state, slot_idx=None, o=None, a_log=None, out_gate=None,
+                    stream=None):
     """One token per sequence.  q, k: [B, H, dk]; g: [B, H, dk] or [B, H] (or the
     decay projection with a_log, as in kda_prefill_chunked); v: [B, H, dv]; beta: [B, H];
     state [n_slots, H, dk, dv] fp32 or bf16, updated in place; slot_idx: int32
-    [B] or None.  Returns o [B, H, dv]."""
+    [B] or None; out_gate: None or z [B, H, dv] (o * sigmoid(z)).  Returns
+    o [B, H, dv]."""
     _need(q.dim() == 3, "q must be [B, H, dk]")
     B = q.shape[0]
-    H, dk, dv = _decode_checks(q, k, v, g, beta, state, slot_idx, o, a_log, (B,))
+    H, dk, dv = _decode_checks(q, k, v, g, beta, state, slot_idx, o, a_log, (B,), out_gate)
     handle, st = _stream(stream, q.device)
     if o is None:
         o = _on_stream(torch.empty((B, H, dv), dtype=q.dtype, device=q.device), st)
     _check(load().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q, a_log),
         _ptr(a_log), _ptr(state), _state_code(state), state.shape[0], _ptr(slot_idx), B, H, dk,
-        dv, _ptr(o), handle))
+        dv, _ptr(out_gate), _ptr(o), handle))
     return o
 
 
 def kda_decode_tokens(q, k, v, g, beta, state, slot_idx=None, o=None, token_states=None,
-                      a_log=None, stream=None):
+                      a_log=None, out_gate=None, stream=None):
     """n_tok consecutive tokens per sequence.  q, k: [B, n_tok, H, dk]; g: the same
     shape or [B, n_tok, H]; v: [B, n_tok, H, dv]; beta: [B, n_tok, H]; state
     [n_slots, H, dk, dv] fp32 or bf16, updated in place.  token_states: None,
     True (allocate [B, n_tok, H, dk, dv] of the state's dtype) or such a tensor.
+    out_gate: None or z [B, n_tok, H, dv] (o * sigmoid(z)).
     Returns (o [B, n_tok, H, dv], token_states)."""
     _need(q.dim() == 4, "q must be [B, n_tok, H, dk]")
     B, n_tok = q.shape[0], q.shape[1]
-    H, dk, dv = _decode_checks(q, k, v, g, beta, state, slot_idx, o, a_log, (B, n_tok))
+    H, dk, dv = _decode_checks(q, k, v, g, beta, state, slot_idx, o, a_log, (B, n_tok),
+                               out_gate)
     if isinstance(token_states, torch.Tensor):
         _shape("token_states", token_states, (B, n_tok, H, dk, dv))
         _dtype("token_states", token_states, state.dtype)
@@ -417,7 +428,8 @@ def kda_decode_tokens(q, k, v, g, beta, state, slot_idx=None, o=None, token_stat
     _check(load().kda_decode_tokens(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q), _gate_code(g, q, a_log),
         _ptr(a_log), _ptr(state), _state_code(state), state.shape[0], _ptr(slot_idx), B, n_tok,
-        H, dk, dv, _ptr(o), _ptr(token_states) if token_states is not None else None, handle))
+        H, dk, dv, _ptr(out_gate), _ptr(o), _ptr(token_states) if token_states is not None else None,
+        handle))
     return o, token_states
 
 

@@ -154,6 +154,18 @@ kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, i
  *   initial_state   : [n_seqs, H, dk, dv] fp32, or NULL for zeros.
  *   final_state     : [n_seqs, H, dk, dv] fp32, or NULL (not written).  May be
  *                     the same pointer as initial_state (in-place update).
+ *   out_gate        : [T, H, dv] dtype, or NULL.  The output gate: when given,
+ *                     every output is o_t * sigmoid(out_gate_t), elementwise
+ *                     per (token, head, value channel), rounded to dtype once.
+ *                     Page "Ling-3.1-flash: a 560B hybrid-attention MoE,
+ *                     counted from its safetensors headers" (section "How KDA
+ *                     and MLA split the work") lists a full-rank gate
+ *                     projection (4096 -> 8192, one value per head and value
+ *                     channel) before the output projection, without naming
+ *                     its activation; the sigmoid is the one the same section
+ *                     gives the gated MLA's output gate.  No normalisation
+ *                     comes before it (the pages name none).  Must not overlap
+ *                     o or final_state.
  *   o               : [T, H, dv] dtype, written; must not overlap any input.
  *   snapshots       : [n_seqs, snap_capacity, H, dk, dv] fp32, or NULL.  Entry
  *                     [n, j] receives sequence n's state after its first
@@ -197,7 +209,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
                                const float* a_log,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                int n_seqs, int H, int dk, int dv, int chunk,
-                               const float* initial_state, float* final_state, void* o,
+                               const float* initial_state, float* final_state,
+                               const void* out_gate, void* o,
                                float* snapshots, int snap_interval, int snap_capacity,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -252,6 +265,8 @@ size_t kda_prefill_workspace_bytes_batch(const int32_t* cu_seqlens_host, int n_s
  *              NULL for slot b = b (then n_slots >= B).  Slots must be
  *              distinct.  A slot outside [0, n_slots) is not touched and that
  *              sequence's output is set to NaN.
+ *   out_gate : [B, H, dv] dtype or NULL: the output gate, o * sigmoid(out_gate),
+ *              as in kda_prefill_chunked.
  * Supported: dk == dv in {16, 32, 64, 128}.  Each state is read once and
  * written once (fused form of one recurrence step).
  */
@@ -259,7 +274,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            const float* beta, kda_dtype dtype, kda_gate gate,
                            const float* a_log, void* state,
                            kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
-                           int B, int H, int dk, int dv, void* o, hipStream_t stream);
+                           int B, int H, int dk, int dv, const void* out_gate, void* o,
+                           hipStream_t stream);
 
 /*
  * kda_decode_tokens -- advance B sequences by n_tok consecutive tokens each, in
@@ -285,6 +301,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
  *   state_dtype  : as in kda_decode_step (a bf16 state is rounded once, after
  *                  the last token).
  *   slot_idx     : as in kda_decode_step.
+ *   out_gate     : [B, n_tok, H, dv] dtype or NULL: the output gate, as in
+ *                  kda_prefill_chunked.
  *   token_states : [B, n_tok, H, dk, dv] state_dtype, or NULL.  When given, entry
  *                  [b, j] receives sequence b's state after token j, so that
  *                  a caller that accepts only the first m drafts can restore
@@ -298,8 +316,8 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const 
                              const float* beta, kda_dtype dtype, kda_gate gate,
                              const float* a_log, void* state,
                              kda_dtype state_dtype, int64_t n_slots, const int32_t* slot_idx,
-                             int B, int n_tok, int H, int dk, int dv, void* o,
-                             void* token_states, hipStream_t stream);
+                             int B, int n_tok, int H, int dk, int dv, const void* out_gate,
+                             void* o, void* token_states, hipStream_t stream);
 
 /*
  * kda_short_conv_prefill -- width-4 causal depthwise convolution over packed

@@ -58,13 +58,13 @@ def cu_arr(vals):
 
 def prefill(lib, **kw):
     a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=0, a_log=None, cu_dev=Fp,
-             cu_host=cu_arr([0, 8]), n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, o=Gp,
-             snaps=None, snap_interval=0, snap_capacity=0, ws=None, ws_bytes=0, stream=None)
+             cu_host=cu_arr([0, 8]), n=1, H=2, dk=128, dv=128, chunk=64, s0=None, sf=None, og=None,
+             o=Gp, snaps=None, snap_interval=0, snap_capacity=0, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
                                    a["gate"], a["a_log"], a["cu_dev"], a["cu_host"], a["n"], a["H"], a["dk"],
                                    a["dv"],
-                                   a["chunk"], a["s0"], a["sf"], a["o"], a["snaps"],
+                                   a["chunk"], a["s0"], a["sf"], a["og"], a["o"], a["snaps"],
                                    a["snap_interval"], a["snap_capacity"], a["ws"], a["ws_bytes"],
                                    a["stream"])
 
@@ -105,6 +105,9 @@ def prefill(lib, **kw):
      "snapshots overlap"),
     (dict(snaps=Hp, snap_interval=64, snap_capacity=2, s0=Hp + 2 * 65536),
      KDA_ERR_INVALID_ARGUMENT, "snapshots overlap"),
+    (dict(og=Hp + 8), KDA_ERR_INVALID_ARGUMENT, "misaligned out_gate"),
+    (dict(og=Gp + 16), KDA_ERR_INVALID_ARGUMENT, "o overlaps"),
+    (dict(og=Hp, sf=Hp + 64), KDA_ERR_INVALID_ARGUMENT, "final_state overlaps out_gate"),
 ])
 def test_prefill_rejects(lib, kw, status, needle):
     assert prefill(lib, **kw) == status
@@ -161,11 +164,11 @@ def test_prefill_nothing_to_do(lib):
 
 def decode(lib, **kw):
     a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_F32, gate=0, a_log=None, state=Fp,
-             sdt=KDA_F32, n_slots=4, slot=None, B=4, H=2, dk=64, dv=64, o=Gp, stream=None)
+             sdt=KDA_F32, n_slots=4, slot=None, B=4, H=2, dk=64, dv=64, og=None, o=Gp, stream=None)
     a.update(kw)
     return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"], a["gate"],
                                a["a_log"], a["state"], a["sdt"], a["n_slots"], a["slot"], a["B"], a["H"],
-                               a["dk"], a["dv"], a["o"], a["stream"])
+                               a["dk"], a["dv"], a["og"], a["o"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -184,6 +187,8 @@ def decode(lib, **kw):
     (dict(sdt=3), KDA_ERR_INVALID_ARGUMENT, "state dtype"),
     # a bf16 state is half the bytes: this one ends just below o, an fp32 one would not
     (dict(state=Gp - 4 * 2 * 64 * 64 * 2, sdt=KDA_F32), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
+    (dict(og=Hp + 4), KDA_ERR_INVALID_ARGUMENT, "misaligned"),
+    (dict(og=Gp + 64), KDA_ERR_INVALID_ARGUMENT, "overlaps"),
 ])
 def test_decode_rejects(lib, kw, status, needle):
     assert decode(lib, **kw) == status
@@ -192,12 +197,12 @@ def test_decode_rejects(lib, kw, status, needle):
 
 def decode_tokens(lib, **kw):
     a = dict(q=A, k=Bp, v=Cp, g=Dp, beta=Ep, dtype=KDA_BF16, gate=1, a_log=None, state=Fp,
-             sdt=KDA_BF16, n_slots=4, slot=None, B=4, n_tok=3, H=2, dk=128, dv=128, o=Gp,
-             snaps=None, stream=None)
+             sdt=KDA_BF16, n_slots=4, slot=None, B=4, n_tok=3, H=2, dk=128, dv=128, og=None,
+             o=Gp, snaps=None, stream=None)
     a.update(kw)
     return lib.kda_decode_tokens(a["q"], a["k"], a["v"], a["g"], a["beta"], a["dtype"],
                                  a["gate"], a["a_log"], a["state"], a["sdt"], a["n_slots"], a["slot"], a["B"],
-                                 a["n_tok"], a["H"], a["dk"], a["dv"], a["o"], a["snaps"],
+                                 a["n_tok"], a["H"], a["dk"], a["dv"], a["og"], a["o"], a["snaps"],
                                  a["stream"])
 
 

@@ -19,6 +19,8 @@ sigma):
 * initial states ~ N(0, s0_std) fp32 where a workload has one, else zero.
 * mixer workload: pre-convolution streams x_q, x_k, x_v ~ N(0, 1) rounded to
   bf16, convolution weights ~ N(0, 0.5) fp32.
+* output gate projection z ~ N(0, 1) per (token, head, value channel), rounded
+  to the input dtype.
 
 Random numbers come from numpy's PCG64 in fixed blocks of 2^22 elements, each
 block seeded by (workload seed, tensor id, block index), so the values do not
@@ -37,7 +39,7 @@ _BLOCK = 1 << 22
 
 # tensor ids: the order in which a workload's tensors are drawn
 TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "S0": 5, "conv_w": 6,
-       "x_q": 7, "x_k": 8, "x_v": 9, "f": 10, "a_log": 11, "b": 12}
+       "x_q": 7, "x_k": 8, "x_v": 9, "f": 10, "a_log": 11, "b": 12, "z": 13}
 
 
 def _threads() -> int:
@@ -221,6 +223,13 @@ def gate_projections(T, H, d, dtype="bf16", g_mu=2.0, g_sigma=0.5, a_log_std=0.0
              else torch.zeros(H))
     b = normal((T, H), seed, TID["b"])
     return GateProjections(f, a_log, b)
+
+
+def output_gate_projection(T, H, dv, dtype="bf16", seed=0) -> torch.Tensor:
+    """The output gate's projection z ~ N(0, 1) per (token, head, value channel),
+    rounded to dtype: [T, H, dv] (or any leading shape given as T)."""
+    lead = tuple(T) if isinstance(T, (tuple, list)) else (T,)
+    return to_dtype(normal(lead + (H, dv), seed, TID["z"]), dtype)
 
 
 def mixer_conv_streams(t_prefill=32768, seed=1005):
