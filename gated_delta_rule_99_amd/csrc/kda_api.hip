@@ -96,6 +96,15 @@ kda_status check_cu(const char* fn, const int32_t* cu_host, int n_seqs, int64_t*
 
 }  // namespace
 
+namespace kda {
+void set_error_detail(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+}
+}  // namespace kda
+
 extern "C" {
 
 const char* kda_status_string(kda_status s) {
@@ -141,15 +150,19 @@ kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, i
                       "kda_state_init launch");
 }
 
-kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const void* g,
-                               const float* beta, kda_dtype dtype, kda_gate gate,
-                               const float* a_log, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
-                               int n_seqs, int H, int dk, int dv, int chunk,
-                               const float* initial_state, float* final_state,
-                               const void* out_gate, void* o,
-                               float* snapshots, int snap_interval, int snap_capacity,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    const char* fn = "kda_prefill_chunked";
+// The body of kda_prefill_chunked and kda_prefill_chunked_noalloc.  ws_floor:
+// the smallest workspace accepted for the matrix-core shapes: the size
+// kda_prefill_workspace_bytes returns (kda_prefill_chunked), or the least the
+// two-kernel path can run on, one tile per sequence and head (the static
+// scratch of kda_prefill_chunked_noalloc; windows are then shorter).
+static kda_status prefill_entry(const char* fn, const void* q, const void* k, const void* v,
+                                const void* g, const float* beta, kda_dtype dtype, kda_gate gate,
+                                const float* a_log, const int32_t* cu_seqlens_dev,
+                                const int32_t* cu_seqlens_host, int n_seqs, int H, int dk, int dv,
+                                int chunk, const float* initial_state, float* final_state,
+                                const void* out_gate, void* o, float* snapshots,
+                                int snap_interval, int snap_capacity, void* workspace,
+                                size_t workspace_bytes, bool floor_one_tile, hipStream_t stream) {
     g_detail[0] = 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
@@ -228,7 +241,9 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
     const kda::Snapshots snap{snapshots, snapshots ? snap_interval : 0, snap_capacity};
 
     const bool mfma = mfma_shape(dtype, dk, dv, chunk);
-    const size_t ws_need = mfma ? kda::prefill_split_workspace_bytes(n_seqs, H) : 0;
+    const size_t ws_need = !mfma          ? 0
+                           : floor_one_tile ? kda::prefill_split_workspace_bytes_least(n_seqs, H)
+                                            : kda::prefill_split_workspace_bytes(n_seqs, H);
     if (mfma && workspace) {
         if (workspace_bytes < ws_need)
             return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, %zu needed", fn,
@@ -259,6 +274,53 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, cons
                                          d, chunk, initial_state, final_state, out_gate, o, snap,
                                          stream);
     return hip_status(err, "kda_prefill_chunked launch");
+}
+
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, const void* g,
+                               const float* beta, kda_dtype dtype, kda_gate gate,
+                               const float* a_log, const int32_t* cu_seqlens_dev,
+                               const int32_t* cu_seqlens_host, int n_seqs, int H, int dk, int dv,
+                               int chunk, const float* initial_state, float* final_state,
+                               const void* out_gate, void* o, float* snapshots, int snap_interval,
+                               int snap_capacity, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    return prefill_entry("kda_prefill_chunked", q, k, v, g, beta, dtype, gate, a_log,
+                         cu_seqlens_dev, cu_seqlens_host, n_seqs, H, dk, dv, chunk, initial_state,
+                         final_state, out_gate, o, snapshots, snap_interval, snap_capacity,
+                         workspace, workspace_bytes, false, stream);
+}
+
+kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       const void* g, const float* beta, kda_dtype dtype,
+                                       kda_gate gate, const float* a_log,
+                                       const int32_t* cu_seqlens_dev,
+                                       const int32_t* cu_seqlens_host, int n_seqs, int H, int dk,
+                                       int dv, int chunk, const float* initial_state,
+                                       float* final_state, const void* out_gate, void* o,
+                                       float* snapshots, int snap_interval, int snap_capacity,
+                                       hipStream_t stream) {
+    const char* fn = "kda_prefill_chunked_noalloc";
+    g_detail[0] = 0;
+    // matrix-core shapes run on the static scratch: at least one tile per
+    // sequence and head must fit in it
+    const bool needs_scratch = n_seqs > 0 && H > 0 && mfma_shape(dtype, dk, dv, chunk);
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (needs_scratch) {
+        const size_t least = kda::prefill_split_workspace_bytes_least(n_seqs, H);
+        if (least > kda::static_scratch_bytes())
+            return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                        "%s: %d sequences x %d heads need %zu bytes of scratch, the library's "
+                        "static scratch holds %zu", fn, n_seqs, H, least,
+                        kda::static_scratch_bytes());
+        if (kda_status s = hip_status(kda::static_scratch(stream, &ws), "static scratch lookup"))
+            return s;
+        ws_bytes = kda::static_scratch_bytes();
+    }
+    return prefill_entry(fn, q, k, v, g, beta, dtype, gate, a_log, cu_seqlens_dev,
+                         cu_seqlens_host, n_seqs, H, dk, dv, chunk, initial_state, final_state,
+                         out_gate, o, snapshots, snap_interval, snap_capacity, ws, ws_bytes, true,
+                         stream);
 }
 
 size_t kda_prefill_workspace_bytes_batch(const int32_t* cu_seqlens_host, int n_seqs, int H,

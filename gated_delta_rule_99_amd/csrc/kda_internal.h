@@ -126,6 +126,9 @@ __device__ __forceinline__ float sigmoid_f(float x) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
 }
 
+// The calling thread's error text (what kda_last_error_detail returns).
+void set_error_detail(const char* fmt, ...);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already checked.
 // out_gate, where taken: the output gate's projection z in o's layout and dtype,
@@ -159,6 +162,14 @@ hipError_t launch_prefill_fused(const void* q, const void* k, const void* v, Gat
 // prefill_split_workspace_bytes(n_seqs, H) bytes; cu_host: the validated host
 // copy of cu_seqlens (for the window plan).
 size_t prefill_split_workspace_bytes(int n_seqs, int H);
+// The least workspace the two-kernel path runs on: one tile per sequence and
+// head (windows of one chunk where nothing more fits).
+size_t prefill_split_workspace_bytes_least(int n_seqs, int H);
+
+// The library's static device scratch (kda_noalloc.hip): its size, and its
+// address on the device that `stream` runs on (looked up once per device).
+size_t static_scratch_bytes();
+hipError_t static_scratch(hipStream_t stream, void** out);
 size_t prefill_split_workspace_bytes_batch(const int32_t* cu_host, int n_seqs, int H);
 hipError_t launch_prefill_split(const void* q, const void* k, const void* v, Gate gate,
                                 const float* beta, const int32_t* cu, const int32_t* cu_host,

@@ -413,6 +413,9 @@ static size_t tile_bytes(int n_seqs, int H) {
     const size_t most = one * MAX_WIN < TILE_BUDGET ? one * MAX_WIN : TILE_BUDGET;
     return most > one ? most : one;
 }
+size_t prefill_split_workspace_bytes_least(int n_seqs, int H) {
+    return (size_t)n_seqs * H * D * D * 4 + order_bytes(n_seqs) + (size_t)n_seqs * H * TILE;
+}
 size_t prefill_split_workspace_bytes(int n_seqs, int H) {
     return (size_t)n_seqs * H * D * D * 4 + order_bytes(n_seqs) + tile_bytes(n_seqs, H);
 }

@@ -42,6 +42,9 @@ _SIGNATURES = {
     "kda_prefill_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32,
                                    _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                    _vp, ctypes.c_size_t, _vp]),
+    "kda_prefill_chunked_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
+                                           _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                           _vp, _i32, _i32, _vp]),
     "kda_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "kda_prefill_workspace_bytes_batch": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32, _i32,
                                                             _i32]),
@@ -285,8 +288,10 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     snapshots is given.
 
     workspace: "auto" (a cached device buffer of kda_prefill_workspace_bytes_batch,
-    one per device and stream), a uint8 device tensor, or None (no workspace:
-    the fused kernel).
+    one per device and stream), a uint8 device tensor, None (no workspace:
+    the fused kernel), or "static": kda_prefill_chunked_noalloc, which runs the
+    two-kernel path on the library's static scratch and allocates nothing (the
+    binding still allocates o and final_state when they are not given).
     snapshots: None, True (allocate [n_seqs, longest // snap_interval, H, dk, dv]
     fp32 zeros) or such a tensor; entry [n, j] receives sequence n's state after
     (j + 1) * snap_interval tokens where it has that many."""
@@ -339,9 +344,16 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=None, chunk: int = 64,
     if final_state is None and output_final_state:
         final_state = _on_stream(torch.empty((n_seqs, H, dk, dv), dtype=torch.float32,
                                              device=q.device), st)
+    if workspace == "static":
+        _check(load().kda_prefill_chunked_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q),
+            _gate_code(g, q, a_log), _ptr(a_log), _ptr(cu_dev), cu_host.data_ptr(), n_seqs, H,
+            dk, dv, int(chunk), _ptr(initial_state), _ptr(final_state), _ptr(out_gate), _ptr(o),
+            _ptr(snapshots), int(snap_interval), snap_cap, handle))
+        return (o, final_state, snapshots) if want_snaps else (o, final_state)
     if isinstance(workspace, str):
         if workspace != "auto":
-            raise ValueError("workspace must be 'auto', a tensor or None")
+            raise ValueError("workspace must be 'auto', 'static', a tensor or None")
         need = kda_prefill_workspace_bytes_batch(cu_host, H, dk, dv, chunk, q.dtype)
         workspace = _workspace(need, q.device, handle, st) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -215,6 +215,35 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_prefill_chunked_noalloc -- kda_prefill_chunked for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those of
+ * kda_prefill_chunked, without the workspace: the matrix-core shapes (bf16,
+ * dk = dv = 128, chunk 64) run the two-kernel path on a static scratch array
+ * of 128 MiB that the library keeps in every GPU's memory it runs on until the
+ * process ends; the other shapes need no scratch.  The call allocates no
+ * device memory (no hipMalloc, hipFree or memset), so it may be captured in a
+ * graph.  The two-kernel path runs on any workspace that holds the state
+ * carry and one operand tile per sequence and head (123 648 bytes per sequence
+ * and head, plus 256 per 64 sequences), in windows as long as the rest of the
+ * scratch allows (up to 32 chunks: at H = 64, the full length for one
+ * sequence, one chunk for 16); a batch that needs more than the scratch returns
+ * KDA_ERR_WORKSPACE_TOO_SMALL: at H = 64, more than 16 sequences per call.  The first call on a device looks the array's address up
+ * (KDA_ERR_HIP if that fails).  All calls on one GPU share its array, which
+ * keeps the last call's contents: calls that overlap on one GPU (unordered
+ * streams) race on it and must be serialised by the caller.
+ */
+kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       const void* g, const float* beta, kda_dtype dtype,
+                                       kda_gate gate, const float* a_log,
+                                       const int32_t* cu_seqlens_dev,
+                                       const int32_t* cu_seqlens_host, int n_seqs, int H, int dk,
+                                       int dv, int chunk, const float* initial_state,
+                                       float* final_state, const void* out_gate, void* o,
+                                       float* snapshots, int snap_interval, int snap_capacity,
+                                       hipStream_t stream);
+
+/*
  * kda_prefill_workspace_bytes -- size of the workspace that lets
  * kda_prefill_chunked use its two-kernel matrix-core path for this shape; 0 when
  * the shape runs a path that needs none.  Depends only on n_seqs and H for the

@@ -374,3 +374,16 @@ def test_binding_checks_decode_arguments(change, err, needle):
     tok = {k_: (v_.unsqueeze(1) if k_ not in ("state", "slot_idx") else v_) for k_, v_ in a.items()}
     with pytest.raises(err):
         kda_pkg.kda_decode_tokens(**tok)
+
+
+def test_noalloc_rejects_beyond_its_scratch(lib):
+    """The no-allocation prefill rejects, before any HIP call, a batch whose
+    workspace exceeds the static scratch (128 MiB): 64 sequences x 64 heads
+    need 64 * 64 * (65536 + 58112) bytes and more."""
+    f = lib.kda_prefill_chunked_noalloc
+    n = 64
+    cu = cu_arr(list(range(0, 64 * (n + 1), 64)))
+    st = f(A, Bp, Cp, Dp, Ep, KDA_BF16, 0, None, Fp, cu, n, 64, 128, 128, 64, None, None, None,
+           Gp, None, 0, 0, None)
+    assert st == KDA_ERR_WORKSPACE_TOO_SMALL
+    assert "static scratch holds 134217728" in lib.kda_last_error_detail().decode()
