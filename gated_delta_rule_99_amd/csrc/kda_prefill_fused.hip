@@ -3,7 +3,7 @@
 // (kda_prefill_split.hip; recurrence from page "Ling-3.1-flash: a 560B
 // hybrid-attention MoE, counted from its safetensors headers", section "How
 // KDA and MLA split the work"):
-//   G = Gam * S,  U = T diag(beta)(V - Kt G),  O = Qt G + P U,  S <- G + Kb^T U.
+//   G = 2^R S,  U = T diag(beta)(V - Kt G),  O = Qt G + P U,  S <- Gam S + Kbar^T U.
 //
 // One workgroup per (sequence, head, 32-column slice of the state), the four
 // slices of a head on one XCD so that q, k, g come from HBM once and from L2
@@ -20,6 +20,8 @@
 //   step s:  [A] producer decay(s+1) | chain Y, R      | output Z
 //            B1
 //            [B] producer N(s+1)     | chain U          |
+//                (a chunk on the pairwise path: PAIR_SYNCS more barriers here,
+//                 which every wave takes; it also forms P here)
 //            B2
 //            [C] producer merge(s+1) | chain S, G(s+1)  | output O, store
 //            B3
@@ -34,10 +36,19 @@ using namespace co;
 
 struct FusedLds {
     ChunkLds ck;              // operand stages of the next chunk
-    uint16_t KbT[D * LDT];    // Kb^T [i][t] of the next chunk
+    uint16_t KbT[D * LDT];    // Kbar^T [i][t] of the next chunk
     float gam[D];             // Gam of the next chunk
+    int slow[4];              // per producer wave: the next chunk takes the pairwise path
     StateLds st;              // state pass (kda_state_pass.h)
 };
+// The pairwise path's rows sit over Kb, T, Tt and P: Kt and Qt stay for the
+// copy-in of the chunk's fragments.
+static_assert(sizeof(PairLds) <= sizeof(ChunkLds) - offsetof(ChunkLds, Kb) - sizeof(float) * C,
+              "the pairwise path's rows fit over Kb, T, Tt and P");
+// Barriers that a chunk on the pairwise path adds to the producer's N phase (four
+// in slow_products and one before its results are stored); the other waves
+// match them.
+constexpr int PAIR_SYNCS = 5;
 
 }  // namespace fu
 
@@ -110,25 +121,63 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         auto kbt_sink = [&](int i, int tg, u32x4 piece) {
             *reinterpret_cast<u32x4*>(sm.KbT + i * LDT + 8 * tg) = piece;
         };
+        // [B] of chunk c: N (and T's diagonal blocks) on the matrix cores, or on
+        // the pairwise path (then P too, and PAIR_SYNCS barriers)
+        auto n_phase = [&](int c, bool slow) {
+            if (!slow) {
+                n_stage(sm.ck, p, lane);
+                return;
+            }
+            ChunkIn in2;
+            load_chunk<GM>(in2, q, k, g, beta, tb + (int64_t)c * C, chunk_len(c), H, h, p, lane);
+            NRaw nw;
+            f32x4 pb[3];
+            slow_products<GM>(*reinterpret_cast<PairLds*>(sm.ck.Kb), in2, p, lane, nw, pb,
+                              [] { __syncthreads(); });
+            NRegs nr;
+            n_finish(sm.ck.beta, p, lane, nw, nr);
+            __syncthreads();  // the pairwise rows are read in full
+            n_store(sm.ck, p, lane, nr);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                if (j >= p_count(p)) break;
+                int rb, cb;
+                lower_block(p_first(p) + j, rb, cb);
+                p_store(sm.ck, rb, cb, lane, pb[j]);
+            }
+            if (p == 0 || p == 2) {  // T's and P's upper blocks the copy-in reads: (0,1), (2,3)
+                st4(sm.ck.T + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
+                st4(sm.ck.P + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
+            }
+        };
+        auto slow_flag = [&]() { return sm.slow[0] | sm.slow[1] | sm.slow[2] | sm.slow[3]; };
         ChunkIn in;
         load_chunk<GM>(in, q, k, g, beta, tb, chunk_len(0), H, h, p, lane);
-        decay_stage<GM>(sm.ck, in, p, lane, gam_sink, kbt_sink);
+        {
+            const bool ws = decay_stage<GM>(sm.ck, in, p, lane, gam_sink, kbt_sink);
+            if (lane == 0) sm.slow[p] = ws;
+        }
         load_chunk<GM>(in, q, k, g, beta, tb + C, chunk_len(1), H, h, p, lane);
         __syncthreads();  // P1
-        n_stage(sm.ck, p, lane);
+        bool slow = slow_flag();
+        n_phase(0, slow);
         __syncthreads();  // P2
-        merge_stage(sm.ck, p, lane);
+        merge_stage(sm.ck, p, lane, !slow);
         __syncthreads();  // P3
         __syncthreads();  // P4: copy-in of chunk 0 done
         for (int s = 0; s < nc; ++s) {
             const bool next = s + 1 < nc;
-            if (next) decay_stage<GM>(sm.ck, in, p, lane, gam_sink, kbt_sink);
+            if (next) {
+                const bool ws = decay_stage<GM>(sm.ck, in, p, lane, gam_sink, kbt_sink);
+                if (lane == 0) sm.slow[p] = ws;
+            }
             load_chunk<GM>(in, q, k, g, beta, tb + (int64_t)(s + 2) * C, chunk_len(s + 2), H, h, p,
                            lane);
             __syncthreads();  // B1
-            if (next) n_stage(sm.ck, p, lane);
+            slow = next && slow_flag();
+            if (next) n_phase(s + 1, slow);
             __syncthreads();  // B2
-            if (next) merge_stage(sm.ck, p, lane);
+            if (next) merge_stage(sm.ck, p, lane, !slow);
             __syncthreads();  // B3
             __syncthreads();  // B0
         }
@@ -169,12 +218,18 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             for (int kk = 0; kk < 2; ++kk) cur.T[kk] = ld8(sm.ck.T + (16 * cw + r) * LDT + 32 * kk + 8 * q4);
             cur.bet = *reinterpret_cast<const float4*>(sm.ck.beta + 16 * cw + 4 * q4);
         };
+        auto pair_syncs = [&](bool slow) {  // the producer's pairwise path, if taken
+            if (slow)
+                for (int i = 0; i < PAIR_SYNCS; ++i) __syncthreads();
+        };
+        auto slow_flag = [&]() { return sm.slow[0] | sm.slow[1] | sm.slow[2] | sm.slow[3]; };
         __syncthreads();  // P1: Gam of chunk 0 is in LDS
         {
             float4 gm[2];
             gam_lds(gm);
             chain_scale_store(sm.st, S, gm, cw, lane);
         }
+        pair_syncs(slow_flag());
         __syncthreads();  // P2
         __syncthreads();  // P3
         copy_in();
@@ -187,10 +242,12 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             cur.v = vnext;
             vnext = load_v(s + 2);
             __syncthreads();  // B1
+            const bool slow = next && slow_flag();
             // ---- [B] U = T R
             chain_u(sm.st, cur, cw, lane);
+            pair_syncs(slow);
             __syncthreads();  // B2
-            // ---- [C] S <- G + Kb^T U (a snapshot when one falls here); next G = Gam(s+1) * S
+            // ---- [C] S <- Gam S + Kbar^T U (a snapshot when one falls here); next operand
             {
                 float4 gm[2];
                 gam_lds(gm);
@@ -232,7 +289,13 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             return z;
         };
         uint4 znext = load_z(0);
+        auto pair_syncs = [&](bool slow) {  // the producer's pairwise path, if taken
+            if (slow)
+                for (int i = 0; i < PAIR_SYNCS; ++i) __syncthreads();
+        };
+        auto slow_flag = [&]() { return sm.slow[0] | sm.slow[1] | sm.slow[2] | sm.slow[3]; };
         __syncthreads();  // P1
+        pair_syncs(slow_flag());
         __syncthreads();  // P2
         __syncthreads();  // P3
         copy_in();
@@ -245,6 +308,7 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             f32x4 Zc[2];
             out_z(sm.st, cur, Zc, lane);
             __syncthreads();  // B1
+            pair_syncs(next && slow_flag());
             __syncthreads();  // B2
             // ---- [C] O = Z + P U (gated), staged through this wave's rows, one 16-byte store
             __builtin_amdgcn_raw_buffer_store_b128(

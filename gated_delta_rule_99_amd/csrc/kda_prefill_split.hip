@@ -1,12 +1,12 @@
 // KDA chunked prefill, two-kernel form for gfx950: bf16 q/k/v, d_k = d_v = 128,
-// chunk C = 64, fp32 state.  Per chunk, with the decay referenced to the chunk end,
-//   Kt = K * D, Qt = Q * D, Kb = K * F   (D = e^{b - b_C}, F = e^{b_C - b})
+// chunk C = 64, fp32 state.  Per chunk, with the scaled operands of
+// kda_chunk_ops.h (decay referenced to R = max(B_C, -RLIM) per channel),
 //   N = strict_lower(diag(beta) Kt Kb^T),  T = (I + N)^{-1},  P = lower(Qt Kb^T)
-//   G = Gam * S,  U = T diag(beta)(V - Kt G),  O = Qt G + P U,  S <- G + Kb^T U
+//   G = 2^R S,  U = T diag(beta)(V - Kt G),  O = Qt G + P U,  S <- Gam S + Kbar^T U
 // (recurrence from page "Ling-3.1-flash: a 560B hybrid-attention MoE, counted
 // from its safetensors headers", section "How KDA and MLA split the work").
-// With R = diag(beta)(V - Kt G), U = T R; T is folded into Wb^T = Kb^T T and
-// PT = P T, so that  S <- G + Wb^T R  and  O = Qt G + PT R.
+// With R = diag(beta)(V - Kt G), U = T R; T is folded into Wb^T = Kbar^T T and
+// PT = P T, so that  S <- Gam S + Wb^T R  and  O = Qt G + PT R.
 //
 // Everything that does not depend on the state is done ONCE per (sequence,
 // head, chunk) by prep_kernel, chunk-parallel, and stored in a workspace as
@@ -50,6 +50,7 @@ struct PrepLds {
     uint16_t Qt[C * LDK];  // [t][i]
     uint16_t Kb[C * LDK];  // [t][i]
     float beta[C];
+    int slow[4];           // per wave: some channel of it decays below 2^-SLOW
 };
 struct TpLds {
     uint16_t T[C * LDT];   // T [t][s], then PT [t][u]
@@ -59,13 +60,7 @@ struct TpLds {
     uint16_t Kbt[D * LDT]; // Kb^T [i][t], then Wb^T [i][u]
 };
 static_assert(sizeof(TpLds) <= sizeof(PrepLds), "the folded operands fit the stage rows");
-
-// Block k (row order) of the 16x16 blocks on and below the diagonal of a 4x4
-// grid: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
-__device__ __forceinline__ void lower_block(int k, int& rb, int& cb) {
-    rb = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
-    cb = k - rb * (rb + 1) / 2;
-}
+static_assert(sizeof(PairLds) <= 3 * C * LDK * 2, "the pairwise path's rows fit the stage rows");
 
 // The decay stage's sinks in prep_kernel: Gam to the tile, the Kb^T pieces of
 // channels ch0 .. ch0 + 3 (ch0 a multiple of 4) into registers.
@@ -119,19 +114,32 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
                                               OFF_BETA + 4 * lane, 0, 0);
     u32x4 kbt[4];  // Kb^T pieces: channel ch0 + e, tokens [8tg, 8tg + 8)
     const PrepSinks sinks{rt, kbt};
-    decay_stage<GM>(sm, in, p, lane, sinks, sinks);
+    const bool wave_slow = decay_stage<GM>(sm, in, p, lane, sinks, sinks);
+    if (lane == 0) sm.slow[p] = wave_slow;
     __syncthreads();
+    const bool slow = sm.slow[0] | sm.slow[1] | sm.slow[2] | sm.slow[3];  // uniform
     tile_export_kq(sm, rt, p, lane);
+    const int pn = p_count(p), pk0 = p_first(p);
     NRegs nr;
-    n_regs(sm, p, lane, nr);
-    const int pn = p < 2 ? 2 : 3, pk0 = p == 0 ? 0 : p == 1 ? 2 : p == 2 ? 4 : 7;
     f32x4 pb[3];
+    if (!slow) {
+        n_regs(sm, p, lane, nr);
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        if (j >= pn) break;
-        int rb, cb;
-        lower_block(pk0 + j, rb, cb);
-        pb[j] = p_tile(sm, rb, cb, lane);
+        for (int j = 0; j < 3; ++j) {
+            if (j >= pn) break;
+            int rb, cb;
+            lower_block(pk0 + j, rb, cb);
+            pb[j] = p_tile(sm, rb, cb, lane);
+        }
+    } else {
+        // some channel decays too strongly for the factored products: the
+        // pairwise path over the reloaded inputs (the stage rows are reused)
+        ChunkIn in2;
+        load_chunk<GM>(in2, q, k, g, beta, c0, L, H, h, p, lane);
+        NRaw nw;
+        slow_products<GM>(*reinterpret_cast<PairLds*>(sm.Kt), in2, p, lane, nw, pb,
+                          [] { __syncthreads(); });
+        n_finish(sm.beta, p, lane, nw, nr);
     }
     __syncthreads();  // the stage rows are read in full: T, Tt, P and Kb^T take their place
     n_store(tp, p, lane, nr);

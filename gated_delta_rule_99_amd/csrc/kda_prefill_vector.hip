@@ -13,6 +13,10 @@
 //   U  = (I + N)^{-1} diag(beta) (V - Kt S)            forward substitution
 //   O  = Qt S + lower(Qt Kh^T) U
 //   S <- Gam * S + (Kh * Gam)^T U                       (Kh * Gam = K e^{b_C - b})
+// (Kt Kh^T)[t][s] = K_t K_s e^{b_t - b_s}.  Where some channel's b_C drops below
+// -VEC_SLOW, Kh would overflow: that chunk forms every factor from b directly
+// (e^{b_t - b_s}, e^{b_t}, e^{b_C - b_t}, all at most 1), which holds for any
+// decay.
 // Tokens past the end of a sequence are treated as k = q = v = 0, g = 0,
 // beta = 0, which leaves the state unchanged.
 //
@@ -22,14 +26,17 @@
 
 namespace kda {
 
+constexpr float VEC_SLOW = 80.f;  // e^80 stays well inside fp32
+
 template <int D, int C>
 struct VecShape {
     static constexpr int DVS = D < 32 ? D : 32;    // value columns per workgroup
     static constexpr int NS = D / DVS;             // slices per head
     static constexpr int LD = D + 1;               // padded row of [C][D] tiles
     static constexpr int NT = 256;
-    // LDS floats: Kt, Kh, Qt [C][LD]; NP [C][C]; U [C][DVS]; S [D][DVS]; Gam [D]; Beta [C]
-    static constexpr int FLOATS = 3 * C * LD + C * C + C * DVS + D * DVS + D + C;
+    // LDS floats: Kt, Kh, Qt [C][LD]; NP [C][C]; U [C][DVS]; S [D][DVS]; Gam [D]; Beta [C];
+    // the chunk's pairwise flag
+    static constexpr int FLOATS = 3 * C * LD + C * C + C * DVS + D * DVS + D + C + 1;
     static constexpr size_t BYTES = sizeof(float) * FLOATS;
 };
 
@@ -52,6 +59,7 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     float* sS = sU + C * DVS;
     float* sGam = sS + D * DVS;
     float* sBeta = sGam + D;
+    int* sSlow = reinterpret_cast<int*>(sBeta + C);
 
     const int tid = threadIdx.x;
     const int slice = blockIdx.x % NS;
@@ -73,6 +81,7 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     for (int64_t c0 = tb; c0 < te; c0 += C) {
         const int L = (int)((te - c0) < C ? (te - c0) : C);
         __syncthreads();  // previous chunk done with every buffer
+        if (tid == 0) *sSlow = 0;
         // raw k -> sKt, g -> sKh, q -> sQt (zeros past the end)
         for (int e = tid; e < C * D; e += NT) {
             const int t = e / D, i = e % D;
@@ -97,19 +106,32 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                        : gate.mode == GATE_PROJ ? sigmoid_f(beta[(size_t)(c0 + t) * H + h])
                                                 : beta[(size_t)(c0 + t) * H + h];
         __syncthreads();
-        // cumulative decay per channel, scaled tiles
+        // cumulative log decay per channel into sKh (raw k stays in sKt, q in sQt)
         if (tid < D) {
             const int i = tid;
             float b = 0.f;
             for (int t = 0; t < C; ++t) {
-                const float kr = sKt[t * LD + i];
                 b += sKh[t * LD + i];
+                sKh[t * LD + i] = b;
+            }
+            sGam[i] = __expf(b);
+            if (b < -VEC_SLOW) *sSlow = 1;  // every writer stores the same value
+        }
+        __syncthreads();
+        // A chunk in which some channel decays below e^-VEC_SLOW takes the
+        // pairwise form: e^{-b} would overflow, so every factor is formed as
+        // e^{b_t - b_s}, e^{b_t} or e^{b_C - b_t} (all at most 1) where it is
+        // used, from raw k, q and b.  Otherwise, the scaled tiles.
+        const bool slow = *sSlow != 0;
+        if (!slow && tid < D) {
+            const int i = tid;
+            for (int t = 0; t < C; ++t) {
+                const float kr = sKt[t * LD + i], b = sKh[t * LD + i];
                 const float e = __expf(b), ei = __expf(-b);
                 sKt[t * LD + i] = kr * e;
                 sKh[t * LD + i] = kr * ei;
                 sQt[t * LD + i] *= e;
             }
-            sGam[i] = __expf(b);
         }
         __syncthreads();
         // N = strict_lower(diag(beta) Kt Kh^T)
@@ -117,7 +139,12 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
             const int t = e / C, s = e % C;
             float acc = 0.f;
             if (s < t) {
-                for (int i = 0; i < D; ++i) acc += sKt[t * LD + i] * sKh[s * LD + i];
+                if (!slow)
+                    for (int i = 0; i < D; ++i) acc += sKt[t * LD + i] * sKh[s * LD + i];
+                else
+                    for (int i = 0; i < D; ++i)
+                        acc += sKt[t * LD + i] * sKt[s * LD + i] *
+                               __expf(sKh[t * LD + i] - sKh[s * LD + i]);
                 acc *= sBeta[t];
             }
             sNP[e] = acc;
@@ -126,7 +153,11 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
         for (int e = tid; e < C * DVS; e += NT) {
             const int t = e / DVS, j = e % DVS;
             float acc = 0.f;
-            for (int i = 0; i < D; ++i) acc += sKt[t * LD + i] * sS[i * DVS + j];
+            if (!slow)
+                for (int i = 0; i < D; ++i) acc += sKt[t * LD + i] * sS[i * DVS + j];
+            else
+                for (int i = 0; i < D; ++i)
+                    acc += sKt[t * LD + i] * __expf(sKh[t * LD + i]) * sS[i * DVS + j];
             const float vv =
                 t < L ? In<Tin>::load1(v + (size_t)(c0 + t) * rowk + (size_t)h * D + j0 + j) : 0.f;
             sU[e] = sBeta[t] * (vv - acc);
@@ -146,8 +177,14 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
         for (int e = tid; e < C * C; e += NT) {
             const int t = e / C, s = e % C;
             float acc = 0.f;
-            if (s <= t)
-                for (int i = 0; i < D; ++i) acc += sQt[t * LD + i] * sKh[s * LD + i];
+            if (s <= t) {
+                if (!slow)
+                    for (int i = 0; i < D; ++i) acc += sQt[t * LD + i] * sKh[s * LD + i];
+                else
+                    for (int i = 0; i < D; ++i)
+                        acc += sQt[t * LD + i] * sKt[s * LD + i] *
+                               __expf(sKh[t * LD + i] - sKh[s * LD + i]);
+            }
             sNP[e] = acc;
         }
         __syncthreads();
@@ -156,20 +193,30 @@ prefill_vector_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
             const int t = e / DVS, j = e % DVS;
             if (t >= L) continue;
             float acc = 0.f;
-            for (int i = 0; i < D; ++i) acc += sQt[t * LD + i] * sS[i * DVS + j];
+            if (!slow)
+                for (int i = 0; i < D; ++i) acc += sQt[t * LD + i] * sS[i * DVS + j];
+            else
+                for (int i = 0; i < D; ++i)
+                    acc += sQt[t * LD + i] * __expf(sKh[t * LD + i]) * sS[i * DVS + j];
             for (int s = 0; s <= t; ++s) acc += sNP[t * C + s] * sU[s * DVS + j];
             const size_t oat = (size_t)(c0 + t) * rowk + (size_t)h * D + j0 + j;
             if (zg) acc *= sigmoid_f(In<Tin>::load1(zg + oat));  // output gate
             In<Tin>::store1(o + oat, acc);
         }
         __syncthreads();
-        // S <- Gam * S + (Kh * Gam)^T U (and the snapshot when one falls here)
+        // S <- Gam * S + (K e^{b_C - b})^T U (and the snapshot when one falls here)
         float* snp = snapshot_at(snap, n, h, H, D, c0 + L - tb, te - tb);
         for (int e = tid; e < D * DVS; e += NT) {
             const int i = e / DVS, j = e % DVS;
             const float gm = sGam[i];
             float acc = 0.f;
-            for (int t = 0; t < C; ++t) acc += (sKh[t * LD + i] * gm) * sU[t * DVS + j];
+            if (!slow) {
+                for (int t = 0; t < C; ++t) acc += (sKh[t * LD + i] * gm) * sU[t * DVS + j];
+            } else {
+                const float bC = sKh[(C - 1) * LD + i];
+                for (int t = 0; t < C; ++t)
+                    acc += sKt[t * LD + i] * __expf(bC - sKh[t * LD + i]) * sU[t * DVS + j];
+            }
             sS[e] = gm * sS[e] + acc;
             if (snp) snp[(size_t)i * D + j0 + j] = sS[e];
         }

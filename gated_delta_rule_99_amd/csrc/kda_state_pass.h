@@ -21,11 +21,13 @@
 // the chunk and chain wave c owns state rows [32c, 32c+32) of the slice.
 //   two-kernel path (chainw_*, outw_*; two barriers per chunk: R complete,
 //   next G complete):
-//     chain  Y = Kt G,  R = diag(beta)(V - Y),  S <- G + Wb^T R,  G' = Gam' S
+//     chain  Y = Kt G,  R = diag(beta)(V - Y),  S <- Gam S + Wb^T R,  G' = 2^R' S
 //     output Z = Qt G,  O = Z + PT R
 //   fused kernel (chain_*, out_*; three barriers: R, U, next G):
-//     chain  Y = Kt G,  R = diag(beta)(V - Y),  U = T R,  S <- G + Kb^T U
+//     chain  Y = Kt G,  R = diag(beta)(V - Y),  U = T R,  S <- Gam S + Kb^T U
 //     output Z = Qt G,  O = Z + P U
+// with G = 2^R S the chunk's state operand in bf16 (2^R = max(Gam, 2^-RLIM),
+// kda_chunk_ops.h) and Gam S kept in the fp32 accumulators.
 // V and O move with one 16-byte access per lane (16 rows x 32 columns per wave)
 // and are turned into the accumulator layout (lane (r, q4) holds rows 4q4 + e
 // of column r) through a staging tile that only the wave itself touches.
@@ -63,7 +65,7 @@ __device__ __forceinline__ void tile_export_kq(const L& sm, __amdgpu_buffer_rsrc
 
 // ---------------------------------------------------------------- state pass
 struct StateLds {
-    uint16_t Gt[DVS * LDK];  // bf16 (Gam * S)^T [j][i]
+    uint16_t Gt[DVS * LDK];  // bf16 (2^R * S)^T [j][i]
     uint16_t Rt[DVS * LDT];  // R^T [j][t]
     uint16_t Ut[DVS * LDT];  // U^T [j][t]
     uint16_t V[C * LDX];     // V slice [t][j]: each chain wave stages its own 16 rows
@@ -92,18 +94,32 @@ __device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t rt, int off) {
 // S[a][jb] holds S[32cw + 16a + 4q4 + e][16jb + r] of the slice.
 typedef f32x4 StateFrag[2][2];
 
-// S *= Gam (per row) and the bf16 copy of G = Gam * S into Gt.
+// The state operand of a chunk's products: G = 2^R * S, with 2^R = max(Gam,
+// 2^-RLIM) the chunk's reference (kda_chunk_ops.h): Gam itself wherever the
+// chunk decays by less than 2^-RLIM.
+__device__ __forceinline__ float4 ref_of(const float4& gam) {
+    constexpr float MIN_REF = 3.4694469519536142e-18f;  // 2^-RLIM
+    return make_float4(fmaxf(gam.x, MIN_REF), fmaxf(gam.y, MIN_REF), fmaxf(gam.z, MIN_REF),
+                       fmaxf(gam.w, MIN_REF));
+}
+__device__ __forceinline__ f32x4 scale4(f32x4 x, const float4& m) {
+    return f32x4{x[0] * m.x, x[1] * m.y, x[2] * m.z, x[3] * m.w};
+}
+
+// The chunk's state operand G = 2^R * S in bf16 into Gt, and S *= Gam (per
+// row): the accumulators then hold Gam * S, to which the chunk's update adds.
 __device__ __forceinline__ void chain_scale_store(StateLds& sm, StateFrag& S, const float4 (&gam)[2],
                                                   int cw, int lane) {
     const int r = lane & 15, q4 = lane >> 4;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a) {
+        const float4 er = ref_of(gam[a]);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            S[a][jb][0] *= gam[a].x; S[a][jb][1] *= gam[a].y;
-            S[a][jb][2] *= gam[a].z; S[a][jb][3] *= gam[a].w;
-            st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, S[a][jb]);
+            st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, scale4(S[a][jb], er));
+            S[a][jb] = scale4(S[a][jb], gam[a]);
         }
+    }
 }
 
 // Stage this wave's V rows (read back by the same wave only).
@@ -145,8 +161,8 @@ __device__ __forceinline__ void chain_u(StateLds& sm, const ChainFrags& cur, int
     }
 }
 
-// [C] S <- G + Kb^T U; the raw S to snp (a snapshot) when snp is set; with
-// more, the next G = Gam' S into Gt.
+// [C] S <- Gam S + Kb^T U; the raw S to snp (a snapshot) when snp is set; with
+// more, the next chunk's operand G' = 2^R' S into Gt and Gam' S into S.
 __device__ __forceinline__ void chain_s(StateLds& sm, const ChainFrags& cur,
                                         const float4 (&gam_next)[2], bool more, StateFrag& S,
                                         float* snp, int j0, int cw, int lane) {
@@ -164,9 +180,9 @@ __device__ __forceinline__ void chain_s(StateLds& sm, const ChainFrags& cur,
                     snp[(size_t)(32 * cw + 16 * a + 4 * q4 + e) * D + j0 + 16 * jb + r] = s[e];
             }
             if (more) {
-                s[0] *= gam_next[a].x; s[1] *= gam_next[a].y;
-                s[2] *= gam_next[a].z; s[3] *= gam_next[a].w;
-                st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, s);
+                st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4,
+                    scale4(s, ref_of(gam_next[a])));
+                s = scale4(s, gam_next[a]);
             }
             S[a][jb] = s;
         }
@@ -235,7 +251,7 @@ __device__ __forceinline__ u32x4 out_o(StateLds& sm, const OutFrags& cur, const 
 }
 
 // ------------------------------------------------ two-kernel path, T folded in
-// With U = T R:  S <- G + Kb^T U = G + Wb^T R  and  O = Z + P U = Z + PT R.  The
+// With U = T R:  S <- Gam S + Kb^T U = Gam S + Wb^T R  and  O = Z + P U = Z + PT R.  The
 // chain then needs no U, and a chunk takes two barriers.
 struct ChainFragsW {
     bf16x8 K[4], W[2][2];
@@ -281,8 +297,8 @@ __device__ __forceinline__ void out_load_z(OutFrags& f, __amdgpu_buffer_rsrc_t r
     f.z = make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-// [C] S <- G + Wb^T R (R from Rt); the raw S to snp (a snapshot) when snp is
-// set; with more, the next G = Gam' S into Gt.
+// [C] S <- Gam S + Wb^T R (R from Rt); the raw S to snp (a snapshot) when snp is
+// set; with more, the next chunk's operand G' = 2^R' S into Gt and Gam' S into S.
 __device__ __forceinline__ void chainw_s(StateLds& sm, const ChainFragsW& cur,
                                          const float4 (&gam_next)[2], bool more, StateFrag& S,
                                          float* snp, int j0, int cw, int lane) {
@@ -300,9 +316,9 @@ __device__ __forceinline__ void chainw_s(StateLds& sm, const ChainFragsW& cur,
                     snp[(size_t)(32 * cw + 16 * a + 4 * q4 + e) * D + j0 + 16 * jb + r] = s[e];
             }
             if (more) {
-                s[0] *= gam_next[a].x; s[1] *= gam_next[a].y;
-                s[2] *= gam_next[a].z; s[3] *= gam_next[a].w;
-                st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, s);
+                st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4,
+                    scale4(s, ref_of(gam_next[a])));
+                s = scale4(s, gam_next[a]);
             }
             S[a][jb] = s;
         }

@@ -134,13 +134,14 @@ kda_status kda_state_init(void* state, kda_dtype state_dtype, int64_t n_slots, i
  *   g               : [T, H, dk] fp32 (log decay; alpha = exp(g)), [T, H] fp32
  *                     with gate = KDA_GATE_HEAD, or the decay projection
  *                     [T, H, dk] in dtype with gate = KDA_GATE_PROJ.  Range:
- *                     the chunked form scales operands by the exponential of
- *                     the cumulative log decay inside a chunk, so the sum of g
- *                     over any chunk (per channel) must stay above about -85;
- *                     below about -88 the scale factors overflow fp32 and the
- *                     outputs are not finite.  Tested to -78.7 with chunk 64
- *                     (alpha ~ 0.3 per token); a smaller chunk widens the range.
- *                     kda_decode_step and kda_decode_tokens have no such limit.
+ *                     any finite g <= 0 (alpha in (0, 1]), however strong the
+ *                     decay over a chunk: the kernels reference the scaled
+ *                     operands to a clamped per-channel point and switch a
+ *                     chunk that decays below 2^-160 (about -111 in natural
+ *                     log; -80 in the fp32 vector kernel) on any channel to
+ *                     pairwise decay factors, so no factor overflows.  Tested
+ *                     down to about -540 per chunk.  g > 0 (alpha > 1) lies
+ *                     outside the method and may overflow.
  *   a_log           : [H] fp32 with KDA_GATE_PROJ, else NULL
  *   beta            : [T, H] fp32 (logits with KDA_GATE_PROJ)
  *   cu_seqlens_dev  : [n_seqs + 1] int32 on the device

@@ -63,7 +63,7 @@ def test_prefill_gate_proj(name):
     o_ref, S_ref = oracle_on(ref)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
     assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, tol,
-                  f" ")
+                  f"gate proj prefill {name}")
 
 
 def test_prefill_gate_proj_ling_layer():

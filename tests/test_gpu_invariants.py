@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import workloads
-from kda_testutil import (TOL_BF16, dev, gpu_or_skip, gpu_prefill, np64, oracle_on,
+from kda_testutil import (TOL_BF16, TOL_F32, dev, gpu_or_skip, gpu_prefill, np64, oracle_on,
                           assert_parity, rel_fro)
 
 pytestmark = pytest.mark.gpu
@@ -72,25 +72,75 @@ def test_split_and_fused_agree():
     assert e <= TOL_BF16 / 4
 
 
-@pytest.mark.parametrize("workspace", ["auto", None])
-def test_strong_decay_within_range(workspace):
-    """Decay strong enough (alpha ~ 0.3 per token and channel) that a 64-token
-    chunk's cumulative log decay reaches about -77 in some channels: the
-    matrix-core paths reference the decay to the chunk's end, so their factor
-    e^(b_t - b_C) then reaches ~e^77, near the fp32 limit (~e^88).  Both paths
-    still match the oracle."""
-    kda()
-    inp = workloads.recurrence_inputs([256, 100], H=2, d=128, dtype="bf16", g_mu=-0.84,
-                                      g_sigma=0.1, s0_std=0.3, seed=25)
+def chunk_log_decays(inp):
+    """Lowest cumulative log decay over any chunk (per channel and head)."""
     cu = [int(c) for c in inp.cu_seqlens]
-    lows = [float(inp.g[t:min(t + 64, cu[n + 1])].sum(0).min())
-            for n in range(len(cu) - 1) for t in range(cu[n], cu[n + 1], 64)]
-    assert -88.0 < min(lows) < -70.0, min(lows)
-    o, S = gpu_prefill(inp, workspace=workspace)
+    return min(float(inp.g[t:min(t + inp.chunk, cu[n + 1])].sum(0).min())
+               for n in range(len(cu) - 1) for t in range(cu[n], cu[n + 1], inp.chunk))
+
+
+# (label, d, dtype, chunk, workspace): the two-kernel and fused matrix-core
+# paths and the vector kernel (bf16 at chunk 32, fp32 at chunk 64)
+DECAY_PATHS = [("split", 128, "bf16", 64, "auto"), ("fused", 128, "bf16", 64, None),
+               ("vector_bf16", 128, "bf16", 32, None), ("vector_f32", 64, "f32", 64, None)]
+
+
+@pytest.mark.parametrize("label,d,dtype,chunk,ws", DECAY_PATHS, ids=[p[0] for p in DECAY_PATHS])
+@pytest.mark.parametrize("regime", ["moderate", "clamped", "extreme", "mixed"])
+def test_decay_range(label, d, dtype, chunk, ws, regime):
+    """Decays over the whole range, against the oracle by every measure:
+      moderate: alpha ~ 0.3 per token on every channel, a chunk of 64 decaying by
+                about e^-77 (the operands' reference sits at the chunk's end);
+      clamped:  alpha ~ e^-1.5, about e^-100 per chunk of 64 (the reference is
+                clamped, the factored products still hold);
+      extreme:  16 channels of every head at alpha ~ e^-4.7, about e^-300 per
+                chunk of 64, beside ordinary ones (the pairwise path);
+      mixed:    the extreme channels only on tokens [128, 320), so that chunks
+                on the pairwise path and factored ones alternate in a sequence
+                and hand the state to each other."""
+    kda()
+    lens = [520, 100, 0, 64]
+    base = dict(H=3, d=d, dtype=dtype, chunk=chunk, s0_std=0.3, seed=25 + d + chunk)
+    if regime == "moderate":
+        inp = workloads.recurrence_inputs(lens, g_mu=-0.84, g_sigma=0.1, **base)
+    elif regime == "clamped":
+        inp = workloads.recurrence_inputs(lens, g_mu=-1.2, g_sigma=0.1, **base)
+    else:
+        inp = workloads.recurrence_inputs(lens, g_mu=3.0, g_sigma=1.0, **base)
+        tokens = None if regime == "extreme" else (128, 320)
+        inp = workloads.with_strong_decay(inp, range(0, d, d // 16), tokens=tokens, seed=26)
+    low = chunk_log_decays(inp)
+    o, S = gpu_prefill(inp, workspace=ws)
     o_ref, S_ref = oracle_on(inp)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, tol,
+                  f"decay {regime} ({label}), lowest chunk log decay {low:.1f}")
+
+
+@pytest.mark.parametrize("ws", ["auto", None], ids=["split", "fused"])
+def test_decay_range_gate_proj(ws):
+    """The fused gate prologue with f ~ N(0, 1) and a rate exp(a_log) = 8 on every
+    head: log alpha = -8 softplus(f), about -6.5 per token on average, chunks of
+    64 decaying by e^-300 to e^-600 on every channel."""
+    m = kda()
+    import math
+    import oracle
+    lens, H, d = [300, 64, 130], 4, 128
+    inp = workloads.recurrence_inputs(lens, H=H, d=d, dtype="bf16", chunk=64, s0_std=0.3,
+                                      seed=27)
+    pr = workloads.gate_projections(inp.T, H, d, dtype="bf16", g_mu=0.0, g_sigma=1.0, seed=28)
+    a_log = torch.full((H,), math.log(8.0))
+    g, beta = oracle.gate_prologue(np64(pr.f), np64(a_log), np64(pr.b))
+    ref = workloads.RecurrenceInputs(inp.q, inp.k, inp.v, torch.from_numpy(g),
+                                     torch.from_numpy(beta), inp.cu_seqlens, inp.S0, "bf16", 64)
+    low = chunk_log_decays(ref)
+    o, S = m.kda_prefill_chunked(dev(inp.q), dev(inp.k), dev(inp.v), dev(pr.f), dev(pr.b),
+                                 cu_seqlens=dev(inp.cu_seqlens), cu_seqlens_host=inp.cu_seqlens,
+                                 initial_state=dev(inp.S0), workspace=ws, a_log=dev(a_log))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_on(ref)
     assert_parity(np64(o), o_ref, np64(S), S_ref, inp.cu_seqlens, TOL_BF16,
-                  f"strong decay ({'two-kernel' if workspace else 'fused'}), lowest chunk "
-                  f"log decay {min(lows):.1f}")
+                  f"gate prologue at rate 8, lowest chunk log decay {low:.1f}")
 
 
 def test_handoff_prefill_prefill():

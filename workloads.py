@@ -39,7 +39,7 @@ _BLOCK = 1 << 22
 
 # tensor ids: the order in which a workload's tensors are drawn
 TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "S0": 5, "conv_w": 6,
-       "x_q": 7, "x_k": 8, "x_v": 9, "f": 10, "a_log": 11, "b": 12, "z": 13}
+       "x_q": 7, "x_k": 8, "x_v": 9, "f": 10, "a_log": 11, "b": 12, "z": 13, "g_strong": 14}
 
 
 def _threads() -> int:
@@ -223,6 +223,22 @@ def gate_projections(T, H, d, dtype="bf16", g_mu=2.0, g_sigma=0.5, a_log_std=0.0
              else torch.zeros(H))
     b = normal((T, H), seed, TID["b"])
     return GateProjections(f, a_log, b)
+
+
+def with_strong_decay(inp: RecurrenceInputs, channels, tokens=None, g_mu=-4.7, g_sigma=0.3,
+                      seed=0) -> RecurrenceInputs:
+    """A copy of inp whose log decay on the given key channels (of every head)
+    is redrawn as log(sigmoid(N(g_mu, g_sigma))), on the given token range (all
+    tokens by default).  With the default recipe alpha ~ e^-4.7 per token, so a
+    64-token chunk decays by about e^-300 on those channels."""
+    g = inp.g.clone()
+    lo, hi = (0, inp.T) if tokens is None else tokens
+    ch = list(channels)
+    draw = torch.nn.functional.logsigmoid(
+        normal((hi - lo, inp.H, len(ch)), seed, TID["g_strong"], g_mu, g_sigma))
+    g[lo:hi, :, ch] = draw
+    return RecurrenceInputs(inp.q, inp.k, inp.v, g, inp.beta, inp.cu_seqlens, inp.S0, inp.dtype,
+                            inp.chunk)
 
 
 def output_gate_projection(T, H, dv, dtype="bf16", seed=0) -> torch.Tensor:
