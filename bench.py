@@ -139,7 +139,8 @@ def cpu_baseline_run(inp):
     oracle.recurrence(sl(q), sl(k), sl(v), sl(g), sl(beta), cu_seqlens=inp.cu_seqlens.numpy(),
                       precision="f32", n_threads=1)
     dt1 = (time.perf_counter() - t0) * inp.H / hs
-    return {"value": inp.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": inp.T / dt, "unit": "tokens/s", "cores": cores, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"whole prefill workload (T={inp.T}, H={inp.H}, d={inp.d}), fp32 "
                       f"sequential recurrence, OpenMP over heads; {dt:.2f} s wall",
             "seconds": round(dt, 3),
@@ -167,26 +168,43 @@ def cpu_decode_single_thread(inp, n_sample=32):
                       f"{inp.n_seqs // n_sample}"}
 
 
-def copy_bandwidth(dev, reps=10):
-    """A plain device copy of 1 GiB (torch's copy kernel), read plus written
-    bytes over the time: the bandwidth a streaming kernel reaches on this machine."""
+def copy_bandwidth(dev, reps=20):
+    """The library's streaming copy (kda_device_copy: 16-byte non-temporal loads
+    and stores, four pieces per lane in flight) of 1 GiB, read plus written bytes
+    over the time: the bandwidth a streaming kernel reaches on this device."""
     import torch
+
+    import gated_delta_rule_99_amd as kda
 
     n = 1 << 28
     a = torch.ones(n, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
-    for _ in range(2):
-        b.copy_(a)
+    for _ in range(3):
+        kda.kda_device_copy(b, a)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
-        b.copy_(a)
+        kda.kda_device_copy(b, a)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     del a, b
     return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def main():
@@ -223,12 +241,13 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     if args.only == "copy":
-        # plain copy of a known size: calibrates the profiler's byte counters
+        # the library's streaming copy of a known size: calibrates the
+        # profiler's byte counters (FETCH_SIZE and WRITE_SIZE per dispatch)
         n = 1 << 28  # 1 GiB of fp32
         a = torch.ones(n, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(max(1, args.steps)):
-            b.copy_(a)
+            kda.kda_device_copy(b, a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n * 4}))
         return
@@ -270,6 +289,11 @@ def main():
         alg_bytes, alg_flops = prefill_algorithmic(T, H, d, C, True, True)
         achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
         traffic = measured_traffic(PREFILL_KERNEL)
+        # MFMA share of peak on the algorithm's own flops, and the share that HBM
+        # allows at this arithmetic intensity (the attainable roofline)
+        mfma_frac = alg_flops / (kern_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS
+        attainable = min(1.0, (alg_flops / alg_bytes) * HBM_PEAK_GBS * 1e9 /
+                         (BF16_MFMA_PEAK_TFLOPS * 1e12))
         result.update({
             "value": T * args.steps / wall,
             "unit": "tokens/s",
@@ -285,9 +309,9 @@ def main():
                          "algorithmic_bytes": alg_bytes},
             "mfma": {"algorithmic_tflops": alg_flops / (kern_ms * 1e-3) / 1e12,
                      "peak": BF16_MFMA_PEAK_TFLOPS,
-                     "frac": alg_flops / (kern_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                     "attainable_frac": min(1.0, (alg_flops / alg_bytes) * HBM_PEAK_GBS * 1e9 /
-                                            (BF16_MFMA_PEAK_TFLOPS * 1e12)),
+                     "frac": mfma_frac,
+                     "attainable_frac": attainable,
+                     "attained_over_attainable": mfma_frac / attainable,
                      "rocprof_busy_frac": measured_mfma_busy(PREFILL_KERNEL),
                      "algorithmic_flops": alg_flops},
         })
@@ -376,7 +400,9 @@ def main():
                             "algorithmic_bytes": alg}}
         copy_gbs = copy_bandwidth(dev)
         dec["copy_kernel"] = {"achieved": copy_gbs, "unit": "GB/s",
-                              "what": "device copy of 1 GiB, read + written bytes per second"}
+                              "kernel": "copy16_kernel (kda_device_copy)",
+                              "what": "16-byte non-temporal device copy of 1 GiB, read + "
+                                      "written bytes per second"}
         dec["frac_of_copy"] = gbs / copy_gbs
         if not args.no_cpu_baseline and args.only is None:
             dec["cpu_single_thread"] = cpu_decode_single_thread(inp)

@@ -12,6 +12,7 @@ from .kda import (  # noqa: F401
     LIB_PATH,
     KdaError,
     kda_decode_step,
+    kda_device_copy,
     kda_decode_tokens,
     kda_prefill_chunked,
     kda_prefill_workspace_bytes,

@@ -503,4 +503,16 @@ kda_status kda_short_conv_decode(const void* x, const float* w, kda_dtype dtype,
                       "kda_short_conv_decode launch");
 }
 
+kda_status kda_device_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    const char* fn = "kda_device_copy";
+    g_detail[0] = 0;
+    if (bytes == 0) return KDA_OK;
+    if (!dst || !src) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: dst and src are required", fn);
+    if (!aligned16(dst) || !aligned16(src) || bytes % 16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: pointers and size must be 16-byte aligned", fn);
+    if (overlaps(dst, bytes, src, bytes))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: dst and src overlap", fn);
+    return hip_status(kda::launch_device_copy(dst, src, bytes, stream), "kda_device_copy launch");
+}
+
 }  // extern "C"

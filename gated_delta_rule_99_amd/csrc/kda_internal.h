@@ -182,6 +182,9 @@ hipError_t launch_short_conv_prefill(const void* x, const float* w, kda_dtype dt
                                      int l2_head_dim, float l2_eps, const void* tail_in,
                                      void* tail_out, void* y, hipStream_t stream);
 
+// bytes (a multiple of 16) from src to dst, both 16-byte aligned, not overlapping.
+hipError_t launch_device_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
 hipError_t launch_short_conv_decode(const void* x, const float* w, kda_dtype dtype,
                                     void* tail, int64_t n_slots, const int32_t* slot_idx, int B,
                                     int channels, int l2_head_dim, float l2_eps, void* y,

@@ -56,6 +56,7 @@ _SIGNATURES = {
                                       _vp, _vp, _vp]),
     "kda_short_conv_decode": (_i32, [_vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32, _i32, _f32,
                                      _vp, _vp]),
+    "kda_device_copy": (_i32, [_vp, _vp, ctypes.c_size_t, _vp]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -237,6 +238,19 @@ def kda_state_init(state: torch.Tensor, src: torch.Tensor | None = None, stream=
     _check(load().kda_state_init(_ptr(state), _state_code(state), n_slots, H, dk, dv, _ptr(src),
                                  _state_code(src) if src is not None else KDA_F32, handle))
     return state
+
+
+def kda_device_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> torch.Tensor:
+    """Copy src into dst (same number of bytes, contiguous, on one GPU) with the
+    library's 16-byte non-temporal streaming copy: the bandwidth reference of
+    the HBM-bound kernels."""
+    _need(dst.is_contiguous() and src.is_contiguous(), "dst and src must be contiguous")
+    nbytes = dst.numel() * dst.element_size()
+    _need(src.numel() * src.element_size() == nbytes, "dst and src must hold the same bytes")
+    _same_device(dst, src=src)
+    handle, _ = _stream(stream, dst.device)
+    _check(load().kda_device_copy(_ptr(dst), _ptr(src), nbytes, handle))
+    return dst
 
 
 def kda_prefill_workspace_bytes(n_seqs: int, H: int, dk: int, dv: int, chunk: int,

@@ -388,6 +388,21 @@ kda_status kda_short_conv_decode(const void* x, const float* w, kda_dtype dtype,
                                  int B, int channels, int l2_head_dim, float l2_eps, void* y,
                                  hipStream_t stream);
 
+/*
+ * kda_device_copy -- the streaming-bandwidth reference for the kernels above
+ * (not part of the recurrence): copies `bytes` from src to dst on the device
+ * with 16-byte non-temporal loads and stores, four independent pieces per lane
+ * in flight.  Its achieved rate is the practical ceiling that the HBM-bound
+ * kernels are compared with, and its byte counters calibrate profiler traffic
+ * readings.
+ *   dst, src : device buffers, 16-byte aligned, not overlapping.
+ *   bytes    : a multiple of 16; 0 does nothing.
+ * Errors: KDA_ERR_INVALID_ARGUMENT for a NULL pointer with bytes > 0, a
+ * misaligned pointer or size, or overlapping buffers; KDA_ERR_HIP if the
+ * launch fails.
+ */
+kda_status kda_device_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

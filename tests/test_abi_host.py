@@ -267,6 +267,18 @@ def test_conv_decode_rejects(lib):
         KDA_ERR_INVALID_ARGUMENT
 
 
+def test_device_copy_rejects(lib):
+    f = lib.kda_device_copy
+    assert f(A, Bp, 0, None) == 0  # nothing to copy: no HIP call
+    assert f(None, Bp, 64, None) == KDA_ERR_INVALID_ARGUMENT
+    assert f(A, None, 64, None) == KDA_ERR_INVALID_ARGUMENT
+    assert f(A + 8, Bp, 64, None) == KDA_ERR_INVALID_ARGUMENT
+    assert f(A, Bp, 72, None) == KDA_ERR_INVALID_ARGUMENT
+    assert "aligned" in lib.kda_last_error_detail().decode()
+    assert f(A, A + 32, 64, None) == KDA_ERR_INVALID_ARGUMENT
+    assert "overlap" in lib.kda_last_error_detail().decode()
+
+
 def test_python_binding_raises_on_error(lib):
     """The binding turns a non-OK status into KdaError with the library's detail
     (no fallback)."""
