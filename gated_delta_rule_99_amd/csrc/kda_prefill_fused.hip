@@ -104,8 +104,8 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         return rem < C ? (int)rem : C;
     };
     // this lane's 16-byte piece of a wave's 16 x 32 block of V or O
-    const int xrow = 16 * w4 + (lane >> 2), xcol = 8 * (lane & 3);
-    const int xoff = xrow * rowb + xcol * 2;
+    const VoPieces<DVS> vp(w4, lane);
+    const int xoff = vp.off(0, rowb);
     auto vo_rsrc = [&](const bf16_t* base, int c) {
         const int cc = (c >= 0 && c < nc) ? c : 0;
         return window(base + (size_t)(tb + (int64_t)cc * C) * row + hoff + j0, chunk_len(c) * rowb);
@@ -200,7 +200,7 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         };
         uint4 vnext = load_v(1);
         ChainFrags cur;  // chunk s's fragments, copied from the producer's LDS
-        cur.v = load_v(0);
+        cur.v[0] = load_v(0);
         auto gam_lds = [&](float4 (&gm)[2]) {
 #pragma unroll
             for (int a = 0; a < 2; ++a)
@@ -237,9 +237,9 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int s = 0; s < nc; ++s) {
             const bool next = s + 1 < nc;
             // ---- [A] Y = Kt G; R = diag(beta)(V - Y)
-            chain_stage_v(sm.st, cur.v, xrow, xcol);
+            chain_stage_v(sm.st, cur.v, vp);
             chain_yr(sm.st, cur, cw, lane);
-            cur.v = vnext;
+            cur.v[0] = vnext;
             vnext = load_v(s + 2);
             __syncthreads();  // B1
             const bool slow = next && slow_flag();
@@ -302,7 +302,7 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         __syncthreads();  // P4
         for (int s = 0; s < nc; ++s) {
             const bool next = s + 1 < nc;
-            const uint4 zc = znext;
+            const uint4 zc[1] = {znext};
             znext = load_z(s + 1);
             // ---- [A] Z = Qt G
             f32x4 Zc[2];
@@ -311,8 +311,9 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             pair_syncs(next && slow_flag());
             __syncthreads();  // B2
             // ---- [C] O = Z + P U (gated), staged through this wave's rows, one 16-byte store
-            __builtin_amdgcn_raw_buffer_store_b128(
-                out_o<OG>(sm.st, cur, Zc, zc, cw, lane, xrow, xcol), vo_rsrc(o, s), xoff, 0, 0);
+            u32x4 out[1];
+            out_o<OG>(sm.st, cur, Zc, zc, cw, lane, vp, out);
+            __builtin_amdgcn_raw_buffer_store_b128(out[0], vo_rsrc(o, s), xoff, 0, 0);
             __syncthreads();  // B3
             // ---- [D] fragments of chunk s + 1
             if (next) copy_in();

@@ -21,7 +21,7 @@
 #include <algorithm>
 #include <vector>
 
-#include "kda_state_pass.h"
+#include "kda_prep_tile.h"
 #include "kda_window_plan.h"
 
 namespace kda {
@@ -39,53 +39,11 @@ constexpr size_t BATCH_TILES = (size_t)4 << 30;  // tiles of the preferred batch
 using namespace sp;
 
 // ---------------------------------------------------------------- prep
-// LDS of prep_kernel: the decay stage's Kt, Qt and Kb rows and beta.  Once the
-// N and P blocks are in registers, T, Tt and P take the place of Kt and Qt
-// (TpLds), so that a workgroup needs 52.5 KB and three fit a CU's 160 KB
-// (with T, Tt and P beside the rows, 80 KB: two).  After the merge, T^T
-// replaces Tt, the Kb^T rows (kept in registers since the decay stage) go after
-// P, and Wb^T and PT are formed over the Kb^T rows and T.
-struct PrepLds {
-    uint16_t Kt[C * LDK];  // [t][i]
-    uint16_t Qt[C * LDK];  // [t][i]
-    uint16_t Kb[C * LDK];  // [t][i]
-    float beta[C];
-    int slow[4];           // per wave: some channel of it decays below 2^-SLOW
-};
-struct TpLds {
-    uint16_t T[C * LDT];   // T [t][s], then PT [t][u]
-    uint16_t Tt[C * LDT];  // T^T [s][t] on the diagonal blocks, N [t][s] below them;
-                           // after the merge, all of T^T [u][s] (zero for s < u)
-    uint16_t P[C * LDT];   // P [t][s]
-    uint16_t Kbt[D * LDT]; // Kb^T [i][t], then Wb^T [i][u]
-};
-static_assert(sizeof(TpLds) <= sizeof(PrepLds), "the folded operands fit the stage rows");
-static_assert(sizeof(PairLds) <= 3 * C * LDK * 2, "the pairwise path's rows fit the stage rows");
-
-// The decay stage's sinks in prep_kernel: Gam to the tile, the Kb^T pieces of
-// channels ch0 .. ch0 + 3 (ch0 a multiple of 4) into registers.
-struct PrepSinks {
-    __amdgpu_buffer_rsrc_t rt;
-    u32x4* kbt;
-    __device__ __forceinline__ void operator()(int ch0, const float (&gam)[4]) const {
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4{__float_as_uint(gam[0]), __float_as_uint(gam[1]), __float_as_uint(gam[2]),
-                  __float_as_uint(gam[3])},
-            rt, OFF_GAM + 4 * ch0, 0, 0);
-    }
-    __device__ __forceinline__ void operator()(int i, int tg, u32x4 piece) const {
-        kbt[i & 3] = piece;
-    }
-};
-
 // grid (active sequences * H, chunks in the window): one workgroup of 4 waves
 // per (sequence rank, head, window chunk) runs the operand stages and exports
-// the tile (layout in kda_state_pass.h).  order[rank] is the sequence
-// (order NULL: rank = sequence).  GM: the decay inputs' GateMode (per channel,
-// per head, or the projection).  Wave p forms P's blocks 2, 2, 3, 3 (p = 0..3)
-// of the ten in row order beside its N blocks, while Kt and Qt are still in
-// LDS; after the merge, rows [32p, 32p + 32) of Wb^T = Kb^T T and row block p
-// of PT = P T.
+// the tile (prep_tile, kda_prep_tile.h).  order[rank] is the sequence (order
+// NULL: rank = sequence).  GM: the decay inputs' GateMode (per channel, per
+// head, or the projection).
 template <int GM>
 __global__ void __launch_bounds__(256, 3)
 prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
@@ -93,7 +51,7 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
             const int32_t* __restrict__ cu, const int32_t* __restrict__ order, int64_t T, int H,
             int w0, int win, uint8_t* __restrict__ ws_tiles) {
     __shared__ __attribute__((aligned(16))) PrepLds sm;
-    TpLds& tp = *reinterpret_cast<TpLds*>(sm.Kt);
+    __shared__ int slow_flags[4];
     const int slot = blockIdx.x / H, h = blockIdx.x - slot * H, cl = blockIdx.y;
     const int n = order ? order[slot] : slot;
     int64_t tb, te;
@@ -101,122 +59,10 @@ prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, Gate g,
     seq_chunks(cu, n, T, tb, te, nc);
     const int c = w0 + cl;
     if (c >= nc) return;
-    const int tid = threadIdx.x, p = tid >> 6, lane = tid & 63;
-    const int r = lane & 15, q4 = lane >> 4;
     const int64_t c0 = tb + (int64_t)c * C;
     const int L = (te - c0) < C ? (int)(te - c0) : C;
     const auto rt = window(ws_tiles + ((size_t)(slot * win + cl) * H + h) * TILE, TILE);
-
-    ChunkIn in;
-    load_chunk<GM>(in, q, k, g, beta, c0, L, H, h, p, lane);
-    if (p == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(chunk_beta<GM>(in, lane)), rt,
-                                              OFF_BETA + 4 * lane, 0, 0);
-    u32x4 kbt[4];  // Kb^T pieces: channel ch0 + e, tokens [8tg, 8tg + 8)
-    const PrepSinks sinks{rt, kbt};
-    const bool wave_slow = decay_stage<GM>(sm, in, p, lane, sinks, sinks);
-    if (lane == 0) sm.slow[p] = wave_slow;
-    __syncthreads();
-    const bool slow = sm.slow[0] | sm.slow[1] | sm.slow[2] | sm.slow[3];  // uniform
-    tile_export_kq(sm, rt, p, lane);
-    const int pn = p_count(p), pk0 = p_first(p);
-    NRegs nr;
-    f32x4 pb[3];
-    if (!slow) {
-        n_regs(sm, p, lane, nr);
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            if (j >= pn) break;
-            int rb, cb;
-            lower_block(pk0 + j, rb, cb);
-            pb[j] = p_tile(sm, rb, cb, lane);
-        }
-    } else {
-        // some channel decays too strongly for the factored products: the
-        // pairwise path over the reloaded inputs (the stage rows are reused)
-        ChunkIn in2;
-        load_chunk<GM>(in2, q, k, g, beta, c0, L, H, h, p, lane);
-        NRaw nw;
-        slow_products<GM>(*reinterpret_cast<PairLds*>(sm.Kt), in2, p, lane, nw, pb,
-                          [] { __syncthreads(); });
-        n_finish(sm.beta, p, lane, nw, nr);
-    }
-    __syncthreads();  // the stage rows are read in full: T, Tt, P and Kb^T take their place
-    n_store(tp, p, lane, nr);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        if (j >= pn) break;
-        int rb, cb;
-        lower_block(pk0 + j, rb, cb);
-        p_store(tp, rb, cb, lane, pb[j]);
-    }
-    if (p == 0 || p == 2)  // P's upper blocks that PT's k-steps read: (0,1), (2,3)
-        st4(tp.P + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
-    {
-        const int cg = lane & 7, tg = lane >> 3, ch0 = 32 * p + 4 * cg;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<u32x4*>(tp.Kbt + (ch0 + e) * LDT + 8 * tg) = kbt[e];
-    }
-    __syncthreads();
-    if (p == 0) merge_t<true>(tp, lane);  // T's off-diagonal blocks; all of T^T in Tt
-    __syncthreads();
-    // Wb^T rows [32p, 32p + 32): Wb^T[i][u] = sum_{s >= u} Kb^T[i][s] T[s][u]
-    // (computed transposed, so that a lane's 4 results lie along a row)
-    f32x4 wacc[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
-            f32x4 acc = Z4;
-#pragma unroll
-            for (int kk = (ub >= 2 ? 1 : 0); kk < 2; ++kk)
-                acc = mma32(ld8(tp.Tt + (16 * ub + r) * LDT + 32 * kk + 8 * q4),
-                            ld8(tp.Kbt + (32 * p + 16 * a + r) * LDT + 32 * kk + 8 * q4), acc);
-            wacc[a][ub] = acc;
-        }
-    // PT row block p: PT[t][u] = sum_{u <= s <= t} P[t][s] T[s][u]; the
-    // exported blocks, (0,1) and (2,3) coming out zero
-    const int nk = p >= 2 ? 2 : 1, nub = p >= 2 ? 4 : 2;
-#pragma unroll
-    for (int ub = 0; ub < 4; ++ub) {
-        if (ub >= nub) break;
-        f32x4 acc = Z4;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (kk >= nk) break;
-            acc = mma32(ld8(tp.Tt + (16 * ub + r) * LDT + 32 * kk + 8 * q4),
-                        ld8(tp.P + (16 * p + r) * LDT + 32 * kk + 8 * q4), acc);
-        }
-        st4(tp.T + (16 * p + r) * LDT + 16 * ub + 4 * q4, acc);  // T is no longer read
-    }
-    // Wb^T over this wave's own Kb^T rows: every store needs an MFMA result
-    // that has consumed the loads of the columns it overwrites (those of ub >= 2
-    // write only columns that the loads they wait for cover), and LDS accesses
-    // of one wave complete in order
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int ub = 0; ub < 4; ++ub)
-            st4(tp.Kbt + (32 * p + 16 * a + r) * LDT + 16 * ub + 4 * q4, wacc[a][ub]);
-    // the exports read what other lanes of this wave wrote
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // exports: Wb^T fragments [a][kk] of rows 32p + 16a, PT fragments of row block p
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                as_u4(ld8(tp.Kbt + (32 * p + 16 * a + r) * LDT + 32 * kk + 8 * q4)), rt,
-                OFF_WBT + ((p * 4 + a * 2 + kk) * 64 + lane) * 16, 0, 0);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        if (kk >= nk) break;
-        __builtin_amdgcn_raw_buffer_store_b128(
-            as_u4(ld8(tp.T + (16 * p + r) * LDT + 32 * kk + 8 * q4)), rt,
-            OFF_PT + ((p * 2 + kk) * 64 + lane) * 16, 0, 0);
-    }
+    prep_tile<GM, 4>(sm, slow_flags, threadIdx.x >> 6, q, k, g, beta, c0, L, H, h, rt);
 }
 
 // ---------------------------------------------------------------- state pass
@@ -296,12 +142,8 @@ state_kernel(const bf16_t* __restrict__ v, const bf16_t* __restrict__ zg,
         return window(ws_tiles + ((size_t)(slot * win + (cc - w0)) * H + h) * TILE,
                       c < c_end ? TILE : 0);
     };
-    // this lane's (row, column) of the chunk in the accumulator layout, as a
-    // byte offset from the slice's first element of the chunk's first row
-    // this lane's 16-byte piece of the wave's 16 x 32 block of V or O:
-    // row 16c + (lane >> 2), columns 8 (lane & 3) .. + 8
-    const int xrow = 16 * cw + (lane >> 2), xcol = 8 * (lane & 3);
-    const int xoff = xrow * rowb + xcol * 2;
+    // this lane's 16-byte piece of the wave's 16 x 32 block of V or O
+    const VoPieces<DVS> vp(cw, lane);
     auto vo_rsrc = [&](const bf16_t* base, int c) {
         const int cc = (c >= c_beg && c < c_end) ? c : c_beg;
         return window(base + (size_t)(tb + (int64_t)cc * C) * row + hoff + j0, chunk_len(c) * rowb);
@@ -319,7 +161,7 @@ state_kernel(const bf16_t* __restrict__ v, const bf16_t* __restrict__ zg,
                     S[a][jb][e] = s_in ? s_in[sidx + (size_t)i * D + j0 + j] : 0.f;
                 }
         auto load_a = [&](int c, ChainFragsW& f) {
-            chainw_load_a(f, tile_rsrc(c), vo_rsrc(v, c), xoff, cw, lane);
+            chainw_load_a(f, tile_rsrc(c), vo_rsrc(v, c), vp, rowb, cw, lane);
         };
         auto load_b = [&](int c, ChainFragsW& f) { chainw_load_b(f, tile_rsrc(c), cw, lane); };
         ChainFragsW F0, F1, F2;
@@ -331,7 +173,7 @@ state_kernel(const bf16_t* __restrict__ v, const bf16_t* __restrict__ zg,
         __syncthreads();
         auto step = [&](int c, const ChainFragsW& cur, const ChainFragsW& nxt,
                         ChainFragsW& later) {
-            chain_stage_v(sm, cur.v, xrow, xcol);
+            chain_stage_v(sm, cur.v, vp);
             load_a(c + 2, later);
             chain_yr(sm, cur, cw, lane);
             __syncthreads();
@@ -364,7 +206,7 @@ state_kernel(const bf16_t* __restrict__ v, const bf16_t* __restrict__ zg,
         auto load_a = [&](int c, OutFrags& f) { outw_load_a(f, tile_rsrc(c), cw, lane); };
         auto load_b = [&](int c, OutFrags& f) {
             outw_load_b(f, tile_rsrc(c), cw, lane);
-            if constexpr (OG) out_load_z(f, vo_rsrc(zg, c), xoff);
+            if constexpr (OG) out_load_z(f, vo_rsrc(zg, c), vp, rowb);
         };
         OutFrags F0, F1, F2;
         load_a(c_beg, F0);
@@ -376,8 +218,9 @@ state_kernel(const bf16_t* __restrict__ v, const bf16_t* __restrict__ zg,
             f32x4 Zc[2];
             out_z(sm, cur, Zc, lane);
             __syncthreads();
-            __builtin_amdgcn_raw_buffer_store_b128(
-                outw_o<OG>(sm, cur, Zc, cur.z, cw, lane, xrow, xcol), vo_rsrc(o, c), xoff, 0, 0);
+            u32x4 out[1];
+            outw_o<OG>(sm, cur, Zc, cw, lane, vp, out);
+            __builtin_amdgcn_raw_buffer_store_b128(out[0], vo_rsrc(o, c), vp.off(0, rowb), 0, 0);
             load_a(c + 2, later);
             load_b(c + 2, later);
             __syncthreads();

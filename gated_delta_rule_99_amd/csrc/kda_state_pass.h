@@ -13,7 +13,8 @@
 //   49152  PT fragments    [c 0..3][kk 0..1][lane][16 B] (zero fragments skipped)
 //   57344  beta[64] fp32, 57600 Gam[128] fp32
 //
-// State pass of one (sequence, head, 32-column slice of the state), 8 waves
+// State pass of one (sequence, head, DV-column slice of the state; DV = 32:
+// four slices per head), 8 waves
 // (recurrence from page "Ling-3.1-flash: a 560B hybrid-attention MoE, counted
 // from its safetensors headers", section "How KDA and MLA split the work"):
 // waves 0-3 carry the chain that the next chunk depends on, waves 4-7 produce
@@ -28,9 +29,9 @@
 //     output Z = Qt G,  O = Z + P U
 // with G = 2^R S the chunk's state operand in bf16 (2^R = max(Gam, 2^-RLIM),
 // kda_chunk_ops.h) and Gam S kept in the fp32 accumulators.
-// V and O move with one 16-byte access per lane (16 rows x 32 columns per wave)
-// and are turned into the accumulator layout (lane (r, q4) holds rows 4q4 + e
-// of column r) through a staging tile that only the wave itself touches.
+// V and O move with DV / 32 16-byte accesses per lane (16 rows x DV columns per
+// wave) and are turned into the accumulator layout (lane (r, q4) holds rows
+// 4q4 + e of column r) through a staging tile that only the wave itself touches.
 #pragma once
 
 #include "kda_chunk_ops.h"
@@ -43,7 +44,25 @@ constexpr int TILE = 58112;
 constexpr int OFF_KT = 0, OFF_QT = 16384, OFF_WBT = 32768, OFF_PT = 49152, OFF_BETA = 57344,
               OFF_GAM = 57600;
 static_assert(TILE % 256 == 0, "tiles stay 256-byte aligned");
-constexpr int LDX = 40;  // row stride (bf16) of the V and O staging tiles
+
+// This lane's 16-byte pieces of its wave's 16 x DV block of V or O (16 rows of
+// the chunk, DV columns of the slice): piece u is row 16 cw + pi / (DV / 8),
+// columns 8 (pi % (DV / 8)) .. + 8, with pi = lane + 64 u.
+template <int DV>
+struct VoPieces {
+    static constexpr int N = DV / 32;
+    int row[N], col[N];
+    __device__ __forceinline__ VoPieces(int cw, int lane) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int pi = lane + 64 * u;
+            row[u] = 16 * cw + pi / (DV / 8);
+            col[u] = 8 * (pi % (DV / 8));
+        }
+    }
+    // byte offset of piece u from the slice's first element of the chunk's first row
+    __device__ __forceinline__ int off(int u, int rowb) const { return row[u] * rowb + col[u] * 2; }
+};
 
 // ---------------------------------------------------------------- tile export
 // Kt and Qt fragments out of LDS (wave p exports row block p); after the decay
@@ -64,35 +83,33 @@ __device__ __forceinline__ void tile_export_kq(const L& sm, __amdgpu_buffer_rsrc
 }
 
 // ---------------------------------------------------------------- state pass
-struct StateLds {
-    uint16_t Gt[DVS * LDK];  // bf16 (2^R * S)^T [j][i]
-    uint16_t Rt[DVS * LDT];  // R^T [j][t]
-    uint16_t Ut[DVS * LDT];  // U^T [j][t]
-    uint16_t V[C * LDX];     // V slice [t][j]: each chain wave stages its own 16 rows
-    uint16_t O[C * LDX];     // O slice [t][j]: each output wave stages its own 16 rows
+template <int DV>
+struct StateLdsT {
+    static constexpr int LDX = DV + 8;  // row stride (bf16) of the V and O staging tiles
+    uint16_t Gt[DV * LDK];  // bf16 (2^R * S)^T [j][i]
+    uint16_t Rt[DV * LDT];  // R^T [j][t]
+    uint16_t Ut[DV * LDT];  // U^T [j][t] (fused path)
+    uint16_t V[C * LDX];    // V slice [t][j]: each chain wave stages its own 16 rows
+    uint16_t O[C * LDX];    // O slice [t][j]: each output wave stages its own 16 rows
 };
+using StateLds = StateLdsT<DVS>;
 
 struct ChainFrags {
     bf16x8 K[4], Kb[2][2], T[2];
     float4 bet, gam[2];
-    uint4 v;  // V[16c + (lane >> 2)][8 (lane & 3) + 0..7]
+    uint4 v[1];  // this lane's piece of V (VoPieces<32>)
 };
-struct OutFrags {
+template <int DV = DVS>
+struct OutFragsT {
     bf16x8 Q[4], P[2];
-    uint4 z;  // output gate: this lane's 16-byte piece of the gate projection
+    uint4 z[DV / 32];  // output gate: this lane's pieces of the gate projection
 };
-
-__device__ __forceinline__ bf16x8 ld_frag(__amdgpu_buffer_rsrc_t rt, int off) {
-    return as_bf8(__builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
-}
-__device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t rt, int off) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0);
-    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
-                       __uint_as_float(x[3]));
-}
+using OutFrags = OutFragsT<DVS>;
 
 // S[a][jb] holds S[32cw + 16a + 4q4 + e][16jb + r] of the slice.
-typedef f32x4 StateFrag[2][2];
+template <int DV>
+using StateFragT = f32x4[2][DV / 16];
+typedef StateFragT<DVS> StateFrag;
 
 // The state operand of a chunk's products: G = 2^R * S, with 2^R = max(Gam,
 // 2^-RLIM) the chunk's reference (kda_chunk_ops.h): Gam itself wherever the
@@ -108,14 +125,15 @@ __device__ __forceinline__ f32x4 scale4(f32x4 x, const float4& m) {
 
 // The chunk's state operand G = 2^R * S in bf16 into Gt, and S *= Gam (per
 // row): the accumulators then hold Gam * S, to which the chunk's update adds.
-__device__ __forceinline__ void chain_scale_store(StateLds& sm, StateFrag& S, const float4 (&gam)[2],
-                                                  int cw, int lane) {
+template <int DV>
+__device__ __forceinline__ void chain_scale_store(StateLdsT<DV>& sm, StateFragT<DV>& S,
+                                                  const float4 (&gam)[2], int cw, int lane) {
     const int r = lane & 15, q4 = lane >> 4;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
         const float4 er = ref_of(gam[a]);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        for (int jb = 0; jb < DV / 16; ++jb) {
             st4(sm.Gt + (16 * jb + r) * LDK + 32 * cw + 16 * a + 4 * q4, scale4(S[a][jb], er));
             S[a][jb] = scale4(S[a][jb], gam[a]);
         }
@@ -123,24 +141,31 @@ __device__ __forceinline__ void chain_scale_store(StateLds& sm, StateFrag& S, co
 }
 
 // Stage this wave's V rows (read back by the same wave only).
-__device__ __forceinline__ void chain_stage_v(StateLds& sm, const uint4& v, int xrow, int xcol) {
-    *reinterpret_cast<uint4*>(sm.V + xrow * LDX + xcol) = v;
+template <int DV>
+__device__ __forceinline__ void chain_stage_v(StateLdsT<DV>& sm, const uint4 (&v)[DV / 32],
+                                              const VoPieces<DV>& vp) {
+#pragma unroll
+    for (int u = 0; u < DV / 32; ++u)
+        *reinterpret_cast<uint4*>(sm.V + vp.row[u] * StateLdsT<DV>::LDX + vp.col[u]) = v[u];
     __builtin_amdgcn_wave_barrier();
 }
 
 // [A] Y = Kt G; R = diag(beta)(V - Y) into Rt.
-template <typename Frags>
-__device__ __forceinline__ void chain_yr(StateLds& sm, const Frags& cur, int cw, int lane) {
+template <int DV, typename Frags>
+__device__ __forceinline__ void chain_yr(StateLdsT<DV>& sm, const Frags& cur, int cw, int lane) {
+    constexpr int NJB = DV / 16, LDX = StateLdsT<DV>::LDX;
     const int r = lane & 15, q4 = lane >> 4;
-    f32x4 Y[2] = {Z4, Z4};
+    f32x4 Y[NJB];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        Y[0] = mma32(cur.K[kk], ld8(sm.Gt + r * LDK + 32 * kk + 8 * q4), Y[0]);
-        Y[1] = mma32(cur.K[kk], ld8(sm.Gt + (16 + r) * LDK + 32 * kk + 8 * q4), Y[1]);
-    }
+    for (int jb = 0; jb < NJB; ++jb) Y[jb] = Z4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+            Y[jb] = mma32(cur.K[kk], ld8(sm.Gt + (16 * jb + r) * LDK + 32 * kk + 8 * q4), Y[jb]);
     const float bb[4] = {cur.bet.x, cur.bet.y, cur.bet.z, cur.bet.w};
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int jb = 0; jb < NJB; ++jb) {
         f32x4 rv;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -190,34 +215,40 @@ __device__ __forceinline__ void chain_s(StateLds& sm, const ChainFrags& cur,
 }
 
 // [A] Z = Qt G.
-__device__ __forceinline__ void out_z(StateLds& sm, const OutFrags& cur, f32x4 (&Zc)[2], int lane) {
+template <int DV>
+__device__ __forceinline__ void out_z(StateLdsT<DV>& sm, const OutFragsT<DV>& cur,
+                                      f32x4 (&Zc)[DV / 16], int lane) {
     const int r = lane & 15, q4 = lane >> 4;
-    Zc[0] = Z4;
-    Zc[1] = Z4;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        Zc[0] = mma32(cur.Q[kk], ld8(sm.Gt + r * LDK + 32 * kk + 8 * q4), Zc[0]);
-        Zc[1] = mma32(cur.Q[kk], ld8(sm.Gt + (16 + r) * LDK + 32 * kk + 8 * q4), Zc[1]);
-    }
+    for (int jb = 0; jb < DV / 16; ++jb) Zc[jb] = Z4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int jb = 0; jb < DV / 16; ++jb)
+            Zc[jb] = mma32(cur.Q[kk], ld8(sm.Gt + (16 * jb + r) * LDK + 32 * kk + 8 * q4), Zc[jb]);
 }
 
 // This wave's 16 output rows, fp32 in the accumulator layout (acc[jb][e]: row
-// 16cw + 4q4 + e, column 16jb + r), to this lane's 16-byte piece of them (row
-// xrow, columns xcol ..) in bf16, through the wave's rows of the staging tile.
-// GATED: each output is first multiplied by sigmoid(z), the output gate, with z
-// this lane's 16-byte piece of the gate projection (same rows and columns): z
-// takes the same way through the staging rows into the accumulator layout, so
-// that the gated value is rounded to bf16 once.  Only the wave itself touches
-// these rows, and a wave's LDS accesses complete in order.
-template <bool GATED>
-__device__ __forceinline__ u32x4 stage_out(StateLds& sm, f32x4 (&acc)[2], const uint4& z, int cw,
-                                           int lane, int xrow, int xcol) {
+// 16cw + 4q4 + e, column 16jb + r), to this lane's 16-byte pieces of them
+// (VoPieces) in bf16, through the wave's rows of the staging tile.  GATED: each
+// output is first multiplied by sigmoid(z), the output gate, with z this lane's
+// pieces of the gate projection (same rows and columns): z takes the same way
+// through the staging rows into the accumulator layout, so that the gated
+// value is rounded to bf16 once.  Only the wave itself touches these rows, and
+// a wave's LDS accesses complete in order.
+template <bool GATED, int DV>
+__device__ __forceinline__ void stage_out(StateLdsT<DV>& sm, f32x4 (&acc)[DV / 16],
+                                          const uint4 (&z)[DV / 32], int cw, int lane,
+                                          const VoPieces<DV>& vp, u32x4 (&out)[DV / 32]) {
+    constexpr int NJB = DV / 16, LDX = StateLdsT<DV>::LDX;
     const int r = lane & 15, q4 = lane >> 4;
     if constexpr (GATED) {
-        *reinterpret_cast<uint4*>(sm.O + xrow * LDX + xcol) = z;
+#pragma unroll
+        for (int u = 0; u < DV / 32; ++u)
+            *reinterpret_cast<uint4*>(sm.O + vp.row[u] * LDX + vp.col[u]) = z[u];
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+        for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 acc[jb][e] *= sigmoid_f(
@@ -225,21 +256,24 @@ __device__ __forceinline__ u32x4 stage_out(StateLds& sm, f32x4 (&acc)[2], const 
         __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[jb][e]);
     __builtin_amdgcn_wave_barrier();
-    const uint4 x = *reinterpret_cast<const uint4*>(sm.O + xrow * LDX + xcol);
-    return u32x4{x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int u = 0; u < DV / 32; ++u) {
+        const uint4 x = *reinterpret_cast<const uint4*>(sm.O + vp.row[u] * LDX + vp.col[u]);
+        out[u] = u32x4{x.x, x.y, x.z, x.w};
+    }
 }
 
 // [C] O = Z + P U (gated by sigmoid(z) with GATED), staged through this wave's
-// rows; returns this lane's 16-byte piece (row xrow, columns xcol ..) for one
-// store.
+// rows; this lane's 16-byte piece (VoPieces<32>) for one store into out.
 template <bool GATED>
-__device__ __forceinline__ u32x4 out_o(StateLds& sm, const OutFrags& cur, const f32x4 (&Zc)[2],
-                                       const uint4& z, int cw, int lane, int xrow, int xcol) {
+__device__ __forceinline__ void out_o(StateLds& sm, const OutFrags& cur, const f32x4 (&Zc)[2],
+                                      const uint4 (&z)[1], int cw, int lane,
+                                      const VoPieces<DVS>& vp, u32x4 (&out)[1]) {
     const int r = lane & 15, q4 = lane >> 4;
     f32x4 acc[2];
 #pragma unroll
@@ -247,64 +281,98 @@ __device__ __forceinline__ u32x4 out_o(StateLds& sm, const OutFrags& cur, const 
         acc[jb] = mma32(cur.P[0], ld8(sm.Ut + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
         if (cw >= 2) acc[jb] = mma32(cur.P[1], ld8(sm.Ut + (16 * jb + r) * LDT + 32 + 8 * q4), acc[jb]);
     }
-    return stage_out<GATED>(sm, acc, z, cw, lane, xrow, xcol);
+    stage_out<GATED, DVS>(sm, acc, z, cw, lane, vp, out);
 }
 
 // ------------------------------------------------ two-kernel path, T folded in
 // With U = T R:  S <- Gam S + Kb^T U = Gam S + Wb^T R  and  O = Z + P U = Z + PT R.  The
 // chain then needs no U, and a chunk takes two barriers.
-struct ChainFragsW {
+template <int DV = DVS>
+struct ChainFragsWT {
     bf16x8 K[4], W[2][2];
     float4 bet, gam[2];
-    uint4 v;  // V[16c + (lane >> 2)][8 (lane & 3) + 0..7]
+    uint4 v[DV / 32];  // this lane's pieces of V (VoPieces<DV>)
 };
+using ChainFragsW = ChainFragsWT<DVS>;
 
-// Kt, beta, Gam and this lane's piece of V (first half); Wb^T (second half).
-__device__ __forceinline__ void chainw_load_a(ChainFragsW& f, __amdgpu_buffer_rsrc_t rt,
-                                              __amdgpu_buffer_rsrc_t rv, int xoff, int cw,
-                                              int lane) {
+// Kt, beta, Gam and this lane's pieces of V (first half); Wb^T (second half).
+// AUX: the cache policy bits of the tile loads.
+template <int DV, int AUX = 0>
+__device__ __forceinline__ void chainw_load_a(ChainFragsWT<DV>& f, __amdgpu_buffer_rsrc_t rt,
+                                              __amdgpu_buffer_rsrc_t rv, const VoPieces<DV>& vp,
+                                              int rowb, int cw, int lane) {
     const int q4 = lane >> 4;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) f.K[kk] = ld_frag(rt, OFF_KT + ((cw * 4 + kk) * 64 + lane) * 16);
-    f.bet = ld_f4(rt, OFF_BETA + (16 * cw + 4 * q4) * 4);
+    for (int kk = 0; kk < 4; ++kk)
+        f.K[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
+            rt, OFF_KT + ((cw * 4 + kk) * 64 + lane) * 16, 0, AUX));
+    {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rt, OFF_BETA + (16 * cw + 4 * q4) * 4,
+                                                              0, AUX);
+        f.bet = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                            __uint_as_float(x[3]));
+    }
 #pragma unroll
-    for (int a = 0; a < 2; ++a) f.gam[a] = ld_f4(rt, OFF_GAM + (32 * cw + 16 * a + 4 * q4) * 4);
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, xoff, 0, 0);
-    f.v = make_uint4(x[0], x[1], x[2], x[3]);
+    for (int a = 0; a < 2; ++a) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+            rt, OFF_GAM + (32 * cw + 16 * a + 4 * q4) * 4, 0, AUX);
+        f.gam[a] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]),
+                               __uint_as_float(x[2]), __uint_as_float(x[3]));
+    }
+#pragma unroll
+    for (int u = 0; u < DV / 32; ++u) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, vp.off(u, rowb), 0, 0);
+        f.v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
 }
-__device__ __forceinline__ void chainw_load_b(ChainFragsW& f, __amdgpu_buffer_rsrc_t rt, int cw,
-                                              int lane) {
+template <int DV, int AUX = 0>
+__device__ __forceinline__ void chainw_load_b(ChainFragsWT<DV>& f, __amdgpu_buffer_rsrc_t rt,
+                                              int cw, int lane) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            f.W[a][kk] = ld_frag(rt, OFF_WBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16);
+            f.W[a][kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
+                rt, OFF_WBT + ((cw * 4 + a * 2 + kk) * 64 + lane) * 16, 0, AUX));
 }
-__device__ __forceinline__ void outw_load_a(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
+template <int DV, int AUX = 0>
+__device__ __forceinline__ void outw_load_a(OutFragsT<DV>& f, __amdgpu_buffer_rsrc_t rt, int cw,
                                             int lane) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) f.Q[kk] = ld_frag(rt, OFF_QT + ((cw * 4 + kk) * 64 + lane) * 16);
+    for (int kk = 0; kk < 4; ++kk)
+        f.Q[kk] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
+            rt, OFF_QT + ((cw * 4 + kk) * 64 + lane) * 16, 0, AUX));
 }
-__device__ __forceinline__ void outw_load_b(OutFrags& f, __amdgpu_buffer_rsrc_t rt, int cw,
+template <int DV, int AUX = 0>
+__device__ __forceinline__ void outw_load_b(OutFragsT<DV>& f, __amdgpu_buffer_rsrc_t rt, int cw,
                                             int lane) {
-    f.P[0] = ld_frag(rt, OFF_PT + (cw * 2 * 64 + lane) * 16);
-    if (cw >= 2) f.P[1] = ld_frag(rt, OFF_PT + ((cw * 2 + 1) * 64 + lane) * 16);  // else zero
+    f.P[0] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(rt, OFF_PT + (cw * 2 * 64 + lane) * 16,
+                                                          0, AUX));
+    if (cw >= 2)  // else zero
+        f.P[1] = as_bf8(__builtin_amdgcn_raw_buffer_load_b128(
+            rt, OFF_PT + ((cw * 2 + 1) * 64 + lane) * 16, 0, AUX));
 }
-// This lane's 16-byte piece of the chunk's gate projection (row xrow, columns
-// xcol ..; a window of zero rows past the chunk).
-__device__ __forceinline__ void out_load_z(OutFrags& f, __amdgpu_buffer_rsrc_t rz, int xoff) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rz, xoff, 0, 0);
-    f.z = make_uint4(x[0], x[1], x[2], x[3]);
+// This lane's 16-byte pieces of the chunk's gate projection (VoPieces; a window
+// of zero rows past the chunk).
+template <int DV>
+__device__ __forceinline__ void out_load_z(OutFragsT<DV>& f, __amdgpu_buffer_rsrc_t rz,
+                                           const VoPieces<DV>& vp, int rowb) {
+#pragma unroll
+    for (int u = 0; u < DV / 32; ++u) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rz, vp.off(u, rowb), 0, 0);
+        f.z[u] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
 }
 
 // [C] S <- Gam S + Wb^T R (R from Rt); the raw S to snp (a snapshot) when snp is
 // set; with more, the next chunk's operand G' = 2^R' S into Gt and Gam' S into S.
-__device__ __forceinline__ void chainw_s(StateLds& sm, const ChainFragsW& cur,
-                                         const float4 (&gam_next)[2], bool more, StateFrag& S,
-                                         float* snp, int j0, int cw, int lane) {
+template <int DV>
+__device__ __forceinline__ void chainw_s(StateLdsT<DV>& sm, const ChainFragsWT<DV>& cur,
+                                         const float4 (&gam_next)[2], bool more,
+                                         StateFragT<DV>& S, float* snp, int j0, int cw, int lane) {
     const int r = lane & 15, q4 = lane >> 4;
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int jb = 0; jb < DV / 16; ++jb) {
         const bf16x8 r0 = ld8(sm.Rt + (16 * jb + r) * LDT + 8 * q4);
         const bf16x8 r1 = ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4);
 #pragma unroll
@@ -326,19 +394,19 @@ __device__ __forceinline__ void chainw_s(StateLds& sm, const ChainFragsW& cur,
 }
 
 // [C] O = Z + PT R (gated by sigmoid(z) with GATED), staged through this
-// wave's rows; returns this lane's 16-byte piece (row xrow, columns xcol ..)
-// for one store.
-template <bool GATED>
-__device__ __forceinline__ u32x4 outw_o(StateLds& sm, const OutFrags& cur, const f32x4 (&Zc)[2],
-                                        const uint4& z, int cw, int lane, int xrow, int xcol) {
+// wave's rows; this lane's 16-byte pieces (VoPieces) for the stores, into out.
+template <bool GATED, int DV>
+__device__ __forceinline__ void outw_o(StateLdsT<DV>& sm, const OutFragsT<DV>& cur,
+                                       const f32x4 (&Zc)[DV / 16], int cw, int lane,
+                                       const VoPieces<DV>& vp, u32x4 (&out)[DV / 32]) {
     const int r = lane & 15, q4 = lane >> 4;
-    f32x4 acc[2];
+    f32x4 acc[DV / 16];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int jb = 0; jb < DV / 16; ++jb) {
         acc[jb] = mma32(cur.P[0], ld8(sm.Rt + (16 * jb + r) * LDT + 8 * q4), Zc[jb]);
         if (cw >= 2) acc[jb] = mma32(cur.P[1], ld8(sm.Rt + (16 * jb + r) * LDT + 32 + 8 * q4), acc[jb]);
     }
-    return stage_out<GATED>(sm, acc, z, cw, lane, xrow, xcol);
+    stage_out<GATED, DV>(sm, acc, cur.z, cw, lane, vp, out);
 }
 
 }  // namespace co
