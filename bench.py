@@ -48,6 +48,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "gated_delta_rule_99_amd", "csrc")
 SOURCES = {
     PREFILL_KERNEL: [os.path.join(_CSRC, "kda_prefill_split.hip"),
+                     os.path.join(_CSRC, "kda_prep_tile.h"),
                      os.path.join(_CSRC, "kda_chunk_ops.h"),
                      os.path.join(_CSRC, "kda_state_pass.h")],
     DECODE_KERNEL: [os.path.join(_CSRC, "kda_decode.hip")],
@@ -218,8 +219,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=500)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "prefill_gate_proj", "decode", "decode_tokens",
-                                       "decode_bf16_state", "conv", "copy"],
+    ap.add_argument("--only", choices=["prefill", "prefill_gate_proj", "prefill_out_gate", "decode",
+                                       "decode_tokens", "decode_bf16_state", "conv", "copy"],
                     default=None, help="run just one kernel (for profiler runs)")
     args = ap.parse_args()
 
@@ -366,6 +367,51 @@ def main():
             result.update({"value": T / (g_ms * 1e-3), "unit": "tokens/s",
                            "ms_per_step": g_ms})
         del q, k, v, f, b, a_log, o, state, inp, pr
+        torch.cuda.empty_cache()
+
+    if args.only == "prefill_out_gate" or (args.only is None and not args.no_decode):
+        # the same layer with the output gate fused into the output stores: every
+        # output multiplied by sigmoid(z), z a bf16 projection in o's layout
+        inp = workloads.ling_prefill()
+        T, H, d, C = inp.T, inp.H, inp.d, inp.chunk
+        z = workloads.output_gate_projection(T, H, d, dtype="bf16", seed=1004)
+        q, k, v, g, beta, zd = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta, z))
+        cu = inp.cu_seqlens.to(dev)
+        state = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+        o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+
+        def ostep(e0=None, e1=None):
+            kda.kda_state_init(state)
+            if e0 is not None:
+                e0.record()
+            kda.kda_prefill_chunked(q, k, v, g, beta, cu_seqlens=cu, cu_seqlens_host=inp.cu_seqlens,
+                                    chunk=C, initial_state=state, final_state=state, o=o,
+                                    out_gate=zd)
+            if e1 is not None:
+                e1.record()
+
+        for _ in range(args.warmup):
+            ostep()
+        torch.cuda.synchronize()
+        pairs = [(ev(), ev()) for _ in range(args.steps)]
+        for e0_, e1_ in pairs:
+            ostep(e0_, e1_)
+        torch.cuda.synchronize()
+        og_ms = sum(a.elapsed_time(b_) for a, b_ in pairs) / len(pairs)
+        alg_bytes, _ = prefill_algorithmic(T, H, d, C, True, True)
+        alg_bytes += T * H * d * 2  # the gate projection z, read once
+        gbs = alg_bytes / (og_ms * 1e-3) / 1e9
+        result["prefill_out_gate"] = {
+            "workload": "the Ling-shaped layer prefill with the output gate fused: o * sigmoid(z), "
+                        "z [8192, 64, 128] bf16",
+            "ms_per_call": og_ms, "tokens_per_s": T / (og_ms * 1e-3),
+            "roofline": {"bound": "hbm", "kernel": PREFILL_KERNELS, "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes": alg_bytes}}
+        if args.only == "prefill_out_gate":
+            result.update({"value": T / (og_ms * 1e-3), "unit": "tokens/s",
+                           "ms_per_step": og_ms})
+        del q, k, v, g, beta, zd, o, state, inp, z
         torch.cuda.empty_cache()
 
     B, H, d = 256, 64, 128  # the batched decode workload's shape
