@@ -50,6 +50,40 @@ static_assert(sizeof(PairLds) <= sizeof(ChunkLds) - offsetof(ChunkLds, Kb) - siz
 // match them.
 constexpr int PAIR_SYNCS = 5;
 
+// The N phase of a chunk on the pairwise path (a chunk that decays below
+// 2^-SLOW on some channel): N, T's diagonal blocks and P from the reloaded
+// inputs of rows [c0, c0 + L), written to sm (PAIR_SYNCS barriers).  Kept out
+// of line, with plain arguments and its results in LDS, so that its registers
+// are saved around this rare call instead of squeezing the producer's loop.
+template <int GM>
+__device__ __attribute__((noinline)) void slow_n_phase(ChunkLds* sm, const bf16_t* q,
+                                                       const bf16_t* k, Gate g,
+                                                       const float* beta, int64_t c0, int L,
+                                                       int H, int h, int p, int lane) {
+    const int r = lane & 15, q4 = lane >> 4;
+    ChunkIn in;
+    load_chunk<GM>(in, q, k, g, beta, c0, L, H, h, p, lane);
+    NRaw nw;
+    f32x4 pb[3];
+    slow_products<GM>(*reinterpret_cast<PairLds*>(sm->Kb), in, p, lane, nw, pb,
+                      [] { __syncthreads(); });
+    NRegs nr;
+    n_finish(sm->beta, p, lane, nw, nr);
+    __syncthreads();  // the pairwise rows are read in full
+    n_store(*sm, p, lane, nr);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        if (j >= p_count(p)) break;
+        int rb, cb;
+        lower_block(p_first(p) + j, rb, cb);
+        p_store(*sm, rb, cb, lane, pb[j]);
+    }
+    if (p == 0 || p == 2) {  // T's and P's upper blocks the copy-in reads: (0,1), (2,3)
+        st4(sm->T + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
+        st4(sm->P + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
+    }
+}
+
 }  // namespace fu
 
 using namespace fu;
@@ -124,43 +158,36 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         // [B] of chunk c: N (and T's diagonal blocks) on the matrix cores, or on
         // the pairwise path (then P too, and PAIR_SYNCS barriers)
         auto n_phase = [&](int c, bool slow) {
-            if (!slow) {
+            if (!slow)
                 n_stage(sm.ck, p, lane);
-                return;
-            }
-            ChunkIn in2;
-            load_chunk<GM>(in2, q, k, g, beta, tb + (int64_t)c * C, chunk_len(c), H, h, p, lane);
-            NRaw nw;
-            f32x4 pb[3];
-            slow_products<GM>(*reinterpret_cast<PairLds*>(sm.ck.Kb), in2, p, lane, nw, pb,
-                              [] { __syncthreads(); });
-            NRegs nr;
-            n_finish(sm.ck.beta, p, lane, nw, nr);
-            __syncthreads();  // the pairwise rows are read in full
-            n_store(sm.ck, p, lane, nr);
-#pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                if (j >= p_count(p)) break;
-                int rb, cb;
-                lower_block(p_first(p) + j, rb, cb);
-                p_store(sm.ck, rb, cb, lane, pb[j]);
-            }
-            if (p == 0 || p == 2) {  // T's and P's upper blocks the copy-in reads: (0,1), (2,3)
-                st4(sm.ck.T + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
-                st4(sm.ck.P + (16 * p + r) * LDT + 16 * (p + 1) + 4 * q4, Z4);
-            }
+            else
+                slow_n_phase<GM>(&sm.ck, q, k, g, beta, tb + (int64_t)c * C, chunk_len(c), H, h, p,
+                                 lane);
         };
         auto slow_flag = [&]() { return sm.slow[0] | sm.slow[1] | sm.slow[2] | sm.slow[3]; };
         ChunkIn in;
+        // the inputs of chunk c2, loaded while chunk c's N phase runs: before it
+        // on the matrix-core path, after it on the pairwise path, which reloads
+        // chunk c's own inputs (so that the two sets are never live together)
+        auto n_phase_load = [&](int c, bool slow, int c2) {
+            if (!slow) {
+                load_chunk<GM>(in, q, k, g, beta, tb + (int64_t)c2 * C, chunk_len(c2), H, h, p,
+                               lane);
+                if (c < nc) n_phase(c, false);
+            } else {
+                n_phase(c, true);
+                load_chunk<GM>(in, q, k, g, beta, tb + (int64_t)c2 * C, chunk_len(c2), H, h, p,
+                               lane);
+            }
+        };
         load_chunk<GM>(in, q, k, g, beta, tb, chunk_len(0), H, h, p, lane);
         {
             const bool ws = decay_stage<GM>(sm.ck, in, p, lane, gam_sink, kbt_sink);
             if (lane == 0) sm.slow[p] = ws;
         }
-        load_chunk<GM>(in, q, k, g, beta, tb + C, chunk_len(1), H, h, p, lane);
         __syncthreads();  // P1
         bool slow = slow_flag();
-        n_phase(0, slow);
+        n_phase_load(0, slow, 1);
         __syncthreads();  // P2
         merge_stage(sm.ck, p, lane, !slow);
         __syncthreads();  // P3
@@ -171,11 +198,9 @@ prefill_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bool ws = decay_stage<GM>(sm.ck, in, p, lane, gam_sink, kbt_sink);
                 if (lane == 0) sm.slow[p] = ws;
             }
-            load_chunk<GM>(in, q, k, g, beta, tb + (int64_t)(s + 2) * C, chunk_len(s + 2), H, h, p,
-                           lane);
             __syncthreads();  // B1
             slow = next && slow_flag();
-            if (next) n_phase(s + 1, slow);
+            n_phase_load(next ? s + 1 : nc, slow, s + 2);
             __syncthreads();  // B2
             if (next) merge_stage(sm.ck, p, lane, !slow);
             __syncthreads();  // B3
