@@ -85,12 +85,14 @@ __device__ __forceinline__ void tile_export_kq(const L& sm, __amdgpu_buffer_rsrc
 // ---------------------------------------------------------------- state pass
 template <int DV>
 struct StateLdsT {
-    static constexpr int LDX = DV + 8;  // row stride (bf16) of the V and O staging tiles
+    static constexpr int LDX = DV + 8;   // row stride (bf16) of the V and O staging tiles
+    static constexpr int LDXF = DV + 4;  // row stride (fp32) of the gated O staging tile
     uint16_t Gt[DV * LDK];  // bf16 (2^R * S)^T [j][i]
     uint16_t Rt[DV * LDT];  // R^T [j][t]
     uint16_t Ut[DV * LDT];  // U^T [j][t] (fused path)
     uint16_t V[C * LDX];    // V slice [t][j]: each chain wave stages its own 16 rows
     uint16_t O[C * LDX];    // O slice [t][j]: each output wave stages its own 16 rows
+    float Of[C * LDXF];     // O slice in fp32, for the output gate (same rows)
 };
 using StateLds = StateLdsT<DVS>;
 
@@ -230,41 +232,49 @@ __device__ __forceinline__ void out_z(StateLdsT<DV>& sm, const OutFragsT<DV>& cu
 
 // This wave's 16 output rows, fp32 in the accumulator layout (acc[jb][e]: row
 // 16cw + 4q4 + e, column 16jb + r), to this lane's 16-byte pieces of them
-// (VoPieces) in bf16, through the wave's rows of the staging tile.  GATED: each
-// output is first multiplied by sigmoid(z), the output gate, with z this lane's
-// pieces of the gate projection (same rows and columns): z takes the same way
-// through the staging rows into the accumulator layout, so that the gated
-// value is rounded to bf16 once.  Only the wave itself touches these rows, and
-// a wave's LDS accesses complete in order.
+// (VoPieces) in bf16, through the wave's rows of a staging tile.  GATED: each
+// output is multiplied by sigmoid(z), the output gate, z this lane's pieces of
+// the gate projection (same rows and columns): the rows are staged in fp32,
+// the gate applied in the piece layout (where z already is) and the product
+// rounded to bf16 once.  Only the wave itself touches these rows, and a wave's
+// LDS accesses complete in order.
 template <bool GATED, int DV>
 __device__ __forceinline__ void stage_out(StateLdsT<DV>& sm, f32x4 (&acc)[DV / 16],
                                           const uint4 (&z)[DV / 32], int cw, int lane,
                                           const VoPieces<DV>& vp, u32x4 (&out)[DV / 32]) {
-    constexpr int NJB = DV / 16, LDX = StateLdsT<DV>::LDX;
+    constexpr int NJB = DV / 16, LDX = StateLdsT<DV>::LDX, LDXF = StateLdsT<DV>::LDXF;
     const int r = lane & 15, q4 = lane >> 4;
     if constexpr (GATED) {
-#pragma unroll
-        for (int u = 0; u < DV / 32; ++u)
-            *reinterpret_cast<uint4*>(sm.O + vp.row[u] * LDX + vp.col[u]) = z[u];
-        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                acc[jb][e] *= sigmoid_f(
-                    bf16_bits_to_f32(sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r]));
+                sm.Of[(16 * cw + 4 * q4 + e) * LDXF + 16 * jb + r] = acc[jb][e];
         __builtin_amdgcn_wave_barrier();
-    }
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb)
+        for (int u = 0; u < DV / 32; ++u) {
+            const float* row = sm.Of + vp.row[u] * LDXF + vp.col[u];
+            const float4 a = *reinterpret_cast<const float4*>(row);
+            const float4 b = *reinterpret_cast<const float4*>(row + 4);
+            const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            const uint32_t zw[4] = {z[u].x, z[u].y, z[u].z, z[u].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[jb][e]);
-    __builtin_amdgcn_wave_barrier();
+            for (int w = 0; w < 4; ++w)
+                out[u][w] = pack2(x[2 * w] * sigmoid_f(bf_lo(zw[w])),
+                                  x[2 * w + 1] * sigmoid_f(bf_hi(zw[w])));
+        }
+    } else {
 #pragma unroll
-    for (int u = 0; u < DV / 32; ++u) {
-        const uint4 x = *reinterpret_cast<const uint4*>(sm.O + vp.row[u] * LDX + vp.col[u]);
-        out[u] = u32x4{x.x, x.y, x.z, x.w};
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sm.O[(16 * cw + 4 * q4 + e) * LDX + 16 * jb + r] = f32_to_bf16_bits(acc[jb][e]);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < DV / 32; ++u) {
+            const uint4 x = *reinterpret_cast<const uint4*>(sm.O + vp.row[u] * LDX + vp.col[u]);
+            out[u] = u32x4{x.x, x.y, x.z, x.w};
+        }
     }
 }
 
