@@ -34,6 +34,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// A dispatch counts its work-items in 32 bits: workgroups x threads per
+// workgroup must stay below 2^32 along the grid's first dimension.
+bool dispatch_fits(int64_t workgroups, int threads) {
+    return workgroups <= (int64_t)0xffffffffll / threads;
+}
+
 // Shapes that run on the matrix cores.
 bool mfma_shape(kda_dtype dtype, int dk, int dv, int chunk) {
     return dtype == KDA_BF16 && dk == 128 && dv == 128 && chunk == 64;
@@ -176,8 +182,10 @@ static kda_status prefill_entry(const char* fn, const void* q, const void* k, co
     if (!cu_seqlens_dev) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens_dev is NULL", fn);
     const int d = dk;
     const int64_t blocks = (int64_t)n_seqs * H * (d == 128 ? 4 : (d < 32 ? 1 : d / 32));
-    if (blocks > 0x7fffffff)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn,
+    // prefill kernels take at most 1024 threads per workgroup
+    if (!dispatch_fits(blocks, 1024))
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "%s: %lld workgroups exceed 4194303 (32-bit dispatch size)", fn,
                     (long long)blocks);
     const size_t es = elem_size(dtype);
     const size_t n_qk = (size_t)T * H * d, n_bt = (size_t)T * H;
@@ -362,8 +370,10 @@ static kda_status decode_common(const char* fn, const void* q, const void* k, co
     if (!slot_idx && n_slots < B)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots (%lld) < B (%d) without slot_idx", fn,
                     (long long)n_slots, B);
-    if ((int64_t)B * H > 0x7fffffff)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: B * H exceeds the grid limit", fn);
+    // every decode shape spends at most 1024 work-items on one (sequence, head)
+    if (!dispatch_fits((int64_t)B * H, 1024))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: B * H = %lld exceeds 4194303 (32-bit dispatch size)",
+                    fn, (long long)B * H);
     if (!q || !k || !v || !g || !beta || !o || !state)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: q, k, v, g, beta, state and o are required",
                     fn);
@@ -455,8 +465,12 @@ kda_status kda_short_conv_prefill(const void* x, const float* w, kda_dtype dtype
     if (kda_status s = check_cu(fn, cu_seqlens_host, n_seqs, &T)) return s;
     if (n_seqs == 0) return KDA_OK;
     if (!cu_seqlens_dev) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens_dev is NULL", fn);
-    if ((T + 15) / 16 > 0x7fffffff)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+    // runs of at least 16 tokens per workgroup of 256 threads; the tail pass
+    // takes one thread per (sequence, channel)
+    if (!dispatch_fits((T + 15) / 16, 256) || !dispatch_fits((int64_t)n_seqs * channels + 255, 1))
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "%s: T = %lld tokens of %d channels exceed the 32-bit dispatch size", fn,
+                    (long long)T, channels);
     const size_t es = elem_size(dtype);
     const size_t nx = (size_t)T * channels * es, nt = (size_t)n_seqs * 3 * channels * es;
     if (T > 0) {
@@ -490,6 +504,9 @@ kda_status kda_short_conv_decode(const void* x, const float* w, kda_dtype dtype,
     if (B == 0) return KDA_OK;
     if (!slot_idx && n_slots < B)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots < B without slot_idx", fn);
+    if (!dispatch_fits(B, 64))  // one 64-thread workgroup per sequence and head group
+        return fail(KDA_ERR_UNSUPPORTED, "%s: B = %d exceeds 67108863 (32-bit dispatch size)",
+                    fn, B);
     if (!x || !y || !conv_tail)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: x, y and conv_tail are required", fn);
     if (!aligned16(x) || !aligned16(y) || !aligned16(conv_tail) || ((uintptr_t)slot_idx & 3u))

@@ -65,7 +65,12 @@ extern "C" {
 typedef enum kda_status KDA_ENUM_BASE {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad cu_seqlens */
-    KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k != d_v) */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k != d_v), or
+                                     a launch beyond the 32-bit dispatch size (2^32
+                                     work-items): decode with B * H > 4194303, prefill
+                                     with n_seqs * H * (4 for d = 128, d / 32 from 32,
+                                     else 1) > 4194303, a convolution over T >= 2^28
+                                     tokens or of B > 67108863 sequences */
     KDA_ERR_HIP = 3,              /* a HIP runtime call failed; see kda_last_error_detail */
     KDA_ERR_WORKSPACE_TOO_SMALL = 4 /* a workspace below the size its query returns */
 } kda_status;

@@ -257,6 +257,23 @@ def test_conv_prefill_rejects(lib, kw, status, needle):
     assert needle in lib.kda_last_error_detail().decode()
 
 
+def test_dispatch_size_rejects(lib):
+    """Launches beyond 2^32 work-items are refused before any HIP call: decode
+    spends up to 1024 work-items per (sequence, head), prefill up to 1024 per
+    workgroup (4 workgroups per head of d = 128), the convolution 256 per 16
+    tokens and 64 per decoded sequence."""
+    assert decode(lib, B=4194304, H=1, slot=Hp, n_slots=8) == KDA_ERR_UNSUPPORTED
+    assert "dispatch" in lib.kda_last_error_detail().decode()
+    n = 4194304 // (64 * 4)
+    assert prefill(lib, n=n, H=64, cu_host=cu_arr([0] * (n + 1))) == KDA_ERR_UNSUPPORTED
+    assert "dispatch" in lib.kda_last_error_detail().decode()
+    assert conv(lib, cu_host=cu_arr([0, 1 << 28])) == KDA_ERR_UNSUPPORTED
+    assert "dispatch" in lib.kda_last_error_detail().decode()
+    assert lib.kda_short_conv_decode(A, Bp, KDA_BF16, Cp, 4, Ep, 1 << 26, 256, 128, 1e-6, Dp,
+                                     None) == KDA_ERR_UNSUPPORTED
+    assert "dispatch" in lib.kda_last_error_detail().decode()
+
+
 def test_conv_decode_rejects(lib):
     f = lib.kda_short_conv_decode
     assert f(A, Bp, KDA_BF16, None, 4, None, 2, 256, 128, 1e-6, Dp, None) == \

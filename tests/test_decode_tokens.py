@@ -57,6 +57,30 @@ def test_decode_tokens_matches_oracle(d, dtype, n_tok):
     assert torch.equal(st[untouched], pool[untouched])
 
 
+@pytest.mark.parametrize("dtype,n_tok", [("bf16", 6), ("f32", 9), ("bf16", 64)])
+def test_decode_tokens_several_groups(dtype, n_tok):
+    """d = 128 over more tokens than the four of the speculative-decoding
+    workload, up to the 64-token maximum, through a slot permutation: outputs
+    and final states match the oracle, other slots are untouched."""
+    m = kda()
+    B, H, n_slots, d = 3, 2, 5, 128
+    inp = workloads.recurrence_inputs([n_tok] * B, H=H, d=d, dtype=dtype, s0_std=0.3,
+                                      seed=80 + n_tok)
+    pool = torch.randn((n_slots, H, d, d), generator=torch.Generator().manual_seed(81)) * 0.3
+    slots = torch.tensor([4, 0, 2], dtype=torch.int32)
+    pool[slots.long()] = inp.S0
+    state = dev(pool)
+    o, _ = run_tokens(m, inp, B, n_tok, state, slot_idx=dev(slots))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_on(inp)
+    st = state.cpu()
+    assert_parity(np64(o).reshape(B * n_tok, H, d), o_ref, np64(st[slots.long()]), S_ref,
+                  inp.cu_seqlens, TOL_F32 if dtype == "f32" else TOL_BF16,
+                  f"decode_tokens d=128 {dtype} n_tok={n_tok}")
+    untouched = [s for s in range(n_slots) if s not in slots.tolist()]
+    assert torch.equal(st[untouched], pool[untouched])
+
+
 @pytest.mark.parametrize("d,dtype", [(16, "f32"), (128, "bf16")])
 def test_decode_tokens_snapshots_match_prefixes(d, dtype):
     """token_states[b, j] is sequence b's state after token j: it matches the

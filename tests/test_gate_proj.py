@@ -83,7 +83,7 @@ def test_prefill_gate_proj_ling_layer():
                   f"gate proj ling layer")
 
 
-@pytest.mark.parametrize("dtype,d,n_tok", [("bf16", 128, 1), ("f32", 64, 4)])
+@pytest.mark.parametrize("dtype,d,n_tok", [("bf16", 128, 1), ("f32", 64, 4), ("bf16", 128, 3)])
 def test_decode_gate_proj(dtype, d, n_tok):
     """n_tok tokens per sequence in one call through a slot permutation."""
     m = kda()
