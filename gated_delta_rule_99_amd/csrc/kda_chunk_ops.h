@@ -77,13 +77,6 @@ __device__ __forceinline__ float bf_hi(uint32_t v) { return bf16_bits_to_f32(v >
 __device__ __forceinline__ bf16x8 as_bf8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 __device__ __forceinline__ u32x4 as_u4(bf16x8 x) { return __builtin_bit_cast(u32x4, x); }
 
-// Window of global memory as a buffer resource: loads past num_bytes read zero,
-// stores past it are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const void* base, int num_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes,
-                                             0x00020000);
-}
-
 // Sequence n's token range (clamped to [0, T)) and chunk count.
 __device__ __forceinline__ void seq_chunks(const int32_t* cu, int n, int64_t T, int64_t& tb,
                                            int64_t& te, int& nc) {

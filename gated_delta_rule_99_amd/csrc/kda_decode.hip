@@ -35,7 +35,10 @@ namespace kda {
 // State access: VEC consecutive state elements of one row (4 or 8), with the
 // non-temporal (streaming) hint, widened to / narrowed from fp32.  fp32 states
 // move 4 elements in 16 bytes; bf16 states 4 elements in 8 bytes or 8 in 16,
-// rounded to nearest even when stored.
+// rounded to nearest even when stored.  Two addressing forms: 64-bit
+// pointers, or a head's state as a buffer window (the lane's offset voff plus
+// a constant row-group offset soff), which keeps no 64-bit address live
+// between the state's load and its store.
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <typename TS>
@@ -53,6 +56,22 @@ struct StateIO<float> {
         static_assert(VEC == 4, "fp32 states move 4 elements per access");
         const f32x4 v = {x[0], x[1], x[2], x[3]};
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    }
+    template <int VEC>
+    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                                float (&x)[VEC]) {
+        static_assert(VEC == 4, "fp32 states move 4 elements per access");
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, BUF_NT);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(v[e]);
+    }
+    template <int VEC>
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                                 const float (&x)[VEC]) {
+        static_assert(VEC == 4, "fp32 states move 4 elements per access");
+        const u32x4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                         __float_as_uint(x[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, BUF_NT);
     }
 };
 template <>
@@ -89,6 +108,39 @@ struct StateIO<bf16_t> {
             const u32x4 v = {pack(x[0], x[1]), pack(x[2], x[3]), pack(x[4], x[5]),
                              pack(x[6], x[7])};
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+        }
+    }
+    template <int VEC>
+    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                                float (&x)[VEC]) {
+        if constexpr (VEC == 4) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, BUF_NT);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                x[2 * e] = bf16_bits_to_f32(v[e] & 0xffffu);
+                x[2 * e + 1] = bf16_bits_to_f32(v[e] >> 16);
+            }
+        } else {
+            static_assert(VEC == 8, "bf16 states move 4 or 8 elements per access");
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, BUF_NT);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16_bits_to_f32(v[e] & 0xffffu);
+                x[2 * e + 1] = bf16_bits_to_f32(v[e] >> 16);
+            }
+        }
+    }
+    template <int VEC>
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                                 const float (&x)[VEC]) {
+        if constexpr (VEC == 4) {
+            const u32x2 v = {pack(x[0], x[1]), pack(x[2], x[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, BUF_NT);
+        } else {
+            static_assert(VEC == 8, "bf16 states move 4 or 8 elements per access");
+            const u32x4 v = {pack(x[0], x[1]), pack(x[2], x[3]), pack(x[4], x[5]),
+                             pack(x[6], x[7])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, BUF_NT);
         }
     }
 };
@@ -234,10 +286,25 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
     if constexpr (PROJ) rate = __expf(a_log[h]);
     const int cg = tid % CG, rg = tid / CG, c0 = VEC * cg;
 
+    // The state's addressing.  Several tokens: a buffer window, which frees the
+    // 64-bit addresses otherwise live across the token loop (d = 128: 162-164
+    // -> 118-130 VGPRs, four waves per SIMD instead of three; four tokens at
+    // 256 sequences x 64 heads 0.404 -> 0.399 ms).  One token: 64-bit pointers
+    // (the window measured 0.333 -> 0.343 ms there, fp32 states).
+    constexpr int SB = D * D * (int)sizeof(TS);      // bytes of one state
+    constexpr int MSTEP = RG * D * (int)sizeof(TS);  // between a thread's rows
+    const int voff = (rg * D + c0) * (int)sizeof(TS);
+
     // 1. stream the state in: RPT independent 16-byte loads per thread
     float s[RPT][VEC];
+    if constexpr (MULTI) {
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) StateIO<TS>::load(st + (size_t)(rg + RG * m) * D + c0, s[m]);
+        for (int m = 0; m < RPT; ++m) StateIO<TS>::load(window(st, SB), voff, MSTEP * m, s[m]);
+    } else {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            StateIO<TS>::load(st + (size_t)(rg + RG * m) * D + c0, s[m]);
+    }
 
     // 2-5 once per token, the state staying in registers
     const int nt = MULTI ? n_tok : 1;
@@ -372,13 +439,24 @@ decode_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* _
             const float a = s_a[i], kk = s_k[i];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) s[m][e] = a * s[m][e] + kk * u[e];
-            if (snap) StateIO<TS>::store(snap + (size_t)i * D + c0, s[m]);
+            if (snap) {
+                if constexpr (MULTI)
+                    StateIO<TS>::store(window(snap, SB), voff, MSTEP * m, s[m]);
+                else
+                    StateIO<TS>::store(snap + (size_t)i * D + c0, s[m]);
+            }
         }
     }
 
     // 6. stream the state out
+    if constexpr (MULTI) {
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) StateIO<TS>::store(st + (size_t)(rg + RG * m) * D + c0, s[m]);
+        for (int m = 0; m < RPT; ++m) StateIO<TS>::store(window(st, SB), voff, MSTEP * m, s[m]);
+    } else {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            StateIO<TS>::store(st + (size_t)(rg + RG * m) * D + c0, s[m]);
+    }
 }
 
 template <int D, typename Tin, typename TS>

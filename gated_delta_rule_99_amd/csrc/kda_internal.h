@@ -126,6 +126,16 @@ __device__ __forceinline__ float sigmoid_f(float x) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
 }
 
+// Window of global memory as a buffer resource: loads past num_bytes read zero,
+// stores past it are dropped.  The base is wave-uniform (scalar registers), so
+// lanes address it with 32-bit offsets instead of 64-bit pointers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const void* base, int num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes,
+                                             0x00020000);
+}
+// Cache-policy operand of buffer loads and stores: non-temporal (streamed once).
+constexpr int BUF_NT = 2;
+
 // The calling thread's error text (what kda_last_error_detail returns).
 void set_error_detail(const char* fmt, ...);
 
