@@ -9,7 +9,8 @@ inputs resident in HBM.  The batched decode step (B=256 sequences x 64 heads,
 one token each, fp32 128x128 states) is timed in the same run and reported as
 achieved state bandwidth under ``decode``.
 
-Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+Prints one JSON line.  ``--gpus`` above 1 is refused: the library's path runs on
+one GPU (one GPU's share of the heads).
 """
 from __future__ import annotations
 
@@ -225,8 +226,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the KDA hot path of one GPU's "
-              "share); --gpus must be 1", file=sys.stderr)
+        print("bench.py: the KDA hot path runs on one GPU (one GPU's share of the heads); "
+              "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
